@@ -1,0 +1,187 @@
+"""CPU oracle for PQ-KV decode attention and PQ encode.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The HIP library never
+calls it and shares no code with it.
+
+It computes the plain definitions, slowly and in float64 (the encode
+decision in float32, the precision the GPU kernel decides in):
+
+* Product quantization of a cached vector (AQPIM page, section 3.1): the
+  D-dimensional vector is cut into M equal contiguous segments; segment m is
+  stored as the index of its nearest codeword in codebook m; decoding looks
+  the indices up and lays the M codewords side by side.
+* Codebooks are kept per layer and per head (AQPIM page, section 3.2 (1));
+  under grouped-query attention a KV head's codebooks serve all the query
+  heads of its group (memory-wall chapter, section 1.4.3 (1)).  Query head h
+  reads KV head h // G with G = Hq / Hkv.
+* Decode attention "the long way" (AQPIM page, section 4): rebuild every
+  cached K and V from its indices, then textbook attention for one query
+  token: s_t = scale * q . K_t over the t < lens[b] cached tokens, a
+  numerically stable softmax, out = sum_t p_t V_t.
+* Chunked softmax (PAM page, section 2.2.3 (1); memory-wall chapter,
+  section 1.4.3 (5.1)): each chunk of tokens keeps its own max m_c, its sum
+  l_c = sum exp(s - m_c) and its unnormalised output o_c = sum exp(s - m_c)V;
+  a reduction rescales every chunk by exp(m_c - max_c m_c) and divides.
+* Encode (AQPIM page, sections 3.1 and 5.2 (2)): per segment, the index of
+  the codeword at the smallest squared Euclidean distance; the lowest index
+  wins a tie.
+
+Readings where the pages are silent (the scale 1/sqrt(D), lens = 0 gives a
+zero output, the head -> KV head map) are listed with the rest of the design
+notes of this repository.
+
+Parity pins: every function here is checked against facts that do not come
+from this file -- the pages' printed sizes, algebraic identities, closed
+forms on tiny inputs, torch's CPU scaled-dot-product attention and scipy's
+distance routine -- in tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def default_scale(head_dim: int) -> float:
+    """Softmax temperature 1/sqrt(D) (the pages do not state one)."""
+    return 1.0 / math.sqrt(head_dim)
+
+
+def reconstruct(codes: np.ndarray, cb: np.ndarray) -> np.ndarray:
+    """Rebuild vectors from their PQ indices (AQPIM page, section 3.1).
+
+    codes: uint8 [..., M]  (indices of one KV head)
+    cb:    [M, K, ds]      (that head's codebook)
+    returns float64 [..., M*ds]: the M looked-up codewords side by side.
+    """
+    M = cb.shape[0]
+    cb64 = cb.astype(np.float64)
+    segments = [cb64[m][codes[..., m].astype(np.intp)] for m in range(M)]
+    return np.concatenate(segments, axis=-1)
+
+
+def _valid_len(lens, b, max_len):
+    return int(min(max(int(lens[b]), 0), max_len))
+
+
+def attention_weights(q_row: np.ndarray, k_hat: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax over t of scale * q . K_t, computed stably (max subtracted)."""
+    s = scale * (k_hat @ q_row.astype(np.float64))
+    s = s - s.max()
+    e = np.exp(s)
+    return e / e.sum()
+
+
+def decode_attention(q, k_codes, v_codes, k_cb, v_cb, lens, scale=None):
+    """Single-token decode attention over a PQ-coded KV cache, the plain way.
+
+    q        fp16 [B, Hq, D]
+    k_codes  uint8 [B, Hkv, Lmax, M]     v_codes the same
+    k_cb     fp16 [Hkv, M, K, D/M]       v_cb the same
+    lens     int [B]; tokens t < lens[b] are attended (clamped to [0, Lmax])
+    returns  float64 [B, Hq, D]; a request with no tokens gives zeros.
+    """
+    B, Hq, D = q.shape
+    Hkv, Lmax = k_codes.shape[1], k_codes.shape[2]
+    G = Hq // Hkv
+    if scale is None:
+        scale = default_scale(D)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = _valid_len(lens, b, Lmax)
+        if L == 0:
+            continue
+        for g in range(Hkv):
+            k_hat = reconstruct(k_codes[b, g, :L], k_cb[g])
+            v_hat = reconstruct(v_codes[b, g, :L], v_cb[g])
+            for h in range(g * G, (g + 1) * G):
+                p = attention_weights(q[b, h], k_hat, scale)
+                out[b, h] = p @ v_hat
+    return out
+
+
+def chunk_partials(q, k_codes, v_codes, k_cb, v_cb, lens, chunk, scale=None, n_chunks=None):
+    """Per-chunk softmax statistics (PAM page, section 2.2.3 (1)).
+
+    Chunk c covers tokens [c*chunk, (c+1)*chunk) intersected with
+    [0, lens[b]).  Returns float64 arrays
+      m [B, Hq, C]    max scaled score in the chunk (-inf if empty)
+      l [B, Hq, C]    sum_t exp(s_t - m)            (0 if empty)
+      o [B, Hq, C, D] sum_t exp(s_t - m) V_t        (0 if empty)
+    with C = ceil(Lmax / chunk) unless given.
+    """
+    B, Hq, D = q.shape
+    Hkv, Lmax = k_codes.shape[1], k_codes.shape[2]
+    G = Hq // Hkv
+    if scale is None:
+        scale = default_scale(D)
+    C = n_chunks if n_chunks is not None else max(1, -(-Lmax // chunk))
+    m = np.full((B, Hq, C), -np.inf)
+    l = np.zeros((B, Hq, C))
+    o = np.zeros((B, Hq, C, D))
+    for b in range(B):
+        L = _valid_len(lens, b, Lmax)
+        for g in range(Hkv):
+            for c in range(C):
+                lo, hi = c * chunk, min((c + 1) * chunk, L)
+                if lo >= hi:
+                    continue
+                k_hat = reconstruct(k_codes[b, g, lo:hi], k_cb[g])
+                v_hat = reconstruct(v_codes[b, g, lo:hi], v_cb[g])
+                for h in range(g * G, (g + 1) * G):
+                    s = scale * (k_hat @ q[b, h].astype(np.float64))
+                    mc = s.max()
+                    e = np.exp(s - mc)
+                    m[b, h, c] = mc
+                    l[b, h, c] = e.sum()
+                    o[b, h, c] = e @ v_hat
+    return m, l, o
+
+
+def merge_partials(m, l, o):
+    """Merge chunk statistics into the final output (PAM page, section
+    2.2.3 (1) and (3); the rescaling of the memory-wall chapter's online
+    softmax, section 1.4.3 (5.1)).
+
+    m, l: [..., C];  o: [..., C, D].  Empty chunks carry m = -inf, l = 0.
+    out = sum_c w_c o_c / sum_c w_c l_c  with  w_c = exp(m_c - max_c m_c);
+    zeros where every chunk is empty.
+    """
+    m = np.asarray(m, dtype=np.float64)
+    l = np.asarray(l, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    m_star = m.max(axis=-1, keepdims=True)
+    finite = np.isfinite(m_star)
+    safe = np.where(finite, m_star, 0.0)
+    w = np.where(np.isfinite(m), np.exp(m - safe), 0.0)
+    num = (w[..., None] * o).sum(axis=-2)
+    den = (w * l).sum(axis=-1)
+    out = np.zeros(num.shape)
+    ok = den > 0
+    out[ok] = num[ok] / den[ok][..., None]
+    return out
+
+
+def encode(x, cb, block=4096):
+    """Nearest-codeword encode (AQPIM page, sections 3.1 and 5.2 (2)).
+
+    x   fp16 [N, H, D]
+    cb  fp16 [H, M, K, ds]
+    returns uint8 [N, H, M]: per (vector, head, segment) the index k that
+    minimises sum_j (x_j - C[k]_j)^2, computed in float32 from the exact fp16
+    values; the lowest index wins a tie (numpy argmin).
+    """
+    N, H, D = x.shape
+    _, M, K, ds = cb.shape
+    codes = np.empty((N, H, M), dtype=np.uint8)
+    cb32 = cb.astype(np.float32)
+    for lo in range(0, N, block):
+        hi = min(N, lo + block)
+        xs = x[lo:hi].astype(np.float32).reshape(hi - lo, H, M, ds)
+        for h in range(H):
+            for m in range(M):
+                diff = xs[:, h, m, None, :] - cb32[h, m][None, :, :]     # [n, K, ds]
+                d2 = np.einsum("nkj,nkj->nk", diff, diff)
+                codes[lo:hi, h, m] = np.argmin(d2, axis=1).astype(np.uint8)
+    return codes

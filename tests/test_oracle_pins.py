@@ -1,0 +1,411 @@
+"""Pins for the CPU oracle: facts that do not come from the oracle itself.
+
+Each test ties one part of the oracle to the pages' printed numbers, to an
+algebraic identity computed another way, to a closed form on a tiny input,
+or to a library routine (torch's CPU attention, scipy's distances).  The
+cases are chosen so that a plausible slip in the oracle (a dropped scale, a
+swapped subspace order, a transposed codebook, K and V mixed up, the wrong
+GQA head map, a missing max in the merge) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _facts():
+    with open(os.path.join(GOLDEN, "page_facts.json")) as f:
+        return json.load(f)
+
+
+def _small(seed=0, B=2, Hq=4, Hkv=2, L=37, M=4, D=128, lens=None):
+    return gen.random_case(seed, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, max_len=L,
+                           n_sub=M, head_dim=D, lens=lens)[1]
+
+
+# --------------------------------------------------------------------------
+# P1-P3: the pages' printed sizes pin the cache layout and the codebook size
+# --------------------------------------------------------------------------
+
+def test_compression_ratio_64_to_1():
+    f = _facts()["compression"]
+    inp = gen.workload_inputs(2, with_encode=False)
+    one_vec_codes = inp["k_codes"][0, 0, 0]               # M uint8 indices
+    one_vec_dense = oracle.reconstruct(inp["k_codes"][0, 0, :1], inp["k_cb"][0])
+    assert one_vec_codes.nbytes == f["pq_bytes"]
+    assert one_vec_dense.astype(np.float16).nbytes == f["dense_bytes"]
+    assert f["dense_bytes"] // f["pq_bytes"] == f["ratio"]
+
+
+def test_dense_footprint_page_sizing():
+    """B=4, L=2048, H=32, D=128 fp16 K+V is 134,217,728 B per layer; the PQ
+    code arrays of the same workload are 64x smaller."""
+    facts = _facts()
+    inp = gen.workload_inputs(2, with_encode=False)
+    B, H, L, M = inp["k_codes"].shape
+    w = gen.WORKLOADS[2]
+    assert (B, H, L) == (facts["dense_kv_step"]["batch"], facts["dense_kv_step"]["heads"],
+                         facts["dense_kv_layer"]["seq_len"])
+    k_hat = oracle.reconstruct(inp["k_codes"][0, 0], inp["k_cb"][0])      # [L, D]
+    assert k_hat.shape == (L, w.head_dim)
+    dense_layer = 2 * B * H * k_hat.astype(np.float16).nbytes             # K and V
+    assert dense_layer == facts["dense_kv_layer"]["bytes"]
+    assert dense_layer // L == facts["dense_kv_step"]["bytes"]
+    assert round(dense_layer * facts["dense_kv_model"]["layers"] / 1e9, 1) == \
+        facts["dense_kv_model"]["printed_gb"]
+    code_bytes = inp["k_codes"].nbytes + inp["v_codes"].nbytes
+    assert code_bytes == dense_layer // facts["compression"]["ratio"] == 2_097_152
+
+
+def test_codebook_size_64kb():
+    f = _facts()["codebook"]
+    inp = gen.workload_inputs(2, with_encode=False)
+    assert inp["k_cb"].shape[1:] == (f["n_sub"], f["n_codes"], f["sub_dim"])
+    assert inp["k_cb"][0].nbytes == f["bytes"] == f["printed_kb"] * 1024
+
+
+def test_gqa_shape():
+    f = _facts()["gqa"]
+    w = gen.WORKLOADS[3]
+    assert (w.n_q_heads, w.n_kv_heads, w.group) == (f["q_heads"], f["kv_heads"], f["q_per_kv"])
+
+
+# --------------------------------------------------------------------------
+# P4: lookup-table scores equal reconstruct-then-dot (AQPIM page, 4 vs 4.1)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [2, 4, 8])
+def test_lookup_scores_equal_reconstruct_dot(M):
+    inp = _small(seed=M, M=M, L=50)
+    q, kc, cb = inp["q"], inp["k_codes"], inp["k_cb"]
+    D = q.shape[-1]
+    ds = D // M
+    scale = oracle.default_scale(D)
+    b, h, g = 1, 3, 1                        # h=3 reads KV head 3 // 2 = 1
+    # lookup form, written out independently of the oracle
+    qs = q[b, h].astype(np.float64).reshape(M, ds)
+    lut = np.einsum("mj,mkj->mk", qs, cb[g].astype(np.float64))         # [M, K]
+    s_lut = scale * lut[np.arange(M)[None, :], kc[b, g].astype(np.intp)].sum(axis=1)
+    # the oracle's reconstruction, dotted
+    s_rec = scale * oracle.reconstruct(kc[b, g], cb[g]) @ q[b, h].astype(np.float64)
+    np.testing.assert_allclose(s_rec, s_lut, rtol=0, atol=1e-12)
+    # and the oracle's softmax weights agree with the softmax of the lookups
+    p = oracle.attention_weights(q[b, h], oracle.reconstruct(kc[b, g], cb[g]), scale)
+    e = np.exp(s_lut - s_lut.max())
+    np.testing.assert_allclose(p, e / e.sum(), rtol=1e-12, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# P5: softmax weights are a distribution
+# --------------------------------------------------------------------------
+
+def test_weights_sum_to_one():
+    inp = _small(seed=5, L=300)
+    k_hat = oracle.reconstruct(inp["k_codes"][0, 1], inp["k_cb"][1])
+    for h in range(inp["q"].shape[1]):
+        p = oracle.attention_weights(inp["q"][0, h], k_hat, oracle.default_scale(128))
+        assert abs(p.sum() - 1.0) <= 1e-12
+        assert (p > 0).all()
+
+
+# --------------------------------------------------------------------------
+# P6: chunk statistics merged by the reduction equal one pass (PAM page 2.2.3)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("chunk", [1, 7, 16, 2048, 61])
+def test_split_merge_equals_single_pass(chunk):
+    inp = _small(seed=11, L=61, lens=[61, 23])
+    args = [inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")]
+    ref = oracle.decode_attention(*args)
+    m, l, o = oracle.chunk_partials(*args, chunk=chunk)
+    got = oracle.merge_partials(m, l, o)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+    # chunks wholly past lens are empty: (-inf, 0, 0)
+    C = m.shape[-1]
+    for c in range(C):
+        if c * chunk >= 23:
+            assert np.isneginf(m[1, :, c]).all() and (l[1, :, c] == 0).all() and (o[1, :, c] == 0).all()
+
+
+def test_uneven_splits_merge():
+    """Token ranges cut at random points (as if held by different devices)."""
+    rng = np.random.default_rng(3)
+    inp = _small(seed=12, B=1, L=97, lens=[97])
+    args = [inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb")]
+    ref = oracle.decode_attention(*args, inp["lens"])
+    for _ in range(5):
+        cuts = np.sort(rng.choice(np.arange(1, 97), size=4, replace=False))
+        edges = [0, *cuts.tolist(), 97]
+        ms, ls, os_ = [], [], []
+        for a, b in zip(edges[:-1], edges[1:]):
+            sub = [args[0], args[1][:, :, a:b], args[2][:, :, a:b], args[3], args[4]]
+            m, l, o = oracle.chunk_partials(*sub, np.array([b - a]), chunk=b - a)
+            ms.append(m), ls.append(l), os_.append(o)
+        got = oracle.merge_partials(np.concatenate(ms, -1), np.concatenate(ls, -1),
+                                    np.concatenate(os_, -2))
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_merge_is_shift_invariant_and_needs_the_max():
+    """Adding a constant to every score leaves the output unchanged; the merge
+    must rescale by exp(m_c - m*) (a merge that forgets m_c fails here)."""
+    rng = np.random.default_rng(0)
+    m = rng.normal(size=(3, 5)) * 10
+    l = rng.uniform(0.5, 2, size=(3, 5))
+    o = rng.normal(size=(3, 5, 4))
+    out = oracle.merge_partials(m, l, o)
+    manual = np.zeros((3, 4))
+    for i in range(3):
+        w = np.exp(m[i] - m[i].max())
+        manual[i] = (w[:, None] * o[i]).sum(0) / (w * l[i]).sum()
+    np.testing.assert_allclose(out, manual, rtol=1e-13)
+    # a chunk whose max is 30 above the others dominates completely
+    m2 = np.array([[0.0, 30.0]])
+    l2 = np.array([[1.0, 1.0]])
+    o2 = np.array([[[1.0], [2.0]]])
+    assert abs(oracle.merge_partials(m2, l2, o2)[0, 0] - 2.0) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# P7: V through per-codeword probability histograms equals sum_t p_t V_t
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [4, 8])
+def test_histogram_v_identity(M):
+    inp = _small(seed=20 + M, M=M, L=80, lens=[80, 41])
+    q, kc, vc, kcb, vcb, lens = (inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens"))
+    out = oracle.decode_attention(q, kc, vc, kcb, vcb, lens)
+    D = q.shape[-1]
+    ds, K = D // M, vcb.shape[2]
+    G = q.shape[1] // kcb.shape[0]
+    for b in range(q.shape[0]):
+        L = int(lens[b])
+        for h in range(q.shape[1]):
+            g = h // G
+            p = oracle.attention_weights(q[b, h], oracle.reconstruct(kc[b, g, :L], kcb[g]),
+                                         oracle.default_scale(D))
+            hist = np.zeros((M, K))
+            for m in range(M):
+                np.add.at(hist[m], vc[b, g, :L, m].astype(np.intp), p)
+            o = np.concatenate([hist[m] @ vcb[g, m].astype(np.float64) for m in range(M)])
+            np.testing.assert_allclose(out[b, h], o, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P8: closed forms and brute force on tiny inputs
+# --------------------------------------------------------------------------
+
+def _vhat_loop(vc_row, vcb_g):
+    """One V vector rebuilt by an explicit loop over subspaces."""
+    M = vcb_g.shape[0]
+    out = []
+    for m in range(M):
+        out.extend(float(x) for x in vcb_g[m, int(vc_row[m])])
+    return np.array(out)
+
+
+def test_single_token_returns_its_value():
+    inp = _small(seed=30, L=9, lens=[1, 1])
+    out = oracle.decode_attention(*(inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")))
+    for b in range(2):
+        for h in range(4):
+            g = h // 2
+            np.testing.assert_array_equal(out[b, h], _vhat_loop(inp["v_codes"][b, g, 0], inp["v_cb"][g]))
+
+
+def test_zero_query_gives_mean_of_values():
+    inp = _small(seed=31, L=17)
+    inp["q"][:] = 0
+    out = oracle.decode_attention(*(inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")))
+    for b in range(2):
+        for h in range(4):
+            g = h // 2
+            mean = np.mean([_vhat_loop(inp["v_codes"][b, g, t], inp["v_cb"][g]) for t in range(17)], axis=0)
+            np.testing.assert_allclose(out[b, h], mean, rtol=0, atol=1e-13)
+
+
+def test_equal_keys_give_mean_of_values():
+    inp = _small(seed=32, L=13)
+    inp["k_codes"][:] = inp["k_codes"][:, :, :1, :]   # every token has the same K
+    out = oracle.decode_attention(*(inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")))
+    mean = np.mean([_vhat_loop(inp["v_codes"][0, 1, t], inp["v_cb"][1]) for t in range(13)], axis=0)
+    np.testing.assert_allclose(out[0, 2], mean, rtol=0, atol=1e-13)
+
+
+def test_two_tokens_sigmoid():
+    inp = _small(seed=33, B=1, Hq=1, Hkv=1, L=2)
+    q, kc, vc, kcb, vcb = (inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb"))
+    scale = 1 / math.sqrt(128)
+    s = []
+    for t in range(2):
+        acc = 0.0
+        for m in range(4):
+            for j in range(32):
+                acc += float(q[0, 0, m * 32 + j]) * float(kcb[0, m, int(kc[0, 0, t, m]), j])
+        s.append(scale * acc)
+    p0 = 1 / (1 + math.exp(-(s[0] - s[1])))
+    v0, v1 = _vhat_loop(vc[0, 0, 0], vcb[0]), _vhat_loop(vc[0, 0, 1], vcb[0])
+    out = oracle.decode_attention(q, kc, vc, kcb, vcb, np.array([2]))
+    np.testing.assert_allclose(out[0, 0], p0 * v0 + (1 - p0) * v1, rtol=0, atol=1e-13)
+
+
+def test_brute_force_tiny_loops():
+    """B=1, H=1, M=2, K=4, D=4, L<=4, written as plain loops."""
+    rng = np.random.default_rng(34)
+    D, M, K = 4, 2, 4
+    ds = D // M
+    kcb = rng.standard_normal((1, M, K, ds)).astype(np.float16)
+    vcb = rng.standard_normal((1, M, K, ds)).astype(np.float16)
+    q = rng.standard_normal((1, 1, D)).astype(np.float16)
+    for L in range(1, 5):
+        kc = rng.integers(0, K, (1, 1, 4, M), dtype=np.uint8)
+        vc = rng.integers(0, K, (1, 1, 4, M), dtype=np.uint8)
+        scores = []
+        for t in range(L):
+            acc = 0.0
+            for d in range(D):
+                m, j = divmod(d, ds)
+                acc += float(q[0, 0, d]) * float(kcb[0, m, kc[0, 0, t, m], j])
+            scores.append(acc / math.sqrt(D))
+        mx = max(scores)
+        w = [math.exp(s - mx) for s in scores]
+        z = sum(w)
+        expect = [0.0] * D
+        for t in range(L):
+            for d in range(D):
+                m, j = divmod(d, ds)
+                expect[d] += w[t] / z * float(vcb[0, m, vc[0, 0, t, m], j])
+        got = oracle.decode_attention(q, kc, vc, kcb, vcb, np.array([L]))
+        np.testing.assert_allclose(got[0, 0], expect, rtol=0, atol=1e-14)
+
+
+def test_tokens_past_lens_do_not_matter_and_empty_gives_zero():
+    inp = _small(seed=35, L=40, lens=[17, 0])
+    args = [inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")]
+    ref = oracle.decode_attention(*args)
+    assert (ref[1] == 0).all()
+    inp["k_codes"][:, :, 17:] ^= 0x5A
+    inp["v_codes"][:, :, 17:] ^= 0xA5
+    again = oracle.decode_attention(*(inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")))
+    np.testing.assert_array_equal(again, ref)
+    # lens beyond the capacity is clamped
+    clamp = oracle.decode_attention(*args[:5], np.array([40, 0]))
+    big = oracle.decode_attention(*args[:5], np.array([1000, -3]))
+    np.testing.assert_array_equal(big, clamp)
+
+
+def test_gqa_head_map():
+    """Query head h attends KV head h // G: head 5 of 8 with 2 KV heads
+    equals single-head attention over KV head 1's cache."""
+    inp = _small(seed=36, B=1, Hq=8, Hkv=2, L=21)
+    full = oracle.decode_attention(*(inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")))
+    one = oracle.decode_attention(inp["q"][:, 5:6], inp["k_codes"][:, 1:2], inp["v_codes"][:, 1:2],
+                                  inp["k_cb"][1:2], inp["v_cb"][1:2], inp["lens"])
+    np.testing.assert_array_equal(full[:, 5], one[:, 0])
+    other = oracle.decode_attention(inp["q"][:, 5:6], inp["k_codes"][:, 0:1], inp["v_codes"][:, 0:1],
+                                    inp["k_cb"][0:1], inp["v_cb"][0:1], inp["lens"])
+    assert np.abs(full[:, 5] - other[:, 0]).max() > 1e-3
+
+
+# --------------------------------------------------------------------------
+# P9: special case that is dense attention -> torch's CPU SDPA in float64
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_identity_codes_reduce_to_dense_attention(M):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(40 + M)
+    D, K, L = 128, 256, 200
+    ds = D // M
+    kcb = rng.standard_normal((1, M, K, ds)).astype(np.float16)
+    vcb = rng.standard_normal((1, M, K, ds)).astype(np.float16)
+    q = rng.standard_normal((1, 1, D)).astype(np.float16)
+    codes = np.repeat(np.arange(L, dtype=np.uint8)[:, None], M, axis=1)[None, None]  # codes[t, m] = t
+    out = oracle.decode_attention(q, codes, codes, kcb, vcb, np.array([L]))
+    # token t is row t of every codebook, segments side by side
+    Kd = np.concatenate([kcb[0, m, :L] for m in range(M)], axis=1).astype(np.float64)
+    Vd = np.concatenate([vcb[0, m, :L] for m in range(M)], axis=1).astype(np.float64)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64)).view(1, 1, 1, D),
+        torch.from_numpy(Kd).view(1, 1, L, D), torch.from_numpy(Vd).view(1, 1, L, D))
+    np.testing.assert_allclose(out[0, 0], ref.view(D).numpy(), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P10: encode = nearest codeword
+# --------------------------------------------------------------------------
+
+def _fp64_distances(x, cb):
+    N, H, D = x.shape
+    _, M, K, ds = cb.shape
+    xs = x.astype(np.float64).reshape(N, H, M, ds)
+    c = cb.astype(np.float64)
+    return ((xs[:, :, :, None, :] - c[None]) ** 2).sum(-1)      # [N, H, M, K]
+
+
+def test_encode_recovers_source_codes_tiny_workload():
+    inp = gen.workload_inputs(1)
+    for x, cb, src in ((inp["x_k"], inp["k_cb"], inp["src_k"]), (inp["x_v"], inp["v_cb"], inp["src_v"])):
+        codes = oracle.encode(x, cb)
+        np.testing.assert_array_equal(codes, src)
+        d = np.sort(_fp64_distances(x, cb), axis=-1)
+        assert (d[..., 1] - d[..., 0]).min() > 1e-4
+
+
+def test_encode_matches_scipy_cdist():
+    spatial = pytest.importorskip("scipy.spatial")
+    rng = np.random.default_rng(50)
+    H, M, K, ds = 3, 4, 256, 32
+    cb = rng.standard_normal((H, M, K, ds)).astype(np.float16)
+    x = rng.standard_normal((300, H, M * ds)).astype(np.float16)     # far from codewords
+    codes = oracle.encode(x, cb)
+    for h in range(H):
+        for m in range(M):
+            d = spatial.distance.cdist(x[:, h, m * ds:(m + 1) * ds].astype(np.float64),
+                                       cb[h, m].astype(np.float64), "sqeuclidean")
+            srt = np.sort(d, axis=1)
+            clear = (srt[:, 1] - srt[:, 0]) > 1e-3          # fp32 and fp64 agree there
+            assert clear.mean() > 0.9
+            np.testing.assert_array_equal(codes[clear, h, m], d.argmin(1)[clear])
+
+
+def test_encode_ties_take_lowest_index():
+    rng = np.random.default_rng(51)
+    cb = rng.standard_normal((1, 2, 8, 4)).astype(np.float16)
+    cb[0, 0, 6] = cb[0, 0, 2]
+    cb[0, 1, 7] = cb[0, 1, 5]
+    x = np.concatenate([cb[0, 0, 6], cb[0, 1, 7]])[None, None, :]
+    np.testing.assert_array_equal(oracle.encode(x, cb)[0, 0], [2, 5])
+
+
+def test_encode_ragged_workload_sample():
+    """A sample of the ragged workload's prefill vectors (sigma = 0.1)."""
+    w = gen.WORKLOADS[5]
+    rng = gen.rng_for(5)
+    cb = gen.codebooks(rng, w.n_kv_heads, w.n_sub, w.n_codes, w.sub_dim)
+    x, src = gen.noisy_codewords(rng, cb, 64, w.encode_sigma)
+    np.testing.assert_array_equal(oracle.encode(x, cb), src)
+    d = np.sort(_fp64_distances(x, cb), axis=-1)
+    assert (d[..., 1] - d[..., 0]).min() > 1e-2
+
+
+# --------------------------------------------------------------------------
+# P11: the tiny workload's shapes
+# --------------------------------------------------------------------------
+
+def test_tiny_workload_shapes():
+    inp = gen.workload_inputs(1)
+    assert inp["q"].shape == (1, 8, 128) and inp["q"].dtype == np.float16
+    assert inp["k_cb"].shape == (8, 4, 256, 32) and inp["k_cb"].dtype == np.float16
+    assert inp["k_codes"].shape == (1, 8, 512, 4) and inp["k_codes"].dtype == np.uint8
+    out = oracle.decode_attention(*(inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")))
+    assert out.shape == (1, 8, 128)
+    assert np.isfinite(out).all()
+    assert abs(oracle.default_scale(128) - 1 / math.sqrt(128)) < 1e-15
