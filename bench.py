@@ -1,0 +1,217 @@
+"""Benchmark of one decode step over a PQ-coded KV cache on one MI355X.
+
+A step is the whole hot path for one layer and one new token:
+  1. encode the new token's K and V vectors (B*Hkv each) by nearest codeword
+     straight into the code cache, at position lens[b]-1;
+  2. the fused score kernel (LUT build, code streaming, chunk softmax,
+     V histograms, codebook contraction) -> per-chunk (m, l, o);
+  3. the chunk-merge kernel -> out.
+The workload is the GQA decode shape (B=8, Hq=64, Hkv=8, L=8192, M=8,
+K=256).  Inputs live in HBM before timing starts; N seeded replicas of every
+input are rotated so that the working set (>= 512 MiB) is twice the 256 MB
+Infinity Cache and each step reads its codes from HBM.
+
+Prints one JSON line.  `value` = KV tokens scanned per second over the timed
+steps (sum of lens per step / step time).  `roofline` is the score kernel's
+algorithmic bytes per launch over its average duration, timed with HIP
+events around each launch on the stream it runs on.  `cpu_baseline` is the
+CPU oracle on the same workload (repeated for 10+ s), on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD_IDS = {"tiny": 1, "page-sizing": 2, "gqa": 3, "long-splitk": 4, "ragged": 5}
+
+
+def algorithmic_bytes(w, lens):
+    """What the method must move for one decode step: the valid K and V codes,
+    both codebooks once per KV head, q (fp16) and out (fp32)."""
+    codes = int(np.sum(lens)) * w.n_kv_heads * 2 * w.n_sub
+    cbs = w.n_kv_heads * 2 * w.n_sub * w.n_codes * w.sub_dim * 2
+    q = w.batch * w.n_q_heads * w.head_dim * 2
+    out = w.batch * w.n_q_heads * w.head_dim * 4
+    return codes + cbs + q + out
+
+
+def cpu_baseline(wid, min_seconds=10.0, max_seconds=30.0):
+    import oracle
+    from synth import gen
+    inp = gen.workload_inputs(wid, with_encode=False)
+    args = [inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")]
+    tokens = int(inp["lens"].sum())
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.decode_attention(*args)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or el + el / reps > max_seconds:
+            break
+    return {"value": tokens * reps / el, "unit": "KV tokens/s", "cores": _oracle_threads(),
+            "kind": "oracle",
+            "sample": f"{gen.WORKLOADS[wid].name} workload, whole decode step, repeated {reps}x "
+                      f"({el:.1f} s)"}
+
+
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return int(max(n)) if n else 1
+    except Exception:
+        return 1
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="gqa", choices=sorted(WORKLOAD_IDS))
+    ap.add_argument("--replicas", type=int, default=0, help="0: enough for 512 MiB")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this library has no "
+              "multi-GPU path; see the sharding notes in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_product_amd as pq
+    from synth import gen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pq.load_library()
+    wid = WORKLOAD_IDS[args.workload]
+    w = gen.WORKLOADS[wid]
+    if w.prefill_encode:
+        print("the ragged workload's decode step is benchmarked without its prefill", file=sys.stderr)
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, L, M, D = w.batch, w.n_q_heads, w.n_kv_heads, w.max_len, w.n_sub, w.head_dim
+
+    base = gen.workload_inputs(wid, with_encode=False)
+    per_rep = sum(base[k].nbytes for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb"))
+    R = args.replicas or max(2, math.ceil((512 << 20) / per_rep))
+    reps = []
+    for r in range(R):
+        inp = base if r == 0 else gen.workload_inputs(wid, replica=r, with_encode=False)
+        rng = np.random.default_rng([7000 + wid, r])
+        xk = rng.standard_normal((B, Hkv, D), dtype=np.float32).astype(np.float16)
+        xv = rng.standard_normal((B, Hkv, D), dtype=np.float32).astype(np.float16)
+        t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev)
+             for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")}
+        t["xk"] = torch.from_numpy(xk).to(dev)
+        t["xv"] = torch.from_numpy(xv).to(dev)
+        lens = inp["lens"].astype(np.int64)
+        slots = np.arange(B, dtype=np.int64) * Hkv * L + np.maximum(lens - 1, 0)
+        t["slots"] = torch.from_numpy(slots).to(dev)
+        reps.append(t)
+    lens_np = base["lens"]
+    tokens_per_step = int(lens_np.sum())
+
+    desc = pq.attn_desc(reps[0]["q"], reps[0]["k_codes"], reps[0]["k_cb"], chunk=args.chunk)
+    C = pq.pq_attn_num_chunks(desc)
+    enc_desc = pq.cache_encode_desc(B, B, Hkv, L, n_sub=M)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    pm = torch.empty((B, Hq, C), dtype=torch.float32, device=dev)
+    pl = torch.empty((B, Hq, C), dtype=torch.float32, device=dev)
+    po = torch.empty((B, Hq, C, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(t, ev=None):
+        pq.pq_encode(t["xk"], t["k_cb"], t["k_codes"], slots=t["slots"], desc=enc_desc, stream=stream)
+        pq.pq_encode(t["xv"], t["v_cb"], t["v_codes"], slots=t["slots"], desc=enc_desc, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        if C > 1:
+            pq.pq_attn_partials(t["q"], t["k_codes"], t["v_codes"], t["k_cb"], t["v_cb"], t["lens"],
+                                desc=desc, part_m=pm, part_l=pl, part_o=po, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            pq.pq_attn_reduce(pm, pl, po, out, stream=stream)
+        else:
+            pq.pq_attn_decode(t["q"], t["k_codes"], t["v_codes"], t["k_cb"], t["v_cb"], t["lens"],
+                              out, desc=desc, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(reps[i % R])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    # (a) the timed region: K whole steps, events around each score kernel
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(reps[i % R], evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = start.elapsed_time(end) / K
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    score_ms = float(np.mean(kern_ms))
+
+    # (b) the same steps without the per-kernel events (the throughput figure)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        step(reps[i % R])
+    end.record(stream)
+    torch.cuda.synchronize()
+    step_ms_plain = start.elapsed_time(end) / K
+
+    value = tokens_per_step / (step_ms_plain * 1e-3)
+    alg = algorithmic_bytes(w, lens_np)
+    achieved = alg / (score_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "PQ-KV decode attn: KV tokens scanned/s + % of HBM peak GB/s; encode vectors/s",
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms_plain,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 in / fp32 compute",
+        "data": "synthetic (seeded generators; codebooks and q fp16 N(0,1), codes uniform uint8)",
+        "config": {"workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} L={L} D={D} M={M} K={w.n_codes}",
+                   "chunk": int(desc.chunk) or "library", "n_chunks": C, "replicas": R,
+                   "step": "encode new K,V -> score kernel -> merge kernel"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_partials_kernel", "algorithmic_bytes": alg,
+                     "avg_launch_us": score_ms * 1e3},
+        "detail": {"step_us_with_kernel_events": step_ms * 1e3, "step_us": step_ms_plain * 1e3,
+                   "score_kernel_us_p50": float(np.median(kern_ms)) * 1e3,
+                   "wall_s": wall, "tokens_per_step": tokens_per_step},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wid)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

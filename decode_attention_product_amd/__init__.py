@@ -1,0 +1,253 @@
+"""Python binding of the PQ-KV decode-attention library (libpqattn.so).
+
+Argument marshalling only: torch tensors supply device memory and the
+stream, every step of the computation runs in the library's HIP kernels.
+The functions carry the C entry points' names; see include/pqattn.h for
+the contract of each.  There is no fallback: if the library is missing or
+cannot be loaded, importing the functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpqattn.so")
+
+PQ_OK = 0
+STATUS_NAMES = {0: "PQ_OK", 1: "PQ_ERR_NULL", 2: "PQ_ERR_SHAPE", 3: "PQ_ERR_UNSUPPORTED",
+                4: "PQ_ERR_WORKSPACE", 5: "PQ_ERR_HIP", 6: "PQ_ERR_ALIGN"}
+
+EXPORTED = ("pq_attn_num_chunks", "pq_attn_workspace_bytes", "pq_attn_decode",
+            "pq_attn_partials", "pq_attn_reduce", "pq_encode", "pq_status_string")
+
+
+class PQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+class PQAttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("n_sub", ctypes.c_int32), ("n_codes", ctypes.c_int32),
+                ("max_len", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class PQEncodeDesc(ctypes.Structure):
+    _fields_ = [("n_vec", ctypes.c_int64), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("n_sub", ctypes.c_int32),
+                ("n_codes", ctypes.c_int32), ("x_stride_vec", ctypes.c_int64),
+                ("x_stride_head", ctypes.c_int64), ("codes_stride_slot", ctypes.c_int64),
+                ("codes_stride_head", ctypes.c_int64), ("codes_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpqattn.so once; raises if it is missing (build it first with
+    ``python -m decode_attention_product_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m decode_attention_product_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.pq_attn_num_chunks.argtypes = [ctypes.POINTER(PQAttnDesc)]
+    lib.pq_attn_num_chunks.restype = ctypes.c_int32
+    lib.pq_attn_workspace_bytes.argtypes = [ctypes.POINTER(PQAttnDesc)]
+    lib.pq_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.pq_attn_decode.argtypes = [ctypes.POINTER(PQAttnDesc), P, P, P, P, P, P, P, P,
+                                   ctypes.c_size_t, P]
+    lib.pq_attn_decode.restype = ctypes.c_int
+    lib.pq_attn_partials.argtypes = [ctypes.POINTER(PQAttnDesc), P, P, P, P, P, P, P, P, P, P]
+    lib.pq_attn_partials.restype = ctypes.c_int
+    lib.pq_attn_reduce.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
+    lib.pq_attn_reduce.restype = ctypes.c_int
+    lib.pq_encode.argtypes = [ctypes.POINTER(PQEncodeDesc), P, P, P, P, P]
+    lib.pq_encode.restype = ctypes.c_int
+    lib.pq_status_string.argtypes = [ctypes.c_int]
+    lib.pq_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().pq_status_string(int(status)).decode()
+
+
+pq_status_string = status_string
+
+
+def _check(status: int, where: str):
+    if status != PQ_OK:
+        raise PQError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _need(t, name, dtype, shape=None, device=True):
+    import torch
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor")
+    del torch
+
+
+def attn_desc(q, k_codes, k_cb, *, chunk: int = 0, scale: Optional[float] = None) -> PQAttnDesc:
+    """Descriptor from tensor shapes: q [B,Hq,D], k_codes [B,Hkv,Lmax,M],
+    k_cb [Hkv,M,K,D/M]."""
+    B, Hq, D = q.shape
+    _, Hkv, Lmax, M = k_codes.shape
+    K = k_cb.shape[2]
+    return PQAttnDesc(B, Hq, Hkv, D, M, K, Lmax, int(chunk),
+                      float(scale if scale is not None else 1.0 / math.sqrt(D)))
+
+
+def pq_attn_num_chunks(desc: PQAttnDesc) -> int:
+    return int(load_library().pq_attn_num_chunks(ctypes.byref(desc)))
+
+
+def pq_attn_workspace_bytes(desc: PQAttnDesc) -> int:
+    return int(load_library().pq_attn_workspace_bytes(ctypes.byref(desc)))
+
+
+def _check_attn_inputs(desc, q, k_codes, v_codes, k_cb, v_cb, lens):
+    import torch
+    B, Hq, Hkv, D = desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim
+    M, K, L = desc.n_sub, desc.n_codes, desc.max_len
+    _need(q, "q", torch.float16, (B, Hq, D))
+    _need(k_codes, "k_codes", torch.uint8, (B, Hkv, L, M))
+    _need(v_codes, "v_codes", torch.uint8, (B, Hkv, L, M))
+    _need(k_cb, "k_cb", torch.float16, (Hkv, M, K, D // M))
+    _need(v_cb, "v_cb", torch.float16, (Hkv, M, K, D // M))
+    _need(lens, "lens", torch.int32, (B,))
+
+
+def pq_attn_decode(q, k_codes, v_codes, k_cb, v_cb, lens, out=None, *, desc=None, chunk=0,
+                   scale=None, workspace=None, stream=None):
+    """One decode step (C entry point pq_attn_decode).  Returns ``out``
+    (fp32 [B, Hq, D]), allocated if not given.  The workspace is allocated
+    through torch when not given."""
+    import torch
+    if desc is None:
+        desc = attn_desc(q, k_codes, k_cb, chunk=chunk, scale=scale)
+    _check_attn_inputs(desc, q, k_codes, v_codes, k_cb, v_cb, lens)
+    if out is None:
+        out = torch.empty((desc.batch, desc.n_q_heads, desc.head_dim), dtype=torch.float32,
+                          device=q.device)
+    _need(out, "out", torch.float32, (desc.batch, desc.n_q_heads, desc.head_dim))
+    ws_bytes = pq_attn_workspace_bytes(desc)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().pq_attn_decode(
+        ctypes.byref(desc), _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_cb), _ptr(v_cb),
+        _ptr(lens), _ptr(out), _ptr(workspace), nbytes, _stream(stream))
+    _check(st, "pq_attn_decode")
+    return out
+
+
+def pq_attn_partials(q, k_codes, v_codes, k_cb, v_cb, lens, *, desc=None, chunk=0, scale=None,
+                     part_m=None, part_l=None, part_o=None, stream=None):
+    """Chunk statistics (C entry point pq_attn_partials).  Returns
+    (part_m [B,Hq,C], part_l [B,Hq,C], part_o [B,Hq,C,D]), fp32."""
+    import torch
+    if desc is None:
+        desc = attn_desc(q, k_codes, k_cb, chunk=chunk, scale=scale)
+    _check_attn_inputs(desc, q, k_codes, v_codes, k_cb, v_cb, lens)
+    C = pq_attn_num_chunks(desc)
+    if C < 1:
+        _check(load_library().pq_attn_partials(ctypes.byref(desc), *([None] * 10)),
+               "pq_attn_partials")
+    B, Hq, D = desc.batch, desc.n_q_heads, desc.head_dim
+    dev = q.device
+    part_m = torch.empty((B, Hq, C), dtype=torch.float32, device=dev) if part_m is None else part_m
+    part_l = torch.empty((B, Hq, C), dtype=torch.float32, device=dev) if part_l is None else part_l
+    part_o = torch.empty((B, Hq, C, D), dtype=torch.float32, device=dev) if part_o is None else part_o
+    _need(part_m, "part_m", torch.float32, (B, Hq, C))
+    _need(part_l, "part_l", torch.float32, (B, Hq, C))
+    _need(part_o, "part_o", torch.float32, (B, Hq, C, D))
+    st = load_library().pq_attn_partials(
+        ctypes.byref(desc), _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_cb), _ptr(v_cb),
+        _ptr(lens), _ptr(part_m), _ptr(part_l), _ptr(part_o), _stream(stream))
+    _check(st, "pq_attn_partials")
+    return part_m, part_l, part_o
+
+
+def pq_attn_reduce(part_m, part_l, part_o, out=None, *, stream=None):
+    """Merge chunk statistics (C entry point pq_attn_reduce).  part_m and
+    part_l [..., C], part_o [..., C, D]; returns out [..., D] fp32."""
+    import torch
+    C, D = part_o.shape[-2], part_o.shape[-1]
+    lead = tuple(part_o.shape[:-2])
+    rows = 1
+    for s in lead:
+        rows *= s
+    _need(part_m, "part_m", torch.float32, (*lead, C))
+    _need(part_l, "part_l", torch.float32, (*lead, C))
+    _need(part_o, "part_o", torch.float32)
+    if out is None:
+        out = torch.empty((*lead, D), dtype=torch.float32, device=part_o.device)
+    _need(out, "out", torch.float32, (*lead, D))
+    st = load_library().pq_attn_reduce(rows, C, D, _ptr(part_m), _ptr(part_l), _ptr(part_o),
+                                       _ptr(out), _stream(stream))
+    _check(st, "pq_attn_reduce")
+    return out
+
+
+def pq_encode(x, codebook, codes, *, slots=None, desc=None, stream=None):
+    """Nearest-codeword encode (C entry point pq_encode).
+
+    Default layout (desc None): x fp16 [N, H, D] and codes uint8 [N, H, M],
+    both contiguous.  Pass ``desc`` (a PQEncodeDesc) for strided layouts, e.g.
+    writing straight into a [B, Hkv, Lmax, M] code cache through ``slots``."""
+    import torch
+    _need(x, "x", torch.float16, None)
+    _need(codebook, "codebook", torch.float16, None)
+    _need(codes, "codes", torch.uint8, None)
+    if slots is not None:
+        _need(slots, "slots", torch.int64, None)
+    if desc is None:
+        N, H, D = x.shape
+        _, M, K, _ = codebook.shape
+        _need(codes, "codes", torch.uint8, (N, H, M))
+        desc = PQEncodeDesc(N, H, D, M, K, H * D, D, H * M, M, codes.numel())
+    st = load_library().pq_encode(ctypes.byref(desc), _ptr(x), _ptr(codebook), _ptr(slots),
+                                  _ptr(codes), _stream(stream))
+    _check(st, "pq_encode")
+    return codes
+
+
+def cache_encode_desc(n_vec, batch, n_kv_heads, max_len, head_dim=128, n_sub=4, n_codes=256,
+                      x_stride_vec=None):
+    """Descriptor that writes the codes of x [N, Hkv, D] (rows x_stride_vec
+    apart) into a [B, Hkv, Lmax, M] code cache at token slots
+    s = b*Hkv*Lmax + t (pass them as the slots tensor)."""
+    if x_stride_vec is None:
+        x_stride_vec = n_kv_heads * head_dim
+    return PQEncodeDesc(n_vec, n_kv_heads, head_dim, n_sub, n_codes, x_stride_vec, head_dim,
+                        n_sub, max_len * n_sub, batch * n_kv_heads * max_len * n_sub)

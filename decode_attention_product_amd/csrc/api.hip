@@ -1,0 +1,189 @@
+// C entry points of the PQ-KV decode-attention library (declared in
+// include/pqattn.h).  Each call checks its arguments on the host, picks the
+// kernel instance for the shape and enqueues it on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "decode_kernel.hpp"
+#include "encode_kernel.hpp"
+#include "plan.h"
+#include "pqattn.h"
+
+namespace pqattn {
+namespace {
+
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeTokensPerThread = 4;
+constexpr int kReduceThreads = 128;
+constexpr int kEncodeThreads = 256;
+constexpr int kEncodeVectors = 128;
+
+using DecodeFn = void (*)(DecodeArgs);
+
+template <int G, int M>
+DecodeFn decode_instance() {
+  return &decode_partials_kernel<G, M, kDecodeTokensPerThread, kDecodeThreads>;
+}
+
+DecodeFn pick_decode(int G, int M) {
+  switch (M * 16 + G) {
+    case 4 * 16 + 1: return decode_instance<1, 4>();
+    case 4 * 16 + 2: return decode_instance<2, 4>();
+    case 4 * 16 + 4: return decode_instance<4, 4>();
+    case 4 * 16 + 8: return decode_instance<8, 4>();
+    case 8 * 16 + 1: return decode_instance<1, 8>();
+    case 8 * 16 + 2: return decode_instance<2, 8>();
+    case 8 * 16 + 4: return decode_instance<4, 8>();
+    case 8 * 16 + 8: return decode_instance<8, 8>();
+  }
+  return nullptr;
+}
+
+pq_status launch(const void* fn, dim3 grid, dim3 block, void* arg, hipStream_t stream) {
+  void* args[] = {arg};
+  const hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
+  return e == hipSuccess ? PQ_OK : PQ_ERR_HIP;
+}
+
+pq_status check_attn_pointers(const void* q, const void* kc, const void* vc, const void* kcb,
+                              const void* vcb, const void* lens) {
+  if (!q || !kc || !vc || !kcb || !vcb || !lens) return PQ_ERR_NULL;
+  if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(kcb) || !aligned16(vcb))
+    return PQ_ERR_ALIGN;
+  return PQ_OK;
+}
+
+pq_status launch_partials(const AttnPlan& p, const void* q, const uint8_t* kc, const uint8_t* vc,
+                          const void* kcb, const void* vcb, const int32_t* lens, float* pm,
+                          float* pl, float* po, float* out, hipStream_t stream) {
+  DecodeArgs a;
+  a.q = static_cast<const __half*>(q);
+  a.k_codes = kc;
+  a.v_codes = vc;
+  a.k_cb = static_cast<const __half*>(kcb);
+  a.v_cb = static_cast<const __half*>(vcb);
+  a.lens = lens;
+  a.part_m = pm;
+  a.part_l = pl;
+  a.part_o = po;
+  a.out = out;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.Lmax = p.Lmax;
+  a.T = p.T;
+  a.C = p.C;
+  a.qscale = p.scale * kLog2e;
+  DecodeFn fn = pick_decode(p.G, p.M);
+  if (!fn) return PQ_ERR_UNSUPPORTED;
+  return launch(reinterpret_cast<const void*>(fn), dim3(unsigned(p.blocks)), dim3(kDecodeThreads),
+                &a, stream);
+}
+
+pq_status launch_reduce(int64_t rows, int32_t C, const float* pm, const float* pl, const float* po,
+                        float* out, hipStream_t stream) {
+  if (rows == 0) return PQ_OK;
+  ReduceArgs a{pm, pl, po, out, C};
+  return launch(reinterpret_cast<const void*>(&reduce_kernel), dim3(unsigned(rows)),
+                dim3(kReduceThreads), &a, stream);
+}
+
+}  // namespace
+}  // namespace pqattn
+
+using namespace pqattn;
+
+extern "C" {
+
+int32_t pq_attn_num_chunks(const pq_attn_desc* desc) {
+  AttnPlan p;
+  return plan_attn(desc, &p) == PQ_OK ? p.C : -1;
+}
+
+size_t pq_attn_workspace_bytes(const pq_attn_desc* desc) {
+  AttnPlan p;
+  return plan_attn(desc, &p) == PQ_OK ? p.ws_bytes : 0;
+}
+
+pq_status pq_attn_decode(const pq_attn_desc* desc, const void* q, const uint8_t* k_codes,
+                         const uint8_t* v_codes, const void* k_cb, const void* v_cb,
+                         const int32_t* lens, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  AttnPlan p;
+  pq_status st = plan_attn(desc, &p);
+  if (st != PQ_OK) return st;
+  st = check_attn_pointers(q, k_codes, v_codes, k_cb, v_cb, lens);
+  if (st != PQ_OK) return st;
+  if (!out) return PQ_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.C == 1)
+    return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, nullptr, nullptr, nullptr,
+                           out, s);
+  if (!workspace || workspace_bytes < p.ws_bytes || !aligned16(workspace)) return PQ_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  float* pm = reinterpret_cast<float*>(ws + p.ws_m_off);
+  float* pl = reinterpret_cast<float*>(ws + p.ws_l_off);
+  float* po = reinterpret_cast<float*>(ws + p.ws_o_off);
+  st = launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, pm, pl, po, nullptr, s);
+  if (st != PQ_OK) return st;
+  return launch_reduce(p.rows, p.C, pm, pl, po, out, s);
+}
+
+pq_status pq_attn_partials(const pq_attn_desc* desc, const void* q, const uint8_t* k_codes,
+                           const uint8_t* v_codes, const void* k_cb, const void* v_cb,
+                           const int32_t* lens, float* part_m, float* part_l, float* part_o,
+                           void* stream) {
+  AttnPlan p;
+  pq_status st = plan_attn(desc, &p);
+  if (st != PQ_OK) return st;
+  st = check_attn_pointers(q, k_codes, v_codes, k_cb, v_cb, lens);
+  if (st != PQ_OK) return st;
+  if (!part_m || !part_l || !part_o) return PQ_ERR_NULL;
+  return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, part_m, part_l, part_o, nullptr,
+                         static_cast<hipStream_t>(stream));
+}
+
+pq_status pq_attn_reduce(int64_t n_rows, int32_t n_chunks, int32_t head_dim, const float* part_m,
+                         const float* part_l, const float* part_o, float* out, void* stream) {
+  pq_status st = check_reduce(n_rows, n_chunks, head_dim);
+  if (st != PQ_OK) return st;
+  if (!part_m || !part_l || !part_o || !out) return PQ_ERR_NULL;
+  return launch_reduce(n_rows, n_chunks, part_m, part_l, part_o, out,
+                       static_cast<hipStream_t>(stream));
+}
+
+pq_status pq_encode(const pq_encode_desc* desc, const void* x, const void* codebook,
+                    const int64_t* slots, uint8_t* codes, void* stream) {
+  EncodePlan p;
+  pq_status st = plan_encode(desc, kEncodeVectors, &p);
+  if (st != PQ_OK) return st;
+  if (!x || !codebook || !codes) return PQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codebook)) return PQ_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(codes) % p.M) != 0) return PQ_ERR_ALIGN;
+  if (p.N == 0) return PQ_OK;
+  if (!slots) {   // identity places: the last one must fit
+    const double last = double(p.N - 1) * double(desc->codes_stride_slot) +
+                        double(p.H - 1) * double(desc->codes_stride_head) + p.M;
+    if (last > double(desc->codes_bytes)) return PQ_ERR_SHAPE;
+  }
+  EncodeArgs a;
+  a.x = static_cast<const __half*>(x);
+  a.cb = static_cast<const __half*>(codebook);
+  a.slots = slots;
+  a.codes = codes;
+  a.N = p.N;
+  a.codes_bytes = desc->codes_bytes;
+  a.sxv = desc->x_stride_vec;
+  a.sxh = desc->x_stride_head;
+  a.scs = desc->codes_stride_slot;
+  a.sch = desc->codes_stride_head;
+  const void* fn = p.M == 4
+      ? reinterpret_cast<const void*>(&encode_kernel<4, kEncodeVectors, kEncodeThreads>)
+      : reinterpret_cast<const void*>(&encode_kernel<8, kEncodeVectors, kEncodeThreads>);
+  return launch(fn, dim3(unsigned(p.blocks_x), unsigned(p.H)), dim3(kEncodeThreads), &a,
+                static_cast<hipStream_t>(stream));
+}
+
+const char* pq_status_string(pq_status status) { return status_string(status); }
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// Host-side argument checking and launch planning (no HIP calls).
+#include "plan.h"
+
+#include <cmath>
+#include <limits>
+
+namespace pqattn {
+
+namespace {
+
+constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
+constexpr int kTargetBlocks = 512;     // two score workgroups per CU (256 CUs)
+constexpr int kChunkGranule = 256;     // one token per thread per pass
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+}  // namespace
+
+int32_t pick_chunk(int32_t B, int32_t Hkv, int32_t Lmax, int32_t target_blocks, int32_t granule) {
+  const int64_t pairs = int64_t(B) * Hkv;
+  int64_t want_chunks = (target_blocks + pairs - 1) / pairs;
+  if (want_chunks < 1) want_chunks = 1;
+  int64_t t = (Lmax + want_chunks - 1) / want_chunks;
+  t = (t + granule - 1) / granule * granule;
+  if (t < granule) t = granule;
+  if (t > Lmax) t = Lmax;
+  return int32_t(t);
+}
+
+pq_status plan_attn(const pq_attn_desc* d, AttnPlan* p) {
+  if (d == nullptr || p == nullptr) return PQ_ERR_NULL;
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 ||
+      d->n_sub < 1 || d->n_codes < 1 || d->max_len < 1 || d->chunk < 0)
+    return PQ_ERR_SHAPE;
+  if (d->n_q_heads % d->n_kv_heads != 0) return PQ_ERR_SHAPE;
+  if (d->head_dim % d->n_sub != 0) return PQ_ERR_SHAPE;
+  if (!std::isfinite(d->scale) || !(d->scale > 0.0f)) return PQ_ERR_SHAPE;
+
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (d->head_dim != kHeadDim || d->n_codes != kCodes) return PQ_ERR_UNSUPPORTED;
+  if (d->n_sub != 4 && d->n_sub != 8) return PQ_ERR_UNSUPPORTED;
+  if (!supported_group(G)) return PQ_ERR_UNSUPPORTED;
+  if (d->max_len % kLenAlign != 0) return PQ_ERR_UNSUPPORTED;
+
+  p->B = d->batch;
+  p->Hq = d->n_q_heads;
+  p->Hkv = d->n_kv_heads;
+  p->G = G;
+  p->D = d->head_dim;
+  p->M = d->n_sub;
+  p->DS = d->head_dim / d->n_sub;
+  p->K = d->n_codes;
+  p->Lmax = d->max_len;
+  p->T = d->chunk > 0 ? (d->chunk < d->max_len ? d->chunk : d->max_len)
+                      : pick_chunk(d->batch, d->n_kv_heads, d->max_len, kTargetBlocks, kChunkGranule);
+  p->C = int32_t((int64_t(p->Lmax) + p->T - 1) / p->T);
+  p->scale = d->scale;
+  p->rows = int64_t(p->B) * p->Hq;
+  p->blocks = int64_t(p->B) * p->Hkv * p->C;
+  if (p->blocks > kMaxBlocks || p->rows > kMaxBlocks) return PQ_ERR_UNSUPPORTED;
+
+  // workspace: m and l [rows][C], o [rows][C][D], each 256-byte aligned
+  const size_t n_stat = size_t(p->rows) * size_t(p->C);
+  if (n_stat > std::numeric_limits<size_t>::max() / (size_t(p->D) * 4 + 8)) return PQ_ERR_SHAPE;
+  if (p->C == 1) {
+    p->ws_m_off = p->ws_l_off = p->ws_o_off = 0;
+    p->ws_bytes = 0;
+  } else {
+    p->ws_m_off = 0;
+    p->ws_l_off = round_up(n_stat * 4, 256);
+    p->ws_o_off = p->ws_l_off + round_up(n_stat * 4, 256);
+    p->ws_bytes = p->ws_o_off + round_up(n_stat * size_t(p->D) * 4, 256);
+  }
+  return PQ_OK;
+}
+
+pq_status plan_encode(const pq_encode_desc* d, int32_t vec_per_block, EncodePlan* p) {
+  if (d == nullptr || p == nullptr) return PQ_ERR_NULL;
+  if (d->n_vec < 0 || d->n_heads < 1 || d->head_dim < 1 || d->n_sub < 1 || d->n_codes < 1)
+    return PQ_ERR_SHAPE;
+  if (d->head_dim % d->n_sub != 0) return PQ_ERR_SHAPE;
+  if (d->x_stride_vec < 0 || d->x_stride_head < 0 || d->codes_stride_slot < 0 ||
+      d->codes_stride_head < 0 || d->codes_bytes < 0)
+    return PQ_ERR_SHAPE;
+  if (d->head_dim != kHeadDim || d->n_codes != kCodes) return PQ_ERR_UNSUPPORTED;
+  if (d->n_sub != 4 && d->n_sub != 8) return PQ_ERR_UNSUPPORTED;
+  // 16-byte rows of x; codes of one (vector, head) written as one M-byte word
+  if (d->x_stride_vec % 8 != 0 || d->x_stride_head % 8 != 0) return PQ_ERR_ALIGN;
+  if (d->codes_stride_slot % d->n_sub != 0 || d->codes_stride_head % d->n_sub != 0)
+    return PQ_ERR_ALIGN;
+  p->N = d->n_vec;
+  p->H = d->n_heads;
+  p->D = d->head_dim;
+  p->M = d->n_sub;
+  p->DS = d->head_dim / d->n_sub;
+  p->K = d->n_codes;
+  p->blocks_x = (d->n_vec + vec_per_block - 1) / vec_per_block;
+  if (p->blocks_x > kMaxBlocks || d->n_heads > 65535) return PQ_ERR_UNSUPPORTED;
+  return PQ_OK;
+}
+
+pq_status check_reduce(int64_t n_rows, int32_t n_chunks, int32_t head_dim) {
+  if (n_rows < 0 || n_chunks < 1 || head_dim < 1) return PQ_ERR_SHAPE;
+  if (head_dim != kHeadDim) return PQ_ERR_UNSUPPORTED;
+  if (n_rows > kMaxBlocks) return PQ_ERR_UNSUPPORTED;
+  return PQ_OK;
+}
+
+const char* status_string(pq_status s) {
+  switch (s) {
+    case PQ_OK: return "ok";
+    case PQ_ERR_NULL: return "a required pointer is NULL";
+    case PQ_ERR_SHAPE: return "descriptor fields are inconsistent or out of range";
+    case PQ_ERR_UNSUPPORTED: return "shape not supported by this library";
+    case PQ_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case PQ_ERR_HIP: return "the HIP runtime refused a launch";
+    case PQ_ERR_ALIGN: return "an array pointer or stride is not suitably aligned";
+  }
+  return "unknown status";
+}
+
+}  // namespace pqattn

@@ -1,0 +1,51 @@
+// Host-side argument checking and launch planning for the PQ-KV attention
+// library.  Pure C++ (no HIP): the same file is compiled into the shared
+// library and into a host-only unit test.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pqattn.h"
+
+namespace pqattn {
+
+constexpr int kHeadDim = 128;   // D supported by the kernels
+constexpr int kCodes = 256;     // K codewords per segment codebook
+constexpr int kLenAlign = 16;   // cache capacity granularity, tokens
+
+// A checked decode-attention shape with the chunking resolved.
+struct AttnPlan {
+  int32_t B, Hq, Hkv, G, D, M, DS, K, Lmax, T, C;
+  float scale;
+  int64_t rows;         // B * Hq
+  int64_t blocks;       // score-kernel workgroups, B * Hkv * C
+  size_t ws_m_off, ws_l_off, ws_o_off, ws_bytes;   // workspace carve-up (C > 1)
+};
+
+// Checks *d and fills *p.  Returns PQ_OK, PQ_ERR_NULL, PQ_ERR_SHAPE or
+// PQ_ERR_UNSUPPORTED.  Never touches the GPU.
+pq_status plan_attn(const pq_attn_desc* d, AttnPlan* p);
+
+// The chunk length the library picks when the caller passes chunk = 0: enough
+// chunks that the score kernel has about `target_blocks` workgroups, each
+// chunk a multiple of `granule` tokens.
+int32_t pick_chunk(int32_t B, int32_t Hkv, int32_t Lmax, int32_t target_blocks, int32_t granule);
+
+struct EncodePlan {
+  int64_t N;
+  int32_t H, D, M, DS, K;
+  int64_t blocks_x;     // vector tiles
+};
+
+pq_status plan_encode(const pq_encode_desc* d, int32_t vec_per_block, EncodePlan* p);
+
+pq_status check_reduce(int64_t n_rows, int32_t n_chunks, int32_t head_dim);
+
+inline bool aligned16(const void* ptr) {
+  return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0;
+}
+
+const char* status_string(pq_status s);
+
+}  // namespace pqattn

@@ -1,0 +1,163 @@
+/*
+ * pqattn.h -- C ABI of the PQ-KV decode-attention library for AMD MI355X
+ * (gfx950).
+ *
+ * What it computes.  A KV cache whose every cached K and V vector of
+ * dimension D is stored as M one-byte indices, one per contiguous segment of
+ * D/M dimensions, into per-head codebooks of K = 256 codewords (product
+ * quantization: AQPIM page, section 3.1; per-layer and per-head codebooks,
+ * section 3.2 (1)).  Attention for one new query token is scored by looking
+ * the query's partial dot products with the codewords up instead of
+ * rebuilding K (AQPIM page, section 4.1; the fused kernel of section
+ * 5.1 (3)), the softmax runs in token chunks whose (max, sum, partial output)
+ * a reduction merges (PAM page, section 2.2.3 (1) and (3)), and new vectors
+ * are encoded by nearest codeword (AQPIM page, section 5.2 (2)).
+ *
+ * Conventions for every call:
+ *  - Array pointers are DEVICE pointers owned by the caller; descriptors are
+ *    host pointers read during the call only.  The library keeps no pointer
+ *    after a call returns and allocates no device memory.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *    stream) and never synchronise.  Results are ready when the stream is.
+ *  - Arguments are checked on the host before anything is enqueued; a
+ *    non-zero pq_status means nothing was launched.  A launch the HIP runtime
+ *    refuses returns PQ_ERR_HIP.  Values inside device arrays cannot be
+ *    checked without a sync: lens[] is clamped to [0, max_len] on the
+ *    device, and every uint8 code is a valid index when K = 256.
+ *  - Two calls that run at the same time need their own workspaces.
+ *  - Supported shapes: head_dim = 128, n_codes = 256, n_sub in {4, 8} (so
+ *    segments of 32 or 16 dims), n_q_heads / n_kv_heads in {1, 2, 4, 8},
+ *    max_len a multiple of 16; q, code and codebook pointers 16-byte
+ *    aligned.  Other valid shapes return PQ_ERR_UNSUPPORTED.
+ */
+#ifndef PQATTN_H
+#define PQATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pq_status {
+  PQ_OK = 0,
+  PQ_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  PQ_ERR_SHAPE = 2,       /* descriptor fields inconsistent or out of range     */
+  PQ_ERR_UNSUPPORTED = 3, /* consistent, but a shape this library does not build */
+  PQ_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned         */
+  PQ_ERR_HIP = 5,         /* the HIP runtime refused a launch                   */
+  PQ_ERR_ALIGN = 6        /* an array pointer is not 16-byte aligned            */
+} pq_status;
+
+/* Shape of one decode step of one layer. */
+typedef struct pq_attn_desc {
+  int32_t batch;       /* B, >= 1                                                */
+  int32_t n_q_heads;   /* Hq; query head h reads KV head h / (Hq / Hkv)          */
+  int32_t n_kv_heads;  /* Hkv; Hq % Hkv == 0                                     */
+  int32_t head_dim;    /* D                                                      */
+  int32_t n_sub;       /* M segments per vector, D % M == 0                      */
+  int32_t n_codes;     /* K codewords per segment codebook                       */
+  int32_t max_len;     /* Lmax: cache capacity in tokens per (b, kv head)        */
+  int32_t chunk;       /* T tokens per softmax chunk; 0 lets the library pick    */
+  float   scale;       /* score scale, normally 1/sqrt(D); must be finite, > 0   */
+} pq_attn_desc;
+
+/* Number of chunks C = ceil(max_len / T) the call will use (T resolved when
+ * desc->chunk is 0), or -1 if the descriptor is invalid or unsupported. */
+int32_t pq_attn_num_chunks(const pq_attn_desc* desc);
+
+/* Workspace pq_attn_decode needs: 0 when C == 1, else room for the chunk
+ * statistics of every (b, query head), B*Hq*C*(D+2)*4 bytes rounded up to
+ * 256-byte blocks.  Returns 0 for an invalid descriptor as well. */
+size_t pq_attn_workspace_bytes(const pq_attn_desc* desc);
+
+/* One decode step: out[b][h] = softmax_t(scale * q[b][h] . K_t) V_t over the
+ * tokens t < lens[b] of KV head h / G, K_t and V_t being the codewords the
+ * cache's indices name, laid side by side (AQPIM page, sections 3.1 and 4.1;
+ * chunked softmax and merge per PAM page, section 2.2.3).
+ *
+ *  q        fp16  [B][Hq][D]
+ *  k_codes  uint8 [B][Hkv][max_len][M]  token-major, M bytes per token
+ *  v_codes  uint8 [B][Hkv][max_len][M]
+ *  k_cb     fp16  [Hkv][M][K][D/M]      K codebooks
+ *  v_cb     fp16  [Hkv][M][K][D/M]      V codebooks
+ *  lens     int32 [B]                   tokens attended per request
+ *  out      fp32  [B][Hq][D]            written; a request with lens 0 gets 0
+ *  workspace, workspace_bytes           at least pq_attn_workspace_bytes();
+ *                                       16-byte aligned; may be NULL when
+ *                                       that is 0.  Contents on entry do
+ *                                       not matter.
+ * Launches the score kernel and, when C > 1, the merge kernel. */
+pq_status pq_attn_decode(const pq_attn_desc* desc, const void* q,
+                         const uint8_t* k_codes, const uint8_t* v_codes,
+                         const void* k_cb, const void* v_cb, const int32_t* lens,
+                         float* out, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* The score kernel alone: per (b, query head, chunk c) the statistics of
+ * tokens [c*T, (c+1)*T) intersected with [0, lens[b]) (PAM page, section
+ * 2.2.3 (1)):
+ *  part_m  fp32 [B][Hq][C]     max_t s_t (natural-log units), -inf if empty
+ *  part_l  fp32 [B][Hq][C]     sum_t exp(s_t - m), 0 if empty
+ *  part_o  fp32 [B][Hq][C][D]  sum_t exp(s_t - m) V_t, unnormalised, 0 if empty
+ * with s_t = scale * q . K_t.  Other arguments as for pq_attn_decode. */
+pq_status pq_attn_partials(const pq_attn_desc* desc, const void* q,
+                           const uint8_t* k_codes, const uint8_t* v_codes,
+                           const void* k_cb, const void* v_cb, const int32_t* lens,
+                           float* part_m, float* part_l, float* part_o, void* stream);
+
+/* Merge chunk statistics (PAM page, section 2.2.3 (3); the rescaling of the
+ * memory-wall chapter's online softmax, section 1.4.3 (5.1)):
+ *   out[r] = sum_c w_c o[r][c] / sum_c w_c l[r][c],  w_c = exp(m[r][c] - max_c m[r][c])
+ * for n_rows rows (a row is one (b, query head)), 0 where every chunk is
+ * empty (m = -inf, l = 0).  Partials may come from several pq_attn_partials
+ * calls over disjoint token ranges, laid side by side along the chunk axis.
+ *  part_m, part_l  fp32 [n_rows][n_chunks]
+ *  part_o          fp32 [n_rows][n_chunks][head_dim]
+ *  out             fp32 [n_rows][head_dim]
+ * head_dim must be 128; n_chunks >= 1. */
+pq_status pq_attn_reduce(int64_t n_rows, int32_t n_chunks, int32_t head_dim,
+                         const float* part_m, const float* part_l, const float* part_o,
+                         float* out, void* stream);
+
+/* Shape and strides of one encode call. */
+typedef struct pq_encode_desc {
+  int64_t n_vec;              /* N vectors per head (tokens), >= 0                  */
+  int32_t n_heads;            /* H                                                  */
+  int32_t head_dim;           /* D                                                  */
+  int32_t n_sub;              /* M                                                  */
+  int32_t n_codes;            /* K                                                  */
+  int64_t x_stride_vec;       /* x element (n, h, d) at x[n*x_stride_vec +          */
+  int64_t x_stride_head;      /*   h*x_stride_head + d], in fp16 elements           */
+  int64_t codes_stride_slot;  /* code (n, h, m) at codes[s*codes_stride_slot +      */
+  int64_t codes_stride_head;  /*   h*codes_stride_head + m], bytes; s = slots[n],   */
+                              /*   or s = n when slots is NULL                      */
+  int64_t codes_bytes;        /* size of the codes buffer: the M codes of a (vector,*/
+                              /*   head) whose place falls outside it are skipped,  */
+                              /*   not written (a bad slot cannot fault the GPU);   */
+                              /*   without slots, every place must fit              */
+} pq_encode_desc;
+
+/* Nearest-codeword encode (AQPIM page, sections 3.1 and 5.2 (2)): for every
+ * vector n, head h and segment m, the index k minimising the squared
+ * Euclidean distance between segment m of x[n][h] and codebook[h][m][k]; the
+ * lowest index wins a tie.  Distances are decided in fp32.
+ *  x         fp16  strided as above; rows 16-byte aligned
+ *  codebook  fp16  [H][M][K][D/M]
+ *  slots     int64 [N] destination token slot per vector, or NULL
+ *  codes     uint8 written at the strided places above
+ * With the code cache of pq_attn_decode, slot = b*Hkv*max_len + t,
+ * codes_stride_slot = M and codes_stride_head = max_len*M put token t of
+ * request b straight into the cache. */
+pq_status pq_encode(const pq_encode_desc* desc, const void* x, const void* codebook,
+                    const int64_t* slots, uint8_t* codes, void* stream);
+
+/* A static, human-readable name for a status code. */
+const char* pq_status_string(pq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PQATTN_H */

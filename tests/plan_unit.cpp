@@ -1,0 +1,89 @@
+// Host-only unit test of the argument checking and launch planning, built
+// with g++ and the address/undefined-behaviour sanitizers by
+// tests/test_abi_host.py.
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <limits>
+
+#include "plan.h"
+
+using namespace pqattn;
+
+static int failures = 0;
+#define EXPECT(cond)                                                   \
+  do {                                                                 \
+    if (!(cond)) {                                                     \
+      std::printf("FAIL %s:%d: %s\n", __FILE__, __LINE__, #cond);      \
+      ++failures;                                                      \
+    }                                                                  \
+  } while (0)
+
+static pq_attn_desc base() {
+  pq_attn_desc d;
+  d.batch = 8; d.n_q_heads = 64; d.n_kv_heads = 8; d.head_dim = 128; d.n_sub = 8;
+  d.n_codes = 256; d.max_len = 8192; d.chunk = 0; d.scale = 0.08838835f;
+  return d;
+}
+
+int main() {
+  AttnPlan p;
+  pq_attn_desc d = base();
+  EXPECT(plan_attn(&d, &p) == PQ_OK);
+  EXPECT(p.G == 8 && p.DS == 16 && p.rows == 512);
+  EXPECT(p.blocks == int64_t(p.B) * p.Hkv * p.C);
+  EXPECT(p.T * (p.C - 1) < p.Lmax && p.T * p.C >= p.Lmax);
+  EXPECT(p.blocks >= 256);
+
+  // explicit chunks
+  d.chunk = 2048;
+  EXPECT(plan_attn(&d, &p) == PQ_OK && p.C == 4 && p.T == 2048);
+  EXPECT(p.ws_bytes >= size_t(512) * 4 * 130 * 4);
+  EXPECT(p.ws_l_off % 256 == 0 && p.ws_o_off % 256 == 0 && p.ws_bytes % 256 == 0);
+  d.chunk = 7;
+  EXPECT(plan_attn(&d, &p) == PQ_OK && p.C == (8192 + 6) / 7);
+  d.chunk = 8192;
+  EXPECT(plan_attn(&d, &p) == PQ_OK && p.C == 1 && p.ws_bytes == 0);
+  d.chunk = 1 << 30;
+  EXPECT(plan_attn(&d, &p) == PQ_OK && p.C == 1);
+
+  // bad and unsupported
+  d = base(); d.n_kv_heads = 7;                 EXPECT(plan_attn(&d, &p) == PQ_ERR_SHAPE);
+  d = base(); d.scale = std::nanf("");          EXPECT(plan_attn(&d, &p) == PQ_ERR_SHAPE);
+  d = base(); d.scale = -1.0f;                  EXPECT(plan_attn(&d, &p) == PQ_ERR_SHAPE);
+  d = base(); d.max_len = 8190;                 EXPECT(plan_attn(&d, &p) == PQ_ERR_UNSUPPORTED);
+  d = base(); d.n_q_heads = 8 * 16;             EXPECT(plan_attn(&d, &p) == PQ_ERR_UNSUPPORTED);
+  d = base(); d.batch = std::numeric_limits<int32_t>::max(); d.chunk = 1;
+  EXPECT(plan_attn(&d, &p) == PQ_ERR_UNSUPPORTED);        // too many workgroups
+  EXPECT(plan_attn(nullptr, &p) == PQ_ERR_NULL);
+
+  // chunk pick: small problems still get one chunk per 256 tokens at most
+  EXPECT(pick_chunk(1, 8, 512, 512, 256) == 256);
+  EXPECT(pick_chunk(64, 32, 4096, 512, 256) == 4096);
+  EXPECT(pick_chunk(1, 8, 131072, 512, 256) == 2048);
+  EXPECT(pick_chunk(1, 1, 16, 512, 256) == 16);
+
+  // encode
+  pq_encode_desc e;
+  e.n_vec = 100; e.n_heads = 32; e.head_dim = 128; e.n_sub = 4; e.n_codes = 256;
+  e.x_stride_vec = 32 * 128; e.x_stride_head = 128; e.codes_stride_slot = 4;
+  e.codes_stride_head = 4096 * 4; e.codes_bytes = 1 << 20;
+  EncodePlan ep;
+  EXPECT(plan_encode(&e, 128, &ep) == PQ_OK && ep.blocks_x == 1 && ep.DS == 32);
+  e.n_vec = 0;        EXPECT(plan_encode(&e, 128, &ep) == PQ_OK && ep.blocks_x == 0);
+  e.n_vec = 100; e.x_stride_head = 12;  EXPECT(plan_encode(&e, 128, &ep) == PQ_ERR_ALIGN);
+  e.x_stride_head = 128; e.codes_stride_slot = 6; EXPECT(plan_encode(&e, 128, &ep) == PQ_ERR_ALIGN);
+  e.codes_stride_slot = 4; e.n_codes = 128; EXPECT(plan_encode(&e, 128, &ep) == PQ_ERR_UNSUPPORTED);
+
+  // reduce
+  EXPECT(check_reduce(10, 1, 128) == PQ_OK);
+  EXPECT(check_reduce(10, 0, 128) == PQ_ERR_SHAPE);
+  EXPECT(check_reduce(10, 4, 96) == PQ_ERR_UNSUPPORTED);
+
+  if (failures) {
+    std::printf("plan_unit: %d failures\n", failures);
+    return 1;
+  }
+  std::printf("plan_unit: all checks passed\n");
+  return 0;
+}

@@ -1,0 +1,171 @@
+"""The C ABI on the host: the library loads, exports every function the
+header declares, and rejects bad arguments before launching anything.
+
+No case here passes host validation: every call carries at least one bad
+field, so nothing reaches the GPU even on a machine that has one.
+"""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import decode_attention_product_amd as pq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pqattn.h")
+CSRC = os.path.join(ROOT, "decode_attention_product_amd", "csrc")
+
+FAKE = 0x10000      # an aligned, non-null address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(pq_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pq.LIB_PATH):
+        pytest.fail("libpqattn.so is not built (python -m decode_attention_product_amd.build)")
+    return pq.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == {"pq_attn_num_chunks", "pq_attn_workspace_bytes", "pq_attn_decode",
+                          "pq_attn_partials", "pq_attn_reduce", "pq_encode", "pq_status_string"}
+    out = subprocess.run(["nm", "-D", "--defined-only", pq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pq_\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def _desc(**kw):
+    d = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_sub=4, n_codes=256,
+             max_len=64, chunk=0, scale=0.0883883)
+    d.update(kw)
+    return pq.PQAttnDesc(**d)
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert pq.status_string(s) and pq.status_string(s) != "unknown status"
+    assert pq.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, 2), ("n_q_heads", 0, 2), ("n_kv_heads", 3, 2), ("head_dim", 130, 2),
+    ("n_sub", 0, 2), ("max_len", 0, 2), ("chunk", -1, 2), ("scale", 0.0, 2),
+    ("scale", float("nan"), 2), ("scale", float("inf"), 2),
+    ("head_dim", 64, 3), ("n_codes", 16, 3), ("n_sub", 2, 3), ("n_sub", 16, 3),
+    ("max_len", 40, 3), ("n_q_heads", 32, 3),      # group of 16 is not built
+])
+def test_bad_descriptor(lib, field, value, status):
+    d = _desc(**{field: value})
+    assert lib.pq_attn_num_chunks(ctypes.byref(d)) == -1
+    assert lib.pq_attn_workspace_bytes(ctypes.byref(d)) == 0
+    st = lib.pq_attn_decode(ctypes.byref(d), *([FAKE] * 7), FAKE, 1 << 30, None)
+    assert st == status
+    st = lib.pq_attn_partials(ctypes.byref(d), *([FAKE] * 9), None)
+    assert st == status
+
+
+def test_null_descriptor(lib):
+    assert lib.pq_attn_decode(None, *([FAKE] * 7), FAKE, 1 << 30, None) == 1
+    assert lib.pq_encode(None, FAKE, FAKE, None, FAKE, None) == 1
+
+
+@pytest.mark.parametrize("which", range(7))
+def test_null_pointer(lib, which):
+    ptrs = [FAKE] * 7          # q, kc, vc, kcb, vcb, lens, out
+    ptrs[which] = None
+    assert lib.pq_attn_decode(ctypes.byref(_desc()), *ptrs, FAKE, 1 << 30, None) == 1
+
+
+def test_misaligned_pointer(lib):
+    ptrs = [FAKE] * 7
+    ptrs[1] = FAKE + 4
+    assert lib.pq_attn_decode(ctypes.byref(_desc()), *ptrs, FAKE, 1 << 30, None) == 6
+
+
+def test_workspace_checks(lib):
+    d = _desc(max_len=4096, chunk=256)
+    need = lib.pq_attn_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    ptrs = [FAKE] * 7
+    assert lib.pq_attn_decode(ctypes.byref(d), *ptrs, None, need, None) == 4
+    assert lib.pq_attn_decode(ctypes.byref(d), *ptrs, FAKE, need - 1, None) == 4
+    assert lib.pq_attn_decode(ctypes.byref(d), *ptrs, FAKE + 8, need, None) == 4
+
+
+def test_chunking_and_workspace_sizes(lib):
+    # the long-context workload: T = 2048 over 131072 tokens -> 64 chunks
+    d = _desc(batch=1, n_q_heads=64, n_kv_heads=8, max_len=131072, chunk=2048)
+    assert lib.pq_attn_num_chunks(ctypes.byref(d)) == 64
+    rows, C, D = 64, 64, 128
+    assert lib.pq_attn_workspace_bytes(ctypes.byref(d)) >= rows * C * (D + 2) * 4
+    assert lib.pq_attn_workspace_bytes(ctypes.byref(d)) <= rows * C * (D + 2) * 4 + 3 * 256
+    # one chunk needs no workspace
+    d1 = _desc(max_len=512, chunk=512)
+    assert lib.pq_attn_num_chunks(ctypes.byref(d1)) == 1
+    assert lib.pq_attn_workspace_bytes(ctypes.byref(d1)) == 0
+    # chunk larger than the cache is clamped to one chunk
+    d2 = _desc(max_len=512, chunk=100000)
+    assert lib.pq_attn_num_chunks(ctypes.byref(d2)) == 1
+    # the library's pick fills the chip: at least 256 workgroups when possible
+    d3 = _desc(batch=8, n_q_heads=64, n_kv_heads=8, n_sub=8, max_len=8192)
+    C3 = lib.pq_attn_num_chunks(ctypes.byref(d3))
+    assert 8 * 8 * C3 >= 256 and 8192 % C3 == 0
+
+
+def test_reduce_checks(lib):
+    assert lib.pq_attn_reduce(4, 0, 128, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert lib.pq_attn_reduce(-1, 2, 128, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert lib.pq_attn_reduce(4, 2, 64, FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert lib.pq_attn_reduce(4, 2, 128, None, FAKE, FAKE, FAKE, None) == 1
+
+
+def _edesc(**kw):
+    d = dict(n_vec=10, n_heads=2, head_dim=128, n_sub=4, n_codes=256, x_stride_vec=256,
+             x_stride_head=128, codes_stride_slot=8, codes_stride_head=4, codes_bytes=80)
+    d.update(kw)
+    return pq.PQEncodeDesc(**d)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_vec", -1, 2), ("n_heads", 0, 2), ("head_dim", 102, 2), ("x_stride_vec", -8, 2),
+    ("codes_bytes", -1, 2), ("n_codes", 512, 3), ("n_sub", 2, 3), ("head_dim", 64, 3),
+    ("x_stride_vec", 250, 6), ("x_stride_head", 4, 6), ("codes_stride_slot", 6, 6),
+    ("codes_stride_head", 2, 6), ("codes_bytes", 79, 2),
+])
+def test_bad_encode_descriptor(lib, field, value, status):
+    d = _edesc(**{field: value})
+    assert lib.pq_encode(ctypes.byref(d), FAKE, FAKE, None, FAKE, None) == status
+
+
+def test_encode_pointer_checks(lib):
+    d = _edesc(codes_bytes=79)        # also invalid: nothing can launch
+    assert lib.pq_encode(ctypes.byref(d), None, FAKE, None, FAKE, None) in (1, 2)
+    d = _edesc(n_sub=3)
+    assert lib.pq_encode(ctypes.byref(d), FAKE, FAKE, None, FAKE, None) == 2
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="no g++")
+def test_plan_unit_with_sanitizers(tmp_path):
+    """The host planning code built with g++, ASan and UBSan, run on edge cases."""
+    exe = tmp_path / "plan_test"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+           os.path.join(ROOT, "tests", "plan_unit.cpp"), os.path.join(CSRC, "plan.cpp"),
+           "-o", str(exe)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True,
+                       env={**os.environ, "ASAN_OPTIONS": "detect_leaks=1"})
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "plan_unit: all" in r.stdout

@@ -1,0 +1,337 @@
+"""GPU parity: the HIP library, called through its C ABI, against the CPU oracle.
+
+Bars: encode codes bit-exact; attention outputs within
+max|gpu - oracle| <= 1e-3 * max|oracle| over the whole output tensor of a call.
+Every input comes from the seeded generators; no expected value comes from
+the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import gen
+
+torch = pytest.importorskip("torch")
+pq = pytest.importorskip("decode_attention_product_amd")
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+def say(msg):
+    print(f"[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    pq.load_library()       # raises if the library is missing: no silent fallback
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def gpu_inputs(inp):
+    return [dev(inp[k]) for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")]
+
+
+def oracle_out(inp, **kw):
+    return oracle.decode_attention(*(inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")), **kw)
+
+
+def assert_attn_close(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    scale = np.abs(ref).max()
+    err = np.abs(got - ref).max()
+    if scale == 0:
+        assert err == 0, f"{what}: expected zeros, max |got| = {err}"
+        return
+    say(f"{what}: max|d| = {err:.3e}, max|ref| = {scale:.3e}, ratio {err / scale:.2e}")
+    assert err <= TOL * scale, f"{what}: max|d| {err:.3e} > {TOL} * {scale:.3e}"
+
+
+def decode_gpu(inp, chunk=0):
+    t = gpu_inputs(inp)
+    out = pq.pq_attn_decode(*t, chunk=chunk)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+# --------------------------------------------------------------------------
+# The five workloads
+# --------------------------------------------------------------------------
+
+def test_tiny_workload_decode_and_encode():
+    say("workload tiny: decode B=1 H=8 L=512 M=4; encode 8 heads x (K, V)")
+    inp = gen.workload_inputs(1)
+    assert_attn_close(decode_gpu(inp), oracle_out(inp), "tiny decode")
+    for x, cb, src in ((inp["x_k"], inp["k_cb"], inp["src_k"]), (inp["x_v"], inp["v_cb"], inp["src_v"])):
+        codes = torch.empty((x.shape[0], x.shape[1], cb.shape[1]), dtype=torch.uint8, device="cuda")
+        pq.pq_encode(dev(x), dev(cb), codes)
+        torch.cuda.synchronize()
+        got = codes.cpu().numpy()
+        np.testing.assert_array_equal(got, oracle.encode(x, cb))
+        np.testing.assert_array_equal(got, src)
+
+
+def test_page_sizing_workload():
+    say("workload page-sizing: B=4 H=32 L=2048 M=4")
+    inp = gen.workload_inputs(2, with_encode=False)
+    assert_attn_close(decode_gpu(inp), oracle_out(inp), "page-sizing decode")
+
+
+def test_gqa_workload():
+    say("workload gqa: B=8 Hq=64 Hkv=8 L=8192 M=8 (library-picked chunks, as benchmarked)")
+    inp = gen.workload_inputs(3, with_encode=False)
+    assert_attn_close(decode_gpu(inp), oracle_out(inp), "gqa decode")
+
+
+def test_long_context_workload():
+    say("workload long-splitk: B=1 Hq=64 Hkv=8 L=131072 M=4 T=2048")
+    inp = gen.workload_inputs(4, with_encode=False)
+    w = gen.WORKLOADS[4]
+    t = gpu_inputs(inp)
+    desc = pq.attn_desc(t[0], t[1], t[3], chunk=w.chunk)
+    assert pq.pq_attn_num_chunks(desc) == 64
+    out = pq.pq_attn_decode(*t, desc=desc)
+    torch.cuda.synchronize()
+    ref = oracle_out(inp)
+    assert_attn_close(out.cpu().numpy(), ref, "long-splitk decode")
+    # the 64 chunk records themselves, on a sample of query heads
+    pm, pl, po = pq.pq_attn_partials(*t, desc=desc)
+    torch.cuda.synchronize()
+    rm, rl, ro = oracle.chunk_partials(inp["q"][:, :2], inp["k_codes"][:, :1], inp["v_codes"][:, :1],
+                                       inp["k_cb"][:1], inp["v_cb"][:1], inp["lens"], chunk=w.chunk)
+    np.testing.assert_allclose(pm.cpu().numpy()[:, :2], rm, rtol=0, atol=1e-4)
+    np.testing.assert_allclose(pl.cpu().numpy()[:, :2], rl, rtol=2e-4, atol=0)
+    assert_attn_close(po.cpu().numpy()[:, :2], ro, "long-splitk partial o (heads 0-1)")
+
+
+def test_ragged_workload_encode_then_decode():
+    """Prefill: encode every prefill token's K and V straight into the code
+    cache, then one decode step over the ragged cache."""
+    say("workload ragged: 64 requests (45x512 + 19x4096), H=32, prefill encode of 6,455,296 vectors")
+    w = gen.WORKLOADS[5]
+    inp = gen.workload_inputs(5)
+    B, H, L, M = w.batch, w.n_kv_heads, w.max_len, w.n_sub
+    lens = inp["lens"]
+    slots = dev(inp["slots"])
+    N = int(lens.sum())
+    kc = dev(inp["k_codes"])           # padding positions keep their random codes
+    vc = dev(inp["v_codes"])
+    desc = pq.cache_encode_desc(N, B, H, L, n_sub=M)
+    pq.pq_encode(dev(inp["x_k"]), dev(inp["k_cb"]), kc, slots=slots, desc=desc)
+    pq.pq_encode(dev(inp["x_v"]), dev(inp["v_cb"]), vc, slots=slots, desc=desc)
+    torch.cuda.synchronize()
+    kc_h, vc_h = kc.cpu().numpy(), vc.cpu().numpy()
+    # expected cache: generator's source indices at the prefill places,
+    # the original random codes elsewhere
+    exp_k, exp_v = inp["k_codes"].copy(), inp["v_codes"].copy()
+    b_of = np.repeat(np.arange(B), lens)
+    t_of = np.concatenate([np.arange(l) for l in lens])
+    exp_k[b_of, :, t_of] = inp["src_k"]
+    exp_v[b_of, :, t_of] = inp["src_v"]
+    np.testing.assert_array_equal(kc_h, exp_k)
+    np.testing.assert_array_equal(vc_h, exp_v)
+    # and the oracle's own encode agrees on a sample of vectors
+    rng = np.random.default_rng(7)
+    idx = np.sort(rng.choice(N, size=3000, replace=False))
+    np.testing.assert_array_equal(oracle.encode(inp["x_k"][idx], inp["k_cb"]), kc_h[b_of[idx], :, t_of[idx]])
+    np.testing.assert_array_equal(oracle.encode(inp["x_v"][idx], inp["v_cb"]), vc_h[b_of[idx], :, t_of[idx]])
+    say("ragged: decode over the encoded cache")
+    out = pq.pq_attn_decode(dev(inp["q"]), kc, vc, dev(inp["k_cb"]), dev(inp["v_cb"]), dev(lens))
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention(inp["q"], exp_k, exp_v, inp["k_cb"], inp["v_cb"], lens)
+    assert_attn_close(out.cpu().numpy(), ref, "ragged decode")
+
+
+# --------------------------------------------------------------------------
+# Edge cases: ragged lengths around chunk edges, every group size, both M
+# --------------------------------------------------------------------------
+
+EDGE = [
+    # (G, M, Lmax, chunk, lens)
+    (1, 4, 64, 0, [0, 1, 63, 64]),
+    (2, 4, 272, 16, [15, 16, 17, 0]),
+    (4, 8, 528, 256, [255, 256, 257, 528]),
+    (8, 8, 1040, 1024, [1023, 1024, 1025, 1]),
+    (8, 4, 2048, 7, [7, 6, 8, 2000]),
+    (1, 8, 4096, 0, [4096, 3000, 1, 2]),
+    (4, 4, 1536, 1536, [1536, 1535, 0, 700]),
+    (8, 8, 4096, 4096, [4096, 4095, 2049, 1]),     # more than one pass per chunk
+]
+
+
+@pytest.mark.parametrize("G,M,Lmax,chunk,lens", EDGE)
+def test_edge_shapes(G, M, Lmax, chunk, lens):
+    say(f"edge G={G} M={M} Lmax={Lmax} chunk={chunk} lens={lens}")
+    Hkv = 2
+    _, inp = gen.random_case(100 + G * 10 + M, batch=len(lens), n_q_heads=G * Hkv,
+                             n_kv_heads=Hkv, max_len=Lmax, n_sub=M, lens=lens)
+    t = gpu_inputs(inp)
+    out = pq.pq_attn_decode(*t, chunk=chunk)
+    torch.cuda.synchronize()
+    ref = oracle_out(inp)
+    assert_attn_close(out.cpu().numpy(), ref, f"edge G={G} M={M}")
+    for b, l in enumerate(lens):
+        if l == 0:
+            assert (out[b] == 0).all()
+
+
+@pytest.mark.parametrize("chunk", [16, 100, 256])
+def test_partials_match_oracle(chunk):
+    say(f"partials chunk={chunk}")
+    _, inp = gen.random_case(200 + chunk, batch=2, n_q_heads=8, n_kv_heads=2, max_len=512,
+                             n_sub=4, lens=[512, 130])
+    t = gpu_inputs(inp)
+    pm, pl, po = pq.pq_attn_partials(*t, chunk=chunk)
+    torch.cuda.synchronize()
+    rm, rl, ro = oracle.chunk_partials(*(inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")),
+                                       chunk=chunk)
+    pm, pl, po = pm.cpu().numpy(), pl.cpu().numpy(), po.cpu().numpy()
+    empty = np.isneginf(rm)
+    assert (np.isneginf(pm) == empty).all()
+    assert (pl[empty] == 0).all() and (po[empty] == 0).all()
+    np.testing.assert_allclose(pm[~empty], rm[~empty], rtol=0, atol=1e-4)
+    np.testing.assert_allclose(pl[~empty], rl[~empty], rtol=2e-4, atol=0)
+    assert_attn_close(po, ro, f"partial o chunk={chunk}")
+
+
+def test_reduce_matches_oracle_merge():
+    say("reduce on random statistics")
+    rng = np.random.default_rng(9)
+    rows, C, D = 37, 11, 128
+    m = rng.normal(size=(rows, C)).astype(np.float32) * 5
+    l = rng.uniform(0.5, 3, size=(rows, C)).astype(np.float32)
+    o = rng.normal(size=(rows, C, D)).astype(np.float32)
+    m[3, :] = -np.inf
+    l[3, :] = 0
+    o[3] = 0
+    m[5, 2:] = -np.inf
+    l[5, 2:] = 0
+    o[5, 2:] = 0
+    out = pq.pq_attn_reduce(dev(m), dev(l), dev(o))
+    torch.cuda.synchronize()
+    ref = oracle.merge_partials(m, l, o)
+    assert (out[3] == 0).all()
+    assert_attn_close(out.cpu().numpy(), ref, "reduce")
+
+
+def test_token_shards_merge_like_one_call():
+    """Token-parallel split (PAM page, section 2.2.3 (2)) emulated on one GPU:
+    each shard of the token range is its own cache; their chunk statistics,
+    laid side by side, merge to the single-call result."""
+    say("token shards -> partials -> reduce")
+    B, Hq, Hkv, L, M = 3, 16, 2, 1024, 4
+    _, inp = gen.random_case(300, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, max_len=L, n_sub=M,
+                             lens=[1024, 700, 333])
+    ref = oracle_out(inp)
+    full = decode_gpu(inp)
+    cuts = [0, 256, 512 + 64, 1024]
+    ms, ls, os_ = [], [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        sh_lens = np.clip(inp["lens"] - a, 0, b - a).astype(np.int32)
+        t = [dev(inp["q"]), dev(inp["k_codes"][:, :, a:b]), dev(inp["v_codes"][:, :, a:b]),
+             dev(inp["k_cb"]), dev(inp["v_cb"]), dev(sh_lens)]
+        pm, pl, po = pq.pq_attn_partials(*t, chunk=128)
+        ms.append(pm), ls.append(pl), os_.append(po)
+    out = pq.pq_attn_reduce(torch.cat(ms, -1).contiguous(), torch.cat(ls, -1).contiguous(),
+                            torch.cat(os_, -2).contiguous())
+    torch.cuda.synchronize()
+    assert_attn_close(out.cpu().numpy(), ref, "shards vs oracle")
+    assert_attn_close(out.cpu().numpy(), full, "shards vs one call")
+
+
+# --------------------------------------------------------------------------
+# Robustness
+# --------------------------------------------------------------------------
+
+def test_tokens_past_lens_are_not_read():
+    say("codes past lens changed on the device")
+    _, inp = gen.random_case(400, batch=2, n_q_heads=4, n_kv_heads=1, max_len=1024, n_sub=4,
+                             lens=[600, 17])
+    t = gpu_inputs(inp)
+    a = pq.pq_attn_decode(*t).clone()
+    t[1][:, :, 600:] ^= 0x33
+    t[2][:, :, 17:] ^= 0x5C
+    t[1][1, :, 17:] ^= 0x11
+    b = pq.pq_attn_decode(*t)
+    torch.cuda.synchronize()
+    assert_attn_close(b.cpu().numpy(), oracle_out(inp), "after changing padding")
+    assert_attn_close(a.cpu().numpy(), b.cpu().numpy().astype(np.float64), "before vs after")
+
+
+def test_repeat_and_two_streams():
+    say("repeated calls on two streams")
+    inp = gen.workload_inputs(2, with_encode=False)
+    t = gpu_inputs(inp)
+    ref = oracle_out(inp)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for i in range(6):
+        s = s1 if i % 2 == 0 else s2
+        with torch.cuda.stream(s):
+            outs.append(pq.pq_attn_decode(*t, stream=s))
+    torch.cuda.synchronize()
+    for o in outs:
+        assert_attn_close(o.cpu().numpy(), ref, "repeat")
+
+
+def test_lens_clamped_and_empty_batch_rows():
+    say("lens beyond capacity and negative")
+    _, inp = gen.random_case(500, batch=3, n_q_heads=8, n_kv_heads=4, max_len=256, n_sub=8,
+                             lens=[256, 0, 100])
+    ref = oracle_out(inp)
+    inp2 = dict(inp)
+    inp2["lens"] = np.array([100000, -5, 100], dtype=np.int32)
+    got = decode_gpu(inp2)
+    assert_attn_close(got, ref, "clamped lens")
+    assert (got[1] == 0).all()
+
+
+def test_encode_strided_slots_and_out_of_range():
+    say("encode through slots into a cache; out-of-range slots skipped")
+    rng = np.random.default_rng(600)
+    B, H, L, M = 3, 4, 64, 8
+    cb = gen.codebooks(rng, H, M, 256, 128 // M)
+    x, src = gen.noisy_codewords(rng, cb, 10, 0.05)
+    cache = np.full((B, H, L, M), 0xEE, dtype=np.uint8)
+    slots = np.array([0, 5, 63, 64 * 4 + 1, 2 * H * L + 7, 2 * H * L + 8, 2 * H * L + 63,
+                      -1, B * H * L, 1 << 40], dtype=np.int64)
+    c = dev(cache)
+    desc = pq.cache_encode_desc(10, B, H, L, n_sub=M)
+    pq.pq_encode(dev(x), dev(cb), c, slots=dev(slots), desc=desc)
+    torch.cuda.synchronize()
+    got = c.cpu().numpy()
+    exp = cache.copy()
+    for n, s in enumerate(slots[:7]):
+        b, t = divmod(int(s), H * L)
+        exp[b, :, t] = src[n]
+    # slot B*H*L - ... : only in-buffer places are written
+    np.testing.assert_array_equal(got, exp)
+    np.testing.assert_array_equal(oracle.encode(x, cb), src)
+
+
+def test_encode_ties_lowest_index():
+    say("encode ties")
+    rng = np.random.default_rng(601)
+    cb = gen.codebooks(rng, 2, 4, 256, 32)
+    cb[1, 2, 200] = cb[1, 2, 17]
+    cb[0, 0, 255] = cb[0, 0, 3]
+    x = np.zeros((2, 2, 128), dtype=np.float16)
+    x[0, 1, 64:96] = cb[1, 2, 17]
+    x[1, 0, 0:32] = cb[0, 0, 3]
+    codes = torch.empty((2, 2, 4), dtype=torch.uint8, device="cuda")
+    pq.pq_encode(dev(x), dev(cb), codes)
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy()
+    assert got[0, 1, 2] == 17 and got[1, 0, 0] == 3
+    np.testing.assert_array_equal(got, oracle.encode(x, cb))
