@@ -13,8 +13,8 @@
 namespace pqattn {
 namespace {
 
-constexpr int kDecodeThreads = 256;
-constexpr int kDecodeTokensPerThread = 4;
+static_assert(kMaxChunk == 8 * kDecodeThreads, "a chunk is at most 8 token slots per thread");
+
 constexpr int kReduceThreads = 128;
 constexpr int kEncodeThreads = 256;
 constexpr int kEncodeVectors = 128;
@@ -22,20 +22,25 @@ constexpr int kEncodeVectors = 128;
 using DecodeFn = void (*)(DecodeArgs);
 
 template <int G, int M>
-DecodeFn decode_instance() {
-  return &decode_partials_kernel<G, M, kDecodeTokensPerThread, kDecodeThreads>;
+DecodeFn pick_nt(int T) {
+  if (T <= kDecodeThreads) return &decode_partials_kernel<G, M, 1>;
+  if (T <= 2 * kDecodeThreads) return &decode_partials_kernel<G, M, 2>;
+  if (T <= 4 * kDecodeThreads) return &decode_partials_kernel<G, M, 4>;
+  if (T <= 8 * kDecodeThreads) return &decode_partials_kernel<G, M, 8>;
+  return nullptr;
 }
 
-DecodeFn pick_decode(int G, int M) {
+// The kernel instance for (G, M) and the chunk length T (T <= kMaxChunk).
+DecodeFn pick_decode(int G, int M, int T) {
   switch (M * 16 + G) {
-    case 4 * 16 + 1: return decode_instance<1, 4>();
-    case 4 * 16 + 2: return decode_instance<2, 4>();
-    case 4 * 16 + 4: return decode_instance<4, 4>();
-    case 4 * 16 + 8: return decode_instance<8, 4>();
-    case 8 * 16 + 1: return decode_instance<1, 8>();
-    case 8 * 16 + 2: return decode_instance<2, 8>();
-    case 8 * 16 + 4: return decode_instance<4, 8>();
-    case 8 * 16 + 8: return decode_instance<8, 8>();
+    case 4 * 16 + 1: return pick_nt<1, 4>(T);
+    case 4 * 16 + 2: return pick_nt<2, 4>(T);
+    case 4 * 16 + 4: return pick_nt<4, 4>(T);
+    case 4 * 16 + 8: return pick_nt<8, 4>(T);
+    case 8 * 16 + 1: return pick_nt<1, 8>(T);
+    case 8 * 16 + 2: return pick_nt<2, 8>(T);
+    case 8 * 16 + 4: return pick_nt<4, 8>(T);
+    case 8 * 16 + 8: return pick_nt<8, 8>(T);
   }
   return nullptr;
 }
@@ -74,7 +79,7 @@ pq_status launch_partials(const AttnPlan& p, const void* q, const uint8_t* kc, c
   a.T = p.T;
   a.C = p.C;
   a.qscale = p.scale * kLog2e;
-  DecodeFn fn = pick_decode(p.G, p.M);
+  DecodeFn fn = pick_decode(p.G, p.M, p.T);
   if (!fn) return PQ_ERR_UNSUPPORTED;
   return launch(reinterpret_cast<const void*>(fn), dim3(unsigned(p.blocks)), dim3(kDecodeThreads),
                 &a, stream);

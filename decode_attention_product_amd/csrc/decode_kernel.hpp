@@ -1,24 +1,34 @@
 // Fused PQ decode-attention score kernel and chunk-merge kernel (gfx950).
 //
-// One workgroup owns one (request b, KV head g, chunk c) and the G query
-// heads that share g.  It
-//   1. builds the lookup table LUT[m][k][h] = q_h[m] . Ck_g[m][k] in LDS
-//      (the query's partial dot products with every K codeword, AQPIM page
-//      section 4.1, kept on chip as the page's GPU note suggests),
-//   2. streams the chunk's K indices from HBM and sums M table entries per
-//      token and head -- the score, without rebuilding K,
-//   3. keeps the chunk's running max and exp-sum (PAM page, section
-//      2.2.3 (1)), rescaling when the max grows between passes,
-//   4. streams the V indices and adds each token's probability into a
-//      per-(segment, codeword, head) histogram in LDS,
-//   5. contracts the histogram with the V codebook,
-//        o[h][m*DS + j] = sum_k Hist[m][k][h] * Cv_g[m][k][j],
-//      which equals sum_t p_t V_t because V_t is made of codewords,
-//   6. writes (m, l, o) for the merge, or the normalised output when the
-//      whole cache is one chunk.
-// Scores are kept in base-2 units (q is pre-multiplied by scale*log2(e)) so
-// the exponentials are single v_exp_f32 instructions; m is written back in
-// natural-log units.
+// One workgroup of 512 threads owns one (request b, KV head g, chunk c) and
+// the G query heads that share g (grouped-query attention, memory-wall
+// chapter section 1.4.3 (1)).  Steps:
+//
+//   0. Every operand the workgroup needs is requested from memory at once:
+//      its K and V codes, the MFMA operands of the K codebook and q (for the
+//      table) and of the V codebook (for the contraction), so HBM/L2 latency
+//      is paid once, not once per phase.
+//   1. Lookup table LUT[m][k][h] = q_h[m] . Ck_g[m][k] -- the query's partial
+//      dot product with every K codeword (AQPIM page, section 4.1; kept on
+//      chip as the page's GPU note suggests) -- computed as M small
+//      [G x DS] x [DS x 256] products on the matrix cores (fp16 inputs,
+//      exact products, fp32 sums), scaled by scale*log2(e) and stored in LDS.
+//   2. Scores: per token and head, the sum over m of LUT[m][code_m][h]; the
+//      K vectors are never rebuilt.
+//   3. Chunk max m_c and p_t = 2^(s_t - m_c) <= 1 (PAM page, section
+//      2.2.3 (1)); l_c = sum_t p_t.
+//   4. V histogram Hist[m][k][h] = sum of p_t over the chunk's tokens whose
+//      segment-m V code is k.  LDS float atomics are slow on gfx950, so p is
+//      added as a 32-bit fixed-point integer (p * 2^31 / Tmax, which cannot
+//      overflow a bin), two heads per 64-bit ds_add_u64.
+//   5. Contraction o[h][m*DS + j] = sum_k Hist[m][k][h] * Cv_g[m][k][j] on
+//      the matrix cores.  This equals sum_t p_t V_t because every V_t is
+//      made of codewords.  The histogram enters as fp16 hi + lo parts, so
+//      the product keeps about 22 bits of the fp32 bin value.
+//   6. (m_c, l_c, o_c) is written for the merge, or o_c / l_c when the whole
+//      cache is one chunk.
+// Scores are in base-2 units (q . C times scale*log2(e)) so exponentials are
+// single v_exp_f32 instructions; m is written back in natural-log units.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,6 +39,10 @@ namespace pqattn {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kDecodeThreads = 512;
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct DecodeArgs {
   const __half* q;           // [B][Hq][D]
@@ -48,56 +62,188 @@ struct DecodeArgs {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float wave_max(float v) {
+// DPP lane moves inside a row of 16 lanes (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;   // quad_perm(1,0,3,2)
+constexpr int kDppXor2 = 0x4E;   // quad_perm(2,3,0,1)
+constexpr int kDppRor4 = 0x124;  // row_ror:4
+constexpr int kDppRor8 = 0x128;  // row_ror:8
+
+// Wave-wide max / sum of N values at once: all-reduce inside each row with
+// DPP, then combine the four rows' results read from lanes 0, 16, 32, 48.
+// Every lane receives the results.
+template <int N>
+__device__ __forceinline__ void wave_max_n(float (&v)[N]) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  for (int i = 0; i < N; ++i) {
+    float x = v[i];
+    x = fmaxf(x, dpp_f<kDppXor1>(x));
+    x = fmaxf(x, dpp_f<kDppXor2>(x));
+    x = fmaxf(x, dpp_f<kDppRor4>(x));
+    x = fmaxf(x, dpp_f<kDppRor8>(x));
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    v[i] = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+  }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+template <int N>
+__device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  for (int i = 0; i < N; ++i) {
+    float x = v[i];
+    x += dpp_f<kDppXor1>(x);
+    x += dpp_f<kDppXor2>(x);
+    x += dpp_f<kDppRor4>(x);
+    x += dpp_f<kDppRor8>(x);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    v[i] = (r0 + r1) + (r2 + r3);
+  }
 }
 
 // Code bytes of one token: M = 4 -> one dword, M = 8 -> two dwords.
 template <int M> struct TokenCodes;
 template <> struct TokenCodes<4> {
-  uint32_t w;
+  uint32_t w = 0;
   __device__ __forceinline__ void load(const uint8_t* p) { w = *reinterpret_cast<const uint32_t*>(p); }
   __device__ __forceinline__ int get(int m) const { return (w >> (8 * m)) & 0xff; }
 };
 template <> struct TokenCodes<8> {
-  uint2 w;
+  uint2 w = {0, 0};
   __device__ __forceinline__ void load(const uint8_t* p) { w = *reinterpret_cast<const uint2*>(p); }
   __device__ __forceinline__ int get(int m) const {
     return ((m < 4 ? w.x : w.y) >> (8 * (m & 3))) & 0xff;
   }
 };
 
-// G query heads per KV head, M segments, NT tokens per thread per pass,
-// NTHR threads per workgroup.
-template <int G, int M, int NT, int NTHR>
-__global__ __launch_bounds__(NTHR) void decode_partials_kernel(DecodeArgs a) {
+// Lookup-table layout: for G >= 4 the heads of one (segment, codeword) are
+// split in quads stored as [m][quad][k] float4 -- 16-byte entries spread a
+// random codeword over 8 LDS bank groups (32-byte entries would use 4); for
+// G <= 2 the layout is [m][k][G].
+template <int G, int K>
+__device__ __forceinline__ int lut_index(int m, int k, int quad) {
+  if constexpr (G >= 4) return ((m * (G / 4) + quad) * K + k) * 4;
+  else return (m * K + k) * G;
+}
+
+// Scores of one token: the M * ceil(G/4) table reads are issued before any
+// sum so their LDS latencies overlap.
+template <int G, int M, int K, typename Codes>
+__device__ __forceinline__ void token_scores(const float* lut, const Codes& code, float* s) {
+  if constexpr (G >= 4) {
+    float4 e[M][G / 4];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int v = 0; v < G / 4; ++v)
+        e[m][v] = *reinterpret_cast<const float4*>(lut + lut_index<G, K>(m, code.get(m), v));
+#pragma unroll
+    for (int v = 0; v < G / 4; ++v) {
+      float4 acc = e[0][v];
+#pragma unroll
+      for (int m = 1; m < M; ++m) {
+        acc.x += e[m][v].x; acc.y += e[m][v].y; acc.z += e[m][v].z; acc.w += e[m][v].w;
+      }
+      s[4 * v + 0] = acc.x; s[4 * v + 1] = acc.y; s[4 * v + 2] = acc.z; s[4 * v + 3] = acc.w;
+    }
+  } else if constexpr (G == 2) {
+    float2 e[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) e[m] = *reinterpret_cast<const float2*>(lut + lut_index<G, K>(m, code.get(m), 0));
+    float2 acc = e[0];
+#pragma unroll
+    for (int m = 1; m < M; ++m) { acc.x += e[m].x; acc.y += e[m].y; }
+    s[0] = acc.x; s[1] = acc.y;
+  } else {
+    float e[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) e[m] = lut[lut_index<G, K>(m, code.get(m), 0)];
+    float acc = e[0];
+#pragma unroll
+    for (int m = 1; m < M; ++m) acc += e[m];
+    s[0] = acc;
+  }
+}
+
+// 4x4 transpose of 16-bit values across the lanes of a quad: lane u holds
+// row u as (w0 = x[u][0] | x[u][1] << 16, w1 = x[u][2] | x[u][3] << 16) and
+// gets column u back as the four halves x[0][u], x[1][u], x[2][u], x[3][u].
+// Rotation d sends, from lane r, the word that lane (r - d) & 3 needs.
+template <int D_ROT>
+__device__ __forceinline__ uint32_t quad_rotate(uint32_t v) {
+  // quad_perm: lane i reads lane (i + D_ROT) & 3
+  constexpr int ctrl = ((0 + D_ROT) & 3) | (((1 + D_ROT) & 3) << 2) | (((2 + D_ROT) & 3) << 4) |
+                       (((3 + D_ROT) & 3) << 6);
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(v), ctrl, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ f16x4 quad_transpose(uint32_t w0, uint32_t w1, int u) {
+  uint16_t e[4];
+  // d = 0: own row u, element u
+  {
+    const uint32_t w = (u >> 1) ? w1 : w0;
+    e[u & 3] = uint16_t((u & 1) ? (w >> 16) : (w & 0xffff));
+  }
+  uint32_t got[4];
+  // the sender r = (u + d) & 3 picks word ((r - d) & 3) >> 1 = (u >> 1) of the receiver
+#define PQ_ROT(DR)                                                           {                                                                            const int recv = (u - DR) & 3; /* receiver of this lane's word */          const uint32_t send = (recv >> 1) ? w1 : w0;                               got[DR] = quad_rotate<DR>(send);                                         }
+  PQ_ROT(1) PQ_ROT(2) PQ_ROT(3)
+#undef PQ_ROT
+#pragma unroll
+  for (int d = 1; d < 4; ++d) {
+    const int r = (u + d) & 3;   // row the word came from
+    e[r] = uint16_t((u & 1) ? (got[d] >> 16) : (got[d] & 0xffff));
+  }
+  f16x4 out;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) out[r] = __builtin_bit_cast(_Float16, e[r]);
+  return out;
+}
+
+// Two fp16 halves of an fp32 value: v ~= hi + lo to about 22 bits.
+__device__ __forceinline__ void split_f16(float v, _Float16& hi, _Float16& lo) {
+  hi = (_Float16)v;
+  lo = (_Float16)(v - (float)hi);
+}
+
+// G query heads per KV head, M segments, NT token slots per thread.
+template <int G, int M, int NT>
+__global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeArgs a) {
+  constexpr int NTHR = kDecodeThreads;
   constexpr int D = 128;
   constexpr int K = 256;
   constexpr int DS = D / M;
   constexpr int NW = NTHR / 64;
-  constexpr int PASS = NT * NTHR;
-  static_assert(NTHR % D == 0, "contraction splits k over NTHR / D slices");
+  constexpr int KSTEP_Q = DS / 16;            // MFMA k-steps of the table build
+  constexpr int LUT_JOBS = (M * 16) / NW;     // (m, 16-codeword tile) jobs per wave
+  constexpr int GP = G >= 2 ? G / 2 : 1;      // 64-bit histogram words per (m, k)
+  static_assert(NW == 8 && (M * DS / 16) == 8, "one contraction job per wave");
+  // fixed point: a bin collects at most NT*NTHR tokens of value <= 1
+  constexpr float kFix = float(1u << 31) / float(NT * NTHR);
+  constexpr float kUnfix = float(NT * NTHR) / float(1u << 31);
 
-  __shared__ float lut[M * K * G];      // [m][k][h], base-2 scaled scores
-  __shared__ float hist[M * K * G];     // [m][k][h], probability mass
-  __shared__ float qs[G * D];           // q * scale * log2(e)
-  __shared__ float red[NW * G];
+  __shared__ __align__(16) float lut[M * K * G];                          // see lut_index
+  __shared__ __align__(16) uint64_t hist64[G >= 2 ? M * GP * K : 2];      // [m][pair][k]
+  __shared__ __align__(16) uint32_t hist32[G == 1 ? M * K : 4];           // [m][k]
+  __shared__ float red[2 * NW * G];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
 
-  // XCD-aware order: consecutive workgroups go to different XCDs, so the
-  // KV head is the fastest index -- all chunks of one head share an XCD and
-  // its L2 copy of that head's codebooks.
+  // XCD-aware order: consecutive workgroups go to different XCDs, so the KV
+  // head is the fastest index; with Hkv a multiple of 8 every chunk of one
+  // head lands on the same XCD and shares its L2 copy of the codebooks.
   const int64_t id = blockIdx.x;
   const int g = int(id % a.Hkv);
   const int64_t rest = id / a.Hkv;
@@ -126,180 +272,235 @@ __global__ __launch_bounds__(NTHR) void decode_partials_kernel(DecodeArgs a) {
     return;
   }
 
-  // ---- stage the G queries, pre-scaled ------------------------------------
-  for (int i = tid; i < G * D; i += NTHR)
-    qs[i] = __half2float(a.q[row0 * D + i]) * a.qscale;
-  for (int i = tid; i < M * K * G; i += NTHR) hist[i] = 0.0f;
-  __syncthreads();
-
-  // ---- LUT build: one (m, k) codeword per thread iteration ----------------
-  {
-    const __half* cbk = a.k_cb + int64_t(g) * M * K * DS;
-    for (int p = tid; p < M * K; p += NTHR) {
-      const int m = p / K;
-      float cw[DS];
-      const uint4* src = reinterpret_cast<const uint4*>(cbk + int64_t(p) * DS);
-#pragma unroll
-      for (int v = 0; v < DS / 8; ++v) {
-        uint4 u = src[v];
-        const __half* hh = reinterpret_cast<const __half*>(&u);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cw[v * 8 + e] = __half2float(hh[e]);
-      }
-      float acc[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float s = 0.0f;
-#pragma unroll
-        for (int j = 0; j < DS; ++j) s = fmaf(qs[h * D + m * DS + j], cw[j], s);
-        acc[h] = s;
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) lut[p * G + h] = acc[h];
-    }
-  }
-  __syncthreads();
-
+  // ---- 0. requests: codes, table operands, contraction operands ------------
   const int64_t bg = int64_t(b) * a.Hkv + g;
   const uint8_t* kc = a.k_codes + bg * a.Lmax * M;
   const uint8_t* vc = a.v_codes + bg * a.Lmax * M;
-
-  float m_run[G], l_thr[G];
+  TokenCodes<M> kcode[NT], vcode[NT];
 #pragma unroll
-  for (int h = 0; h < G; ++h) { m_run[h] = -INFINITY; l_thr[h] = 0.0f; }
-
-  for (int tp = t_begin; tp < t_end; tp += PASS) {
-    // ---- scores of this pass ----------------------------------------------
-    float s[NT][G];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int t = tp + i * NTHR + tid;
-      if (t < t_end) {
-        TokenCodes<M> code;
-        code.load(kc + int64_t(t) * M);
-#pragma unroll
-        for (int h = 0; h < G; ++h) s[i][h] = 0.0f;
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const float* e = lut + (m * K + code.get(m)) * G;
-#pragma unroll
-          for (int h = 0; h < G; ++h) s[i][h] += e[h];
-        }
-      } else {
-#pragma unroll
-        for (int h = 0; h < G; ++h) s[i][h] = -INFINITY;
-      }
-    }
-    // ---- pass max over the workgroup ----------------------------------------
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = s[0][h];
-#pragma unroll
-      for (int i = 1; i < NT; ++i) mx = fmaxf(mx, s[i][h]);
-      mx = wave_max(mx);
-      if (lane == 0) red[wave * G + h] = mx;
-    }
-    __syncthreads();
-    bool grew = false;
-    float alpha[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = red[h];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red[w * G + h]);
-      const float m_new = fmaxf(m_run[h], mx);
-      alpha[h] = (m_run[h] == -INFINITY) ? 0.0f : fast_exp2(m_run[h] - m_new);
-      grew |= (m_run[h] != -INFINITY) && (m_new > m_run[h]);
-      m_run[h] = m_new;
-      l_thr[h] *= alpha[h];
-    }
-    if (grew) {   // uniform: every thread saw the same maxima
-      // NTHR is a multiple of G, so this thread always touches head tid % G
-      float a_mine = alpha[0];
-#pragma unroll
-      for (int h = 1; h < G; ++h) a_mine = (tid % G == h) ? alpha[h] : a_mine;
-      for (int i = tid; i < M * K * G; i += NTHR) hist[i] *= a_mine;
-    }
-    __syncthreads();
-    // ---- probabilities into the V histogram ---------------------------------
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int t = tp + i * NTHR + tid;
-      if (t < t_end) {
-        float p[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          p[h] = fast_exp2(s[i][h] - m_run[h]);
-          l_thr[h] += p[h];
-        }
-        TokenCodes<M> code;
-        code.load(vc + int64_t(t) * M);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          float* e = hist + (m * K + code.get(m)) * G;
-#pragma unroll
-          for (int h = 0; h < G; ++h) atomicAdd(e + h, p[h]);
-        }
-      }
+  for (int i = 0; i < NT; ++i) {
+    const int t = t_begin + i * NTHR + tid;
+    if (t < t_end) {
+      kcode[i].load(kc + int64_t(t) * M);
+      vcode[i].load(vc + int64_t(t) * M);
     }
   }
 
-  // ---- chunk sum l ------------------------------------------------------------
-  __syncthreads();   // histogram complete; red free
-  float l_sum[G];
+  const __half* ckg = a.k_cb + int64_t(g) * M * K * DS;
+  const __half* cvg = a.v_cb + int64_t(g) * M * K * DS;
+  // table build: wave w owns segment m_l = w % M and codeword tiles
+  // nt = w / M + (NW / M) * i
+  const int m_l = wave % M;
+  f16x4 qa[KSTEP_Q];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float v = wave_sum(l_thr[h]);
-    if (lane == 0) red[wave * G + h] = v;
+  for (int s = 0; s < KSTEP_Q; ++s) {
+    if (l16 < G) {
+      qa[s] = *reinterpret_cast<const f16x4*>(a.q + (row0 + l16) * D + m_l * DS + s * 16 + 4 * q4);
+    } else {
+      qa[s] = f16x4{0, 0, 0, 0};
+    }
+  }
+  f16x4 ckb[LUT_JOBS][KSTEP_Q];
+#pragma unroll
+  for (int i = 0; i < LUT_JOBS; ++i) {
+    const int nt = wave / M + (NW / M) * i;
+    const __half* row = ckg + (int64_t(m_l) * K + nt * 16 + l16) * DS + 4 * q4;
+#pragma unroll
+    for (int s = 0; s < KSTEP_Q; ++s) ckb[i][s] = *reinterpret_cast<const f16x4*>(row + s * 16);
+  }
+  // contraction: wave w owns segment m_v and 16 output columns jt*16..+15.
+  // The MFMA wants, in lane (l16, q4), rows 4*q4..+3 of column l16 of each
+  // 16-codeword block; lane (4a + u, q4) loads row 4*q4 + u, columns
+  // 4a..4a+3 (8 contiguous bytes) and the quad transposes them.
+  const int m_v = wave % M;
+  const int jt = wave / M;
+  const int qu = l16 & 3;
+  uint2 cvr[K / 16];
+#pragma unroll
+  for (int s = 0; s < K / 16; ++s) {
+    const __half* src = cvg + (int64_t(m_v) * K + s * 16 + 4 * q4 + qu) * DS + jt * 16 + 4 * (l16 >> 2);
+    cvr[s] = *reinterpret_cast<const uint2*>(src);
+  }
+
+  // zero the histogram
+  if constexpr (G >= 2) {
+    for (int i = tid; i < M * GP * K / 2; i += NTHR)
+      reinterpret_cast<uint4*>(hist64)[i] = make_uint4(0, 0, 0, 0);
+  } else {
+    for (int i = tid; i < M * K / 4; i += NTHR)
+      reinterpret_cast<uint4*>(hist32)[i] = make_uint4(0, 0, 0, 0);
+  }
+
+  // ---- 1. lookup table on the matrix cores ----------------------------------
+#pragma unroll
+  for (int i = 0; i < LUT_JOBS; ++i) {
+    const int nt = wave / M + (NW / M) * i;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KSTEP_Q; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[s], ckb[i][s], acc, 0, 0, 0);
+    // lane holds LUT[h = 4*q4 + r][k = nt*16 + l16], r < 4
+    const int k = nt * 16 + l16;
+    if constexpr (G >= 4) {
+      if (4 * q4 < G)
+        *reinterpret_cast<float4*>(lut + lut_index<G, K>(m_l, k, q4)) =
+            make_float4(acc[0] * a.qscale, acc[1] * a.qscale, acc[2] * a.qscale, acc[3] * a.qscale);
+    } else if constexpr (G == 2) {
+      float* dst = lut + lut_index<G, K>(m_l, k, 0);
+      if (q4 == 0) *reinterpret_cast<float2*>(dst) = make_float2(acc[0] * a.qscale, acc[1] * a.qscale);
+    } else {
+      if (q4 == 0) lut[lut_index<G, K>(m_l, k, 0)] = acc[0] * a.qscale;
+    }
   }
   __syncthreads();
+
+  // ---- 2. scores --------------------------------------------------------------
+  float s[NT][G];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int t = t_begin + i * NTHR + tid;
+    if (t < t_end) {
+      token_scores<G, M, K>(lut, kcode[i], s[i]);
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[i][h] = -INFINITY;
+    }
+  }
+
+  // ---- 3. chunk max and probabilities ----------------------------------------
+  float m_c[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mx = s[0][h];
+#pragma unroll
+    for (int i = 1; i < NT; ++i) mx = fmaxf(mx, s[i][h]);
+    m_c[h] = mx;
+  }
+  wave_max_n<G>(m_c);
+  if (lane < G) {
+    float mine = m_c[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) mine = (lane == h) ? m_c[h] : mine;
+    red[wave * G + lane] = mine;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float mx = red[h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red[w * G + h]);
+    m_c[h] = mx;
+  }
+
+  // ---- 4. V histogram (fixed point, integer LDS atomics) -----------------------
+  float l_thr[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) l_thr[h] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int t = t_begin + i * NTHR + tid;
+    if (t < t_end) {
+      uint32_t u[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = fast_exp2(s[i][h] - m_c[h]);
+        l_thr[h] += p;
+        u[h] = uint32_t(fmaf(p, kFix, 0.5f));   // p * kFix <= 2^31 / Tmax, rounded
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int code = vcode[i].get(m);
+        if constexpr (G >= 2) {
+#pragma unroll
+          for (int pp = 0; pp < GP; ++pp) {
+            const uint64_t w = __builtin_bit_cast(uint64_t, make_uint2(u[2 * pp], u[2 * pp + 1]));
+            atomicAdd(reinterpret_cast<unsigned long long*>(hist64 + (m * GP + pp) * K + code),
+                      (unsigned long long)w);
+          }
+        } else {
+          atomicAdd(hist32 + m * K + code, u[0]);
+        }
+      }
+    }
+  }
+  wave_sum_n<G>(l_thr);
+  if (lane < G) {
+    float mine = l_thr[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) mine = (lane == h) ? l_thr[h] : mine;
+    red[NW * G + wave * G + lane] = mine;
+  }
+  __syncthreads();   // histogram and partial sums complete
+  float l_c[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) v += red[w * G + h];
-    l_sum[h] = v;
+    for (int w = 0; w < NW; ++w) v += red[NW * G + w * G + h];
+    l_c[h] = v;
   }
 
-  // ---- contraction with the V codebook ---------------------------------------
-  // thread -> column (m, j) and a slice of the codewords; slices are summed
-  // through LDS (the LUT is no longer needed).
-  constexpr int KS = NTHR / D;            // codeword slices
-  constexpr int KPER = K / KS;
-  {
-    const int col = tid % D;
-    const int ks = tid / D;
-    const int m = col / DS;
-    const int j = col % DS;
-    const __half* cbv = a.v_cb + int64_t(g) * M * K * DS + int64_t(m) * K * DS + j;
-    float acc[G];
+  // ---- 5. contraction with the V codebook on the matrix cores ----------------
+  // 5b. A[h][k] = Hist[m_v][k][h] (lanes l16 >= G are zero), B[k][j] = Cv[m_v][k][j]
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.0f;
-    const int k0 = ks * KPER;
-    for (int k = k0; k < k0 + KPER; ++k) {
-      const float w = __half2float(cbv[int64_t(k) * DS]);
-      const float* e = hist + (m * K + k) * G;
-#pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = fmaf(e[h], w, acc[h]);
+  for (int st = 0; st < K / 16; ++st) {
+    const int k0 = st * 16 + 4 * q4;
+    float hv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (l16 < G) {
+      if constexpr (G >= 2) {
+        const uint64_t* src = hist64 + (m_v * GP + (l16 >> 1)) * K + k0;
+        const uint4 w01 = reinterpret_cast<const uint4*>(src)[0];
+        const uint4 w23 = reinterpret_cast<const uint4*>(src)[1];
+        const bool hi = (l16 & 1) != 0;
+        hv[0] = float(hi ? w01.y : w01.x) * kUnfix;
+        hv[1] = float(hi ? w01.w : w01.z) * kUnfix;
+        hv[2] = float(hi ? w23.y : w23.x) * kUnfix;
+        hv[3] = float(hi ? w23.w : w23.z) * kUnfix;
+      } else {
+        const uint4 w = *reinterpret_cast<const uint4*>(hist32 + m_v * K + k0);
+        hv[0] = float(w.x) * kUnfix; hv[1] = float(w.y) * kUnfix;
+        hv[2] = float(w.z) * kUnfix; hv[3] = float(w.w) * kUnfix;
+      }
     }
+    f16x4 ahi, alo;
 #pragma unroll
-    for (int h = 0; h < G; ++h) lut[(ks * G + h) * D + col] = acc[h];
+    for (int t = 0; t < 4; ++t) { _Float16 x, y; split_f16(hv[t], x, y); ahi[t] = x; alo[t] = y; }
+    const f16x4 cvb = quad_transpose(cvr[st].x, cvr[st].y, qu);
+    o = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, cvb, o, 0, 0, 0);
+    o = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, cvb, o, 0, 0, 0);
+  }
+
+  // ---- 6. write (m, l, o) or the normalised output ----------------------------
+  // lane holds o[h = 4*q4 + r][d = m_v*DS + jt*16 + l16]; the chunk max and
+  // sum of head h are at red[h] and red[NW*G + h] (written below by wave 0's
+  // combine) -- reuse the per-wave slots: every thread already has m_c, l_c.
+  __shared__ float fin[2 * G];
+  if (tid < G) {
+    float mh = m_c[0], lh = l_c[0];
+#pragma unroll
+    for (int x = 1; x < G; ++x) {
+      mh = (tid == x) ? m_c[x] : mh;
+      lh = (tid == x) ? l_c[x] : lh;
+    }
+    fin[tid] = mh;
+    fin[G + tid] = lh;
   }
   __syncthreads();
-
-  for (int i = tid; i < G * D; i += NTHR) {
-    const int h = i / D, d = i % D;
-    float o = 0.0f;
+  const int d = m_v * DS + jt * 16 + l16;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) o += lut[(ks * G + h) * D + d];
-    if (a.out != nullptr) {
-      const float l = l_sum[h];
-      a.out[(row0 + h) * D + d] = l > 0.0f ? o / l : 0.0f;
-    } else {
-      a.part_o[((row0 + h) * a.C + c) * D + d] = o;
-      if (d == 0) {
-        a.part_m[(row0 + h) * a.C + c] = m_run[h] * kLn2;
-        a.part_l[(row0 + h) * a.C + c] = l_sum[h];
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * q4 + r;
+    if (h < G) {
+      const float mh = fin[h], lh = fin[G + h];
+      if (a.out != nullptr) {
+        a.out[(row0 + h) * D + d] = lh > 0.0f ? o[r] * __builtin_amdgcn_rcpf(lh) : 0.0f;
+      } else {
+        a.part_o[((row0 + h) * a.C + c) * D + d] = o[r];
+        if (d == 0) {
+          a.part_m[(row0 + h) * a.C + c] = mh * kLn2;
+          a.part_l[(row0 + h) * a.C + c] = lh;
+        }
       }
     }
   }

@@ -9,8 +9,8 @@ namespace pqattn {
 namespace {
 
 constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
-constexpr int kTargetBlocks = 512;     // two score workgroups per CU (256 CUs)
-constexpr int kChunkGranule = 256;     // one token per thread per pass
+constexpr int kTargetBlocks = 256;     // one score workgroup per CU (256 CUs)
+constexpr int kChunkGranule = 512;     // one token per thread of a 512-thread workgroup
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -25,6 +25,7 @@ int32_t pick_chunk(int32_t B, int32_t Hkv, int32_t Lmax, int32_t target_blocks, 
   int64_t t = (Lmax + want_chunks - 1) / want_chunks;
   t = (t + granule - 1) / granule * granule;
   if (t < granule) t = granule;
+  if (t > kMaxChunk) t = kMaxChunk;
   if (t > Lmax) t = Lmax;
   return int32_t(t);
 }
@@ -55,6 +56,7 @@ pq_status plan_attn(const pq_attn_desc* d, AttnPlan* p) {
   p->Lmax = d->max_len;
   p->T = d->chunk > 0 ? (d->chunk < d->max_len ? d->chunk : d->max_len)
                       : pick_chunk(d->batch, d->n_kv_heads, d->max_len, kTargetBlocks, kChunkGranule);
+  if (p->T > kMaxChunk) return PQ_ERR_UNSUPPORTED;
   p->C = int32_t((int64_t(p->Lmax) + p->T - 1) / p->T);
   p->scale = d->scale;
   p->rows = int64_t(p->B) * p->Hq;

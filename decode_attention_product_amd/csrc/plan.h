@@ -13,6 +13,7 @@ namespace pqattn {
 constexpr int kHeadDim = 128;   // D supported by the kernels
 constexpr int kCodes = 256;     // K codewords per segment codebook
 constexpr int kLenAlign = 16;   // cache capacity granularity, tokens
+constexpr int kMaxChunk = 4096; // longest chunk one score workgroup takes
 
 // A checked decode-attention shape with the chunking resolved.
 struct AttnPlan {

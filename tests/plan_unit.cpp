@@ -42,10 +42,13 @@ int main() {
   EXPECT(p.ws_l_off % 256 == 0 && p.ws_o_off % 256 == 0 && p.ws_bytes % 256 == 0);
   d.chunk = 7;
   EXPECT(plan_attn(&d, &p) == PQ_OK && p.C == (8192 + 6) / 7);
-  d.chunk = 8192;
+  d.chunk = 4096;
+  EXPECT(plan_attn(&d, &p) == PQ_OK && p.C == 2);
+  d.chunk = 8192;                                   // longer than one workgroup takes
+  EXPECT(plan_attn(&d, &p) == PQ_ERR_UNSUPPORTED);
+  d.max_len = 4096; d.chunk = 1 << 30;              // clamped to the capacity
   EXPECT(plan_attn(&d, &p) == PQ_OK && p.C == 1 && p.ws_bytes == 0);
-  d.chunk = 1 << 30;
-  EXPECT(plan_attn(&d, &p) == PQ_OK && p.C == 1);
+  d.max_len = 8192;
 
   // bad and unsupported
   d = base(); d.n_kv_heads = 7;                 EXPECT(plan_attn(&d, &p) == PQ_ERR_SHAPE);
@@ -62,6 +65,9 @@ int main() {
   EXPECT(pick_chunk(64, 32, 4096, 512, 256) == 4096);
   EXPECT(pick_chunk(1, 8, 131072, 512, 256) == 2048);
   EXPECT(pick_chunk(1, 1, 16, 512, 256) == 16);
+  EXPECT(pick_chunk(1, 1, 1 << 20, 256, 512) == kMaxChunk);
+  d = base(); d.chunk = 0;
+  EXPECT(plan_attn(&d, &p) == PQ_OK && p.T <= kMaxChunk && p.T % 512 == 0);
 
   // encode
   pq_encode_desc e;

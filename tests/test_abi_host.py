@@ -124,6 +124,16 @@ def test_chunking_and_workspace_sizes(lib):
     assert 8 * 8 * C3 >= 256 and 8192 % C3 == 0
 
 
+def test_chunk_longer_than_a_workgroup_takes(lib):
+    d = _desc(max_len=8192, chunk=4097)
+    assert lib.pq_attn_num_chunks(ctypes.byref(d)) == -1
+    assert lib.pq_attn_decode(ctypes.byref(d), *([FAKE] * 7), FAKE, 1 << 30, None) == 3
+    d = _desc(max_len=8192, chunk=4096)
+    assert lib.pq_attn_num_chunks(ctypes.byref(d)) == 2
+    d = _desc(max_len=4096, chunk=10000)      # clamped to the capacity first
+    assert lib.pq_attn_num_chunks(ctypes.byref(d)) == 1
+
+
 def test_reduce_checks(lib):
     assert lib.pq_attn_reduce(4, 0, 128, FAKE, FAKE, FAKE, FAKE, None) == 2
     assert lib.pq_attn_reduce(-1, 2, 128, FAKE, FAKE, FAKE, FAKE, None) == 2

@@ -259,9 +259,10 @@ def test_tokens_past_lens_are_not_read():
                              lens=[600, 17])
     t = gpu_inputs(inp)
     a = pq.pq_attn_decode(*t).clone()
-    t[1][:, :, 600:] ^= 0x33
-    t[2][:, :, 17:] ^= 0x5C
-    t[1][1, :, 17:] ^= 0x11
+    t[1][0, :, 600:] ^= 0x33          # request 0 attends 600 tokens
+    t[2][0, :, 600:] ^= 0x5C
+    t[1][1, :, 17:] ^= 0x11           # request 1 attends 17
+    t[2][1, :, 17:] ^= 0xC3
     b = pq.pq_attn_decode(*t)
     torch.cuda.synchronize()
     assert_attn_close(b.cpu().numpy(), oracle_out(inp), "after changing padding")
