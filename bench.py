@@ -83,6 +83,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0: enough for 512 MiB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--no-encode", action="store_true", help="skip the prefill-encode leg")
+    ap.add_argument("--encode-reps", type=int, default=5)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -208,9 +210,50 @@ def main():
                    "score_kernel_us_p50": float(np.median(kern_ms)) * 1e3,
                    "wall_s": wall, "tokens_per_step": tokens_per_step},
     }
+    if not args.no_encode:
+        result["encode"] = encode_leg(pq, torch, dev, args.encode_reps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wid)
     print(json.dumps(result), flush=True)
+
+
+def encode_leg(pq, torch, dev, reps):
+    """Prefill encode of the ragged workload: every prefill token's K and V
+    (6,455,296 vectors of D=128) by nearest codeword straight into the code
+    cache, timed with HIP events around `reps` K+V call pairs."""
+    from synth import gen
+    w = gen.WORKLOADS[5]
+    inp = gen.workload_inputs(5)
+    B, H, L, M = w.batch, w.n_kv_heads, w.max_len, w.n_sub
+    N = int(inp["lens"].sum())
+    t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev)
+         for k in ("x_k", "x_v", "k_cb", "v_cb", "k_codes", "v_codes", "slots")}
+    desc = pq.cache_encode_desc(N, B, H, L, n_sub=M)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        pq.pq_encode(t["x_k"], t["k_cb"], t["k_codes"], slots=t["slots"], desc=desc, stream=stream)
+        pq.pq_encode(t["x_v"], t["v_cb"], t["v_codes"], slots=t["slots"], desc=desc, stream=stream)
+
+    call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us_pair = a.elapsed_time(b) * 1e3 / reps
+    n_vec = 2 * N * H
+    bytes_pair = 2 * (N * H * w.head_dim * 2 + N * H * M + H * M * w.n_codes * w.sub_dim * 2)
+    flops_pair = n_vec * 2 * w.n_codes * w.head_dim
+    return {"value": n_vec / (us_pair * 1e-6), "unit": "vectors/s",
+            "workload": f"ragged prefill: {N} tokens x {H} heads x (K, V) = {n_vec} vectors",
+            "us_per_kv_pair": us_pair,
+            "hbm_gbs": bytes_pair / (us_pair * 1e-6) / 1e9,
+            "hbm_frac": bytes_pair / (us_pair * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "mfma_tflops": flops_pair / (us_pair * 1e-6) / 1e12,
+            "mfma_frac_fp16": flops_pair / (us_pair * 1e-6) / 1e12 / 2500.0}
 
 
 if __name__ == "__main__":

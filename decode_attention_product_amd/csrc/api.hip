@@ -16,8 +16,7 @@ namespace {
 static_assert(kMaxChunk == 8 * kDecodeThreads, "a chunk is at most 8 token slots per thread");
 
 constexpr int kReduceThreads = 128;
-constexpr int kEncodeThreads = 256;
-constexpr int kEncodeVectors = 128;
+constexpr int kEncodeVectors = 256;   // vectors per encode workgroup (one wave per segment)
 
 using DecodeFn = void (*)(DecodeArgs);
 
@@ -182,10 +181,9 @@ pq_status pq_encode(const pq_encode_desc* desc, const void* x, const void* codeb
   a.sxh = desc->x_stride_head;
   a.scs = desc->codes_stride_slot;
   a.sch = desc->codes_stride_head;
-  const void* fn = p.M == 4
-      ? reinterpret_cast<const void*>(&encode_kernel<4, kEncodeVectors, kEncodeThreads>)
-      : reinterpret_cast<const void*>(&encode_kernel<8, kEncodeVectors, kEncodeThreads>);
-  return launch(fn, dim3(unsigned(p.blocks_x), unsigned(p.H)), dim3(kEncodeThreads), &a,
+  const void* fn = p.M == 4 ? reinterpret_cast<const void*>(&encode_kernel<4, kEncodeVectors>)
+                            : reinterpret_cast<const void*>(&encode_kernel<8, kEncodeVectors>);
+  return launch(fn, dim3(unsigned(p.blocks_x), unsigned(p.H)), dim3(64 * p.M), &a,
                 static_cast<hipStream_t>(stream));
 }
 

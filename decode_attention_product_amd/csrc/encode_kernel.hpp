@@ -1,21 +1,28 @@
 // Nearest-codeword PQ encode kernel (gfx950).
 //
-// For every vector, head and segment m the index of the codeword at the
+// For every vector, head and segment m, the index of the codeword at the
 // smallest squared Euclidean distance (AQPIM page, sections 3.1 and
-// 5.2 (2)); the lowest index wins a tie.  Since |x - c|^2 = |x|^2 + |c|^2 -
-// 2 x.c and |x|^2 does not depend on the codeword, the kernel ranks
-// |c|^2 - 2 x.c, with x.c from v_dot2_f32_f16 (fp16 products, fp32 sums).
+// 5.2 (2)); the lowest index wins a tie.  Since
+//   |x - c|^2 = |x|^2 - 2 (x.c - |c|^2 / 2)
+// and |x|^2 does not depend on the codeword, the kernel takes the argmax of
+// x.c - |c|^2/2.  The dot products of 16 vectors with 16 codewords are one
+// matrix-core instruction (fp16 inputs, exact products, fp32 sums) whose
+// accumulator starts at -|c|^2/2, so the scores come out ready to compare.
 //
-// One workgroup owns one head and a tile of NV vectors, staged in LDS.  For
-// each segment every lane holds four codewords of that segment in registers
-// (k = lane, lane+64, lane+128, lane+192); a wave takes one vector at a
-// time, each lane ranks its four codewords, and a butterfly of cross-lane
-// exchanges finds the wave's (distance, index) minimum.
+// Workgroup = one head and a tile of NV vectors; wave w handles segment
+// m = w, holding that segment's 256 codewords in registers as MFMA B
+// operands for the whole tile.  Lane (l16, q4) of an instruction's result
+// holds vectors 4*q4 .. 4*q4+3 against codeword nt*16 + l16; each lane keeps
+// a running best over the 16 codeword tiles, then the 16 lanes of a row
+// reduce (score, index) with DPP -- larger score, or equal score and lower
+// index, wins.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
+
+#include "decode_kernel.hpp"   // f16x4, f32x4, DPP helpers
 
 namespace pqattn {
 
@@ -31,87 +38,130 @@ struct EncodeArgs {
   int64_t sxv, sxh, scs, sch;
 };
 
-template <int M, int NV, int NTHR>
-__global__ __launch_bounds__(NTHR) void encode_kernel(EncodeArgs a) {
+template <int CTRL>
+__device__ __forceinline__ int dpp_int(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+
+// (score, index) -> the better of the pair and its DPP partner.
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& s, int& k) {
+  const float os = dpp_f<CTRL>(s);
+  const int ok = dpp_int<CTRL>(k);
+  const bool take = (os > s) || (os == s && ok < k);
+  s = take ? os : s;
+  k = take ? ok : k;
+}
+
+template <int M, int NV>
+__global__ __launch_bounds__(64 * M) void encode_kernel(EncodeArgs a) {
   constexpr int D = 128;
   constexpr int K = 256;
   constexpr int DS = D / M;
-  constexpr int NW = NTHR / 64;
-  constexpr int R = K / 64;            // codewords per lane
+  constexpr int KS = DS / 16;          // MFMA k-steps per segment
+  constexpr int NTILE = NV / 16;       // 16-vector tiles
+  constexpr int NCT = K / 16;          // 16-codeword tiles
 
-  __shared__ uint4 xs[NV * D / 8];     // the tile's vectors, fp16
-  __shared__ __align__(16) uint8_t cs[NV * M];   // chosen codes
+  __shared__ __align__(16) uint8_t cs[NV * M];   // chosen codes [v][m]
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int m = threadIdx.x >> 6;      // this wave's segment
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
   const int h = blockIdx.y;
   const int64_t n0 = int64_t(blockIdx.x) * NV;
   const int nv = int(min<int64_t>(NV, a.N - n0));
 
-  for (int e = tid; e < nv * (D / 8); e += NTHR) {
-    const int v = e / (D / 8), part = e % (D / 8);
-    xs[e] = *reinterpret_cast<const uint4*>(a.x + (n0 + v) * a.sxv + int64_t(h) * a.sxh + part * 8);
+  // ---- codebook of (h, m) as MFMA B operands ------------------------------
+  const __half* cb = a.cb + (int64_t(h) * M + m) * K * DS;
+  f16x4 bop[NCT][KS];
+#pragma unroll
+  for (int nt = 0; nt < NCT; ++nt)
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      bop[nt][s] = *reinterpret_cast<const f16x4*>(cb + (nt * 16 + l16) * DS + s * 16 + 4 * q4);
+
+  // A operands (16 vectors x this segment) of one tile; the next tile's are
+  // requested while the current one is scored
+  auto load_a = [&](int t, f16x4 (&dst)[KS]) {
+    const int v = t * 16 + l16;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (v < nv) {
+        dst[s] = *reinterpret_cast<const f16x4*>(a.x + (n0 + v) * a.sxv + int64_t(h) * a.sxh +
+                                                 m * DS + s * 16 + 4 * q4);
+      } else {
+        dst[s] = f16x4{0, 0, 0, 0};
+      }
+    }
+  };
+  f16x4 acur[KS], anext[KS];
+  load_a(0, acur);
+
+  // -|c|^2 / 2 of codeword nt*16 + l16: this lane's 4*KS elements, then the
+  // four lanes l16, l16+16, l16+32, l16+48 that share the codeword
+  float cinit[NCT];
+#pragma unroll
+  for (int nt = 0; nt < NCT; ++nt) {
+    float p = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const f16x2 lo = {bop[nt][s][0], bop[nt][s][1]};
+      const f16x2 hi = {bop[nt][s][2], bop[nt][s][3]};
+      p = __builtin_amdgcn_fdot2(lo, lo, p, false);
+      p = __builtin_amdgcn_fdot2(hi, hi, p, false);
+    }
+    p += __shfl_xor(p, 16, 64);
+    p += __shfl_xor(p, 32, 64);
+    cinit[nt] = -0.5f * p;
+  }
+
+  // ---- scores, running argmax, row reduction ------------------------------
+  for (int t = 0; t < NTILE; ++t) {
+    if (t * 16 >= nv) break;           // uniform over the workgroup
+    if (t + 1 < NTILE) load_a(t + 1, anext);
+    float best[4];
+    int bk[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { best[r] = -INFINITY; bk[r] = l16; }
+#pragma unroll
+    for (int nt = 0; nt < NCT; ++nt) {
+      f32x4 acc = {cinit[nt], cinit[nt], cinit[nt], cinit[nt]};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(acur[s], bop[nt][s], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool take = acc[r] > best[r];   // ascending codewords: ties keep the lower
+        best[r] = take ? acc[r] : best[r];
+        bk[r] = take ? nt * 16 + l16 : bk[r];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      argmax_step<kDppXor1>(best[r], bk[r]);
+      argmax_step<kDppXor2>(best[r], bk[r]);
+      argmax_step<kDppRor4>(best[r], bk[r]);
+      argmax_step<kDppRor8>(best[r], bk[r]);
+    }
+    if (l16 == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = t * 16 + 4 * q4 + r;
+        if (v < nv) cs[v * M + m] = uint8_t(bk[r]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acur[s] = anext[s];
   }
   __syncthreads();
 
-  for (int m = 0; m < M; ++m) {
-    // this lane's codewords of segment m, and their squared norms
-    f16x2 cw[R][DS / 2];
-    float nrm[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int k = lane + 64 * r;
-      const uint4* src = reinterpret_cast<const uint4*>(a.cb + ((int64_t(h) * M + m) * K + k) * DS);
-#pragma unroll
-      for (int v = 0; v < DS / 8; ++v) {
-        uint4 u = src[v];
-        const f16x2* p2 = reinterpret_cast<const f16x2*>(&u);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cw[r][v * 4 + e] = p2[e];
-      }
-      float s = 0.0f;
-#pragma unroll
-      for (int j = 0; j < DS / 2; ++j) s = __builtin_amdgcn_fdot2(cw[r][j], cw[r][j], s, false);
-      nrm[r] = s;
-    }
-    for (int v = wave; v < nv; v += NW) {
-      f16x2 xv[DS / 2];
-      const uint4* xrow = xs + v * (D / 8) + m * (DS / 8);
-#pragma unroll
-      for (int q = 0; q < DS / 8; ++q) {
-        uint4 u = xrow[q];
-        const f16x2* p2 = reinterpret_cast<const f16x2*>(&u);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) xv[q * 4 + e] = p2[e];
-      }
-      float best = INFINITY;
-      int bi = 0;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float dot = 0.0f;
-#pragma unroll
-        for (int j = 0; j < DS / 2; ++j) dot = __builtin_amdgcn_fdot2(xv[j], cw[r][j], dot, false);
-        const float dist = fmaf(-2.0f, dot, nrm[r]);
-        if (dist < best) { best = dist; bi = lane + 64 * r; }   // r ascending: lower k kept on ties
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ob = __shfl_xor(best, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
-      }
-      if (lane == 0) cs[v * M + m] = uint8_t(bi);
-    }
-  }
-  __syncthreads();
-
-  for (int v = tid; v < nv; v += NTHR) {
+  for (int v = threadIdx.x; v < nv; v += 64 * M) {
     const int64_t n = n0 + v;
     const int64_t s = a.slots ? a.slots[n] : n;
     if (s < 0 || (a.scs > 0 && s > a.codes_bytes / a.scs)) continue;
     const int64_t off = s * a.scs + int64_t(h) * a.sch;
-    if (off + M > a.codes_bytes) continue;
+    if (off < 0 || off + M > a.codes_bytes) continue;
     uint8_t* dst = a.codes + off;
     if constexpr (M == 4) {
       *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(cs + v * M);
