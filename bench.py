@@ -45,6 +45,62 @@ def algorithmic_bytes(w, lens):
     return codes + cbs + q + out
 
 
+class HipEvents:
+    """Raw hipEvent_t handles from the process's HIP runtime (the one torch
+    loaded), for pq_attn_partials_timed, which has the runtime stamp them at
+    the score kernel's own start and end."""
+
+    def __init__(self):
+        import ctypes
+        path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l)
+        self.hip = ctypes.CDLL(path)
+        self.ct = ctypes
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            h = self.ct.c_void_p()
+            if self.hip.hipEventCreate(self.ct.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(h.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        f = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(f), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partials_gqa_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_product_amd", "csrc", "decode_kernel.hpp")
+
+
+def kernel_source_hash():
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per score-kernel launch from the committed counter runs, or
+    None when the kernel source changed since they were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def cpu_baseline(wid, min_seconds=10.0, max_seconds=30.0):
     import oracle
     from synth import gen
@@ -85,6 +141,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--no-encode", action="store_true", help="skip the prefill-encode leg")
     ap.add_argument("--encode-reps", type=int, default=5)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run 3 device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -139,27 +197,22 @@ def main():
     def step(t, ev=None):
         pq.pq_encode(t["xk"], t["k_cb"], t["k_codes"], slots=t["slots"], desc=enc_desc, stream=stream)
         pq.pq_encode(t["xv"], t["v_cb"], t["v_codes"], slots=t["slots"], desc=enc_desc, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
-        if C > 1:
-            pq.pq_attn_partials(t["q"], t["k_codes"], t["v_codes"], t["k_cb"], t["v_cb"], t["lens"],
-                                desc=desc, part_m=pm, part_l=pl, part_o=po, stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
-            pq.pq_attn_reduce(pm, pl, po, out, stream=stream)
-        else:
-            pq.pq_attn_decode(t["q"], t["k_codes"], t["v_codes"], t["k_cb"], t["v_cb"], t["lens"],
-                              out, desc=desc, stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
+        # the score kernel writes the chunk records; the merge kernel reads them
+        # (for C == 1 the merge is a pass over one record per row)
+        pq.pq_attn_partials(t["q"], t["k_codes"], t["v_codes"], t["k_cb"], t["v_cb"], t["lens"],
+                            desc=desc, part_m=pm, part_l=pl, part_o=po, stream=stream, events=ev)
+        pq.pq_attn_reduce(pm, pl, po, out, stream=stream)
 
     for i in range(args.warmup):
         step(reps[i % R])
     torch.cuda.synchronize()
 
     K = args.steps
-    # (a) the timed region: K whole steps, events around each score kernel
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    # (a) the timed region: K whole steps; the runtime stamps a pair of events
+    # at each score kernel's own start and end
+    hip = HipEvents()
+    raw = hip.create(2 * K)
+    evs = [(raw[2 * i], raw[2 * i + 1]) for i in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -170,7 +223,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = start.elapsed_time(end) / K
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_ms = [hip.elapsed_ms(a, b) for a, b in evs]
+    hip.destroy(raw)
     score_ms = float(np.mean(kern_ms))
 
     # (b) the same steps without the per-kernel events (the throughput figure)
@@ -203,13 +257,22 @@ def main():
                    "chunk": int(desc.chunk) or "library", "n_chunks": C, "replicas": R,
                    "step": "encode new K,V -> score kernel -> merge kernel"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(),
                      "kernel": "decode_partials_kernel", "algorithmic_bytes": alg,
                      "avg_launch_us": score_ms * 1e3},
         "detail": {"step_us_with_kernel_events": step_ms * 1e3, "step_us": step_ms_plain * 1e3,
                    "score_kernel_us_p50": float(np.median(kern_ms)) * 1e3,
                    "wall_s": wall, "tokens_per_step": tokens_per_step},
     }
+    if args.copy_probe_mib:
+        # a plain device copy of known size, to calibrate FETCH_SIZE/WRITE_SIZE
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = n
     if not args.no_encode:
         result["encode"] = encode_leg(pq, torch, dev, args.encode_reps)
     if not args.no_cpu_baseline:

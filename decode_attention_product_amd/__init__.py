@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "PQ_OK", 1: "PQ_ERR_NULL", 2: "PQ_ERR_SHAPE", 3: "PQ_ERR_UNSU
                 4: "PQ_ERR_WORKSPACE", 5: "PQ_ERR_HIP", 6: "PQ_ERR_ALIGN"}
 
 EXPORTED = ("pq_attn_num_chunks", "pq_attn_workspace_bytes", "pq_attn_decode",
-            "pq_attn_partials", "pq_attn_reduce", "pq_encode", "pq_status_string")
+            "pq_attn_partials", "pq_attn_partials_timed", "pq_attn_reduce", "pq_encode",
+            "pq_status_string")
 
 
 class PQError(RuntimeError):
@@ -69,6 +70,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pq_attn_decode.restype = ctypes.c_int
     lib.pq_attn_partials.argtypes = [ctypes.POINTER(PQAttnDesc), P, P, P, P, P, P, P, P, P, P]
     lib.pq_attn_partials.restype = ctypes.c_int
+    lib.pq_attn_partials_timed.argtypes = [ctypes.POINTER(PQAttnDesc), P, P, P, P, P, P, P, P, P,
+                                           P, P, P]
+    lib.pq_attn_partials_timed.restype = ctypes.c_int
     lib.pq_attn_reduce.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
     lib.pq_attn_reduce.restype = ctypes.c_int
     lib.pq_encode.argtypes = [ctypes.POINTER(PQEncodeDesc), P, P, P, P, P]
@@ -172,9 +176,11 @@ def pq_attn_decode(q, k_codes, v_codes, k_cb, v_cb, lens, out=None, *, desc=None
 
 
 def pq_attn_partials(q, k_codes, v_codes, k_cb, v_cb, lens, *, desc=None, chunk=0, scale=None,
-                     part_m=None, part_l=None, part_o=None, stream=None):
+                     part_m=None, part_l=None, part_o=None, stream=None, events=None):
     """Chunk statistics (C entry point pq_attn_partials).  Returns
-    (part_m [B,Hq,C], part_l [B,Hq,C], part_o [B,Hq,C,D]), fp32."""
+    (part_m [B,Hq,C], part_l [B,Hq,C], part_o [B,Hq,C,D]), fp32.  With
+    ``events=(start, stop)`` (raw hipEvent_t handles) the call goes through
+    pq_attn_partials_timed and the events bracket the kernel's execution."""
     import torch
     if desc is None:
         desc = attn_desc(q, k_codes, k_cb, chunk=chunk, scale=scale)
@@ -191,9 +197,13 @@ def pq_attn_partials(q, k_codes, v_codes, k_cb, v_cb, lens, *, desc=None, chunk=
     _need(part_m, "part_m", torch.float32, (B, Hq, C))
     _need(part_l, "part_l", torch.float32, (B, Hq, C))
     _need(part_o, "part_o", torch.float32, (B, Hq, C, D))
-    st = load_library().pq_attn_partials(
-        ctypes.byref(desc), _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_cb), _ptr(v_cb),
-        _ptr(lens), _ptr(part_m), _ptr(part_l), _ptr(part_o), _stream(stream))
+    lib = load_library()
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_cb), _ptr(v_cb),
+            _ptr(lens), _ptr(part_m), _ptr(part_l), _ptr(part_o), _stream(stream))
+    if events is None:
+        st = lib.pq_attn_partials(*args)
+    else:
+        st = lib.pq_attn_partials_timed(*args, events[0], events[1])
     _check(st, "pq_attn_partials")
     return part_m, part_l, part_o
 

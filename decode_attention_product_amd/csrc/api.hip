@@ -2,6 +2,7 @@
 // include/pqattn.h).  Each call checks its arguments on the host, picks the
 // kernel instance for the shape and enqueues it on the caller's stream.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cmath>
 
@@ -44,9 +45,14 @@ DecodeFn pick_decode(int G, int M, int T) {
   return nullptr;
 }
 
-pq_status launch(const void* fn, dim3 grid, dim3 block, void* arg, hipStream_t stream) {
+// Launch; with events, the runtime stamps them at the kernel's own start and
+// end (hipExtLaunchKernel), which is what a kernel timer should see.
+pq_status launch(const void* fn, dim3 grid, dim3 block, void* arg, hipStream_t stream,
+                 hipEvent_t start = nullptr, hipEvent_t stop = nullptr) {
   void* args[] = {arg};
-  const hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
+  const hipError_t e = (start || stop)
+      ? hipExtLaunchKernel(fn, grid, block, args, 0, stream, start, stop, 0)
+      : hipLaunchKernel(fn, grid, block, args, 0, stream);
   return e == hipSuccess ? PQ_OK : PQ_ERR_HIP;
 }
 
@@ -60,7 +66,8 @@ pq_status check_attn_pointers(const void* q, const void* kc, const void* vc, con
 
 pq_status launch_partials(const AttnPlan& p, const void* q, const uint8_t* kc, const uint8_t* vc,
                           const void* kcb, const void* vcb, const int32_t* lens, float* pm,
-                          float* pl, float* po, float* out, hipStream_t stream) {
+                          float* pl, float* po, float* out, hipStream_t stream,
+                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr) {
   DecodeArgs a;
   a.q = static_cast<const __half*>(q);
   a.k_codes = kc;
@@ -81,7 +88,7 @@ pq_status launch_partials(const AttnPlan& p, const void* q, const uint8_t* kc, c
   DecodeFn fn = pick_decode(p.G, p.M, p.T);
   if (!fn) return PQ_ERR_UNSUPPORTED;
   return launch(reinterpret_cast<const void*>(fn), dim3(unsigned(p.blocks)), dim3(kDecodeThreads),
-                &a, stream);
+                &a, stream, start, stop);
 }
 
 pq_status launch_reduce(int64_t rows, int32_t C, const float* pm, const float* pl, const float* po,
@@ -145,6 +152,21 @@ pq_status pq_attn_partials(const pq_attn_desc* desc, const void* q, const uint8_
   if (!part_m || !part_l || !part_o) return PQ_ERR_NULL;
   return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, part_m, part_l, part_o, nullptr,
                          static_cast<hipStream_t>(stream));
+}
+
+pq_status pq_attn_partials_timed(const pq_attn_desc* desc, const void* q, const uint8_t* k_codes,
+                                 const uint8_t* v_codes, const void* k_cb, const void* v_cb,
+                                 const int32_t* lens, float* part_m, float* part_l, float* part_o,
+                                 void* stream, void* start_event, void* stop_event) {
+  AttnPlan p;
+  pq_status st = plan_attn(desc, &p);
+  if (st != PQ_OK) return st;
+  st = check_attn_pointers(q, k_codes, v_codes, k_cb, v_cb, lens);
+  if (st != PQ_OK) return st;
+  if (!part_m || !part_l || !part_o) return PQ_ERR_NULL;
+  return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, part_m, part_l, part_o, nullptr,
+                         static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
+                         static_cast<hipEvent_t>(stop_event));
 }
 
 pq_status pq_attn_reduce(int64_t n_rows, int32_t n_chunks, int32_t head_dim, const float* part_m,

@@ -107,6 +107,17 @@ pq_status pq_attn_partials(const pq_attn_desc* desc, const void* q,
                            const void* k_cb, const void* v_cb, const int32_t* lens,
                            float* part_m, float* part_l, float* part_o, void* stream);
 
+/* pq_attn_partials for kernel timing: start_event and stop_event (hipEvent_t
+ * handles created by the caller, either may be NULL) are stamped by the
+ * runtime at the score kernel's own start and end (hipExtLaunchKernel), so
+ * hipEventElapsedTime between them is the kernel's execution time.
+ * Everything else is exactly pq_attn_partials. */
+pq_status pq_attn_partials_timed(const pq_attn_desc* desc, const void* q,
+                                 const uint8_t* k_codes, const uint8_t* v_codes,
+                                 const void* k_cb, const void* v_cb, const int32_t* lens,
+                                 float* part_m, float* part_l, float* part_o, void* stream,
+                                 void* start_event, void* stop_event);
+
 /* Merge chunk statistics (PAM page, section 2.2.3 (3); the rescaling of the
  * memory-wall chapter's online softmax, section 1.4.3 (5.1)):
  *   out[r] = sum_c w_c o[r][c] / sum_c w_c l[r][c],  w_c = exp(m[r][c] - max_c m[r][c])

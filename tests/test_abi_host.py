@@ -36,8 +36,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert set(names) == {"pq_attn_num_chunks", "pq_attn_workspace_bytes", "pq_attn_decode",
-                          "pq_attn_partials", "pq_attn_reduce", "pq_encode", "pq_status_string"}
+    assert set(names) == set(pq.EXPORTED)
     out = subprocess.run(["nm", "-D", "--defined-only", pq.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (pq_\w+)$", out, flags=re.M))
@@ -73,6 +72,8 @@ def test_bad_descriptor(lib, field, value, status):
     st = lib.pq_attn_decode(ctypes.byref(d), *([FAKE] * 7), FAKE, 1 << 30, None)
     assert st == status
     st = lib.pq_attn_partials(ctypes.byref(d), *([FAKE] * 9), None)
+    assert st == status
+    st = lib.pq_attn_partials_timed(ctypes.byref(d), *([FAKE] * 9), None, None, None)
     assert st == status
 
 
