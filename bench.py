@@ -1,8 +1,8 @@
 """Benchmark of one decode step over a PQ-coded KV cache on one MI355X.
 
 A step is the whole hot path for one layer and one new token:
-  1. encode the new token's K and V vectors (B*Hkv each) by nearest codeword
-     straight into the code cache, at position lens[b]-1;
+  1. encode the new token's K and V vectors (B*Hkv each, one launch) by
+     nearest codeword straight into the code cache, at position lens[b]-1;
   2. the fused score kernel (LUT build, code streaming, chunk softmax,
      V histograms, codebook contraction) -> per-chunk (m, l, o);
   3. the chunk-merge kernel -> out.
@@ -195,8 +195,9 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(t, ev=None):
-        pq.pq_encode(t["xk"], t["k_cb"], t["k_codes"], slots=t["slots"], desc=enc_desc, stream=stream)
-        pq.pq_encode(t["xv"], t["v_cb"], t["v_codes"], slots=t["slots"], desc=enc_desc, stream=stream)
+        # the new token's K and V, one launch
+        pq.pq_encode_many([t["xk"], t["xv"]], [t["k_cb"], t["v_cb"]], [t["k_codes"], t["v_codes"]],
+                          slots=t["slots"], desc=enc_desc, stream=stream)
         # the score kernel writes the chunk records; the merge kernel reads them
         # (for C == 1 the merge is a pass over one record per row)
         pq.pq_attn_partials(t["q"], t["k_codes"], t["v_codes"], t["k_cb"], t["v_cb"], t["lens"],
@@ -255,7 +256,7 @@ def main():
         "data": "synthetic (seeded generators; codebooks and q fp16 N(0,1), codes uniform uint8)",
         "config": {"workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} L={L} D={D} M={M} K={w.n_codes}",
                    "chunk": int(desc.chunk) or "library", "n_chunks": C, "replicas": R,
-                   "step": "encode new K,V -> score kernel -> merge kernel"},
+                   "step": "encode new K and V (one launch) -> score kernel -> merge kernel"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(),
                      "kernel": "decode_partials_kernel", "algorithmic_bytes": alg,
@@ -283,7 +284,7 @@ def main():
 def encode_leg(pq, torch, dev, reps):
     """Prefill encode of the ragged workload: every prefill token's K and V
     (6,455,296 vectors of D=128) by nearest codeword straight into the code
-    cache, timed with HIP events around `reps` K+V call pairs."""
+    cache (K and V in one launch), timed with HIP events around `reps` calls."""
     from synth import gen
     w = gen.WORKLOADS[5]
     inp = gen.workload_inputs(5)
@@ -295,8 +296,8 @@ def encode_leg(pq, torch, dev, reps):
     stream = torch.cuda.current_stream()
 
     def call():
-        pq.pq_encode(t["x_k"], t["k_cb"], t["k_codes"], slots=t["slots"], desc=desc, stream=stream)
-        pq.pq_encode(t["x_v"], t["v_cb"], t["v_codes"], slots=t["slots"], desc=desc, stream=stream)
+        pq.pq_encode_many([t["x_k"], t["x_v"]], [t["k_cb"], t["v_cb"]], [t["k_codes"], t["v_codes"]],
+                          slots=t["slots"], desc=desc, stream=stream)
 
     call()
     torch.cuda.synchronize()

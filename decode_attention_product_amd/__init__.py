@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "PQ_OK", 1: "PQ_ERR_NULL", 2: "PQ_ERR_SHAPE", 3: "PQ_ERR_UNSU
 
 EXPORTED = ("pq_attn_num_chunks", "pq_attn_workspace_bytes", "pq_attn_decode",
             "pq_attn_partials", "pq_attn_partials_timed", "pq_attn_reduce", "pq_encode",
-            "pq_status_string")
+            "pq_encode_many", "pq_status_string")
 
 
 class PQError(RuntimeError):
@@ -77,6 +77,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pq_attn_reduce.restype = ctypes.c_int
     lib.pq_encode.argtypes = [ctypes.POINTER(PQEncodeDesc), P, P, P, P, P]
     lib.pq_encode.restype = ctypes.c_int
+    lib.pq_encode_many.argtypes = [ctypes.POINTER(PQEncodeDesc), ctypes.c_int32,
+                                   ctypes.POINTER(P), ctypes.POINTER(P), P, ctypes.POINTER(P), P]
+    lib.pq_encode_many.restype = ctypes.c_int
     lib.pq_status_string.argtypes = [ctypes.c_int]
     lib.pq_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -249,6 +252,30 @@ def pq_encode(x, codebook, codes, *, slots=None, desc=None, stream=None):
     st = load_library().pq_encode(ctypes.byref(desc), _ptr(x), _ptr(codebook), _ptr(slots),
                                   _ptr(codes), _stream(stream))
     _check(st, "pq_encode")
+    return codes
+
+
+def pq_encode_many(xs, codebooks, codes, *, desc, slots=None, stream=None):
+    """Encode several tensors of one shape in one launch (C entry point
+    pq_encode_many), e.g. a new token's K and V: plane i gets what
+    pq_encode(xs[i], codebooks[i], codes[i], ...) gives."""
+    import torch
+    n = len(xs)
+    if not (len(codebooks) == len(codes) == n):
+        raise ValueError("xs, codebooks and codes must have the same length")
+    for t in xs:
+        _need(t, "x", torch.float16, None)
+    for t in codebooks:
+        _need(t, "codebook", torch.float16, None)
+    for t in codes:
+        _need(t, "codes", torch.uint8, None)
+    if slots is not None:
+        _need(slots, "slots", torch.int64, None)
+    arr = ctypes.c_void_p * max(n, 1)
+    st = load_library().pq_encode_many(
+        ctypes.byref(desc), n, arr(*[_ptr(t) for t in xs]), arr(*[_ptr(t) for t in codebooks]),
+        _ptr(slots), arr(*[_ptr(t) for t in codes]), _stream(stream))
+    _check(st, "pq_encode_many")
     return codes
 
 

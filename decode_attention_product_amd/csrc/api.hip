@@ -178,25 +178,37 @@ pq_status pq_attn_reduce(int64_t n_rows, int32_t n_chunks, int32_t head_dim, con
                        static_cast<hipStream_t>(stream));
 }
 
-pq_status pq_encode(const pq_encode_desc* desc, const void* x, const void* codebook,
-                    const int64_t* slots, uint8_t* codes, void* stream) {
+}  // extern "C"
+
+namespace pqattn {
+namespace {
+
+pq_status encode_planes(const pq_encode_desc* desc, int32_t n, const void* const* x,
+                        const void* const* codebook, const int64_t* slots, uint8_t* const* codes,
+                        hipStream_t stream) {
   EncodePlan p;
   pq_status st = plan_encode(desc, kEncodeVectors, &p);
   if (st != PQ_OK) return st;
+  if (n < 1 || n > kMaxEncodePlanes) return PQ_ERR_SHAPE;
   if (!x || !codebook || !codes) return PQ_ERR_NULL;
-  if (!aligned16(x) || !aligned16(codebook)) return PQ_ERR_ALIGN;
-  if ((reinterpret_cast<uintptr_t>(codes) % p.M) != 0) return PQ_ERR_ALIGN;
+  for (int i = 0; i < n; ++i) {
+    if (!x[i] || !codebook[i] || !codes[i]) return PQ_ERR_NULL;
+    if (!aligned16(x[i]) || !aligned16(codebook[i])) return PQ_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(codes[i]) % p.M) != 0) return PQ_ERR_ALIGN;
+  }
   if (p.N == 0) return PQ_OK;
   if (!slots) {   // identity places: the last one must fit
     const double last = double(p.N - 1) * double(desc->codes_stride_slot) +
                         double(p.H - 1) * double(desc->codes_stride_head) + p.M;
     if (last > double(desc->codes_bytes)) return PQ_ERR_SHAPE;
   }
-  EncodeArgs a;
-  a.x = static_cast<const __half*>(x);
-  a.cb = static_cast<const __half*>(codebook);
+  EncodeArgs a{};
+  for (int i = 0; i < n; ++i) {
+    a.x[i] = static_cast<const __half*>(x[i]);
+    a.cb[i] = static_cast<const __half*>(codebook[i]);
+    a.codes[i] = codes[i];
+  }
   a.slots = slots;
-  a.codes = codes;
   a.N = p.N;
   a.codes_bytes = desc->codes_bytes;
   a.sxv = desc->x_stride_vec;
@@ -205,8 +217,24 @@ pq_status pq_encode(const pq_encode_desc* desc, const void* x, const void* codeb
   a.sch = desc->codes_stride_head;
   const void* fn = p.M == 4 ? reinterpret_cast<const void*>(&encode_kernel<4, kEncodeVectors>)
                             : reinterpret_cast<const void*>(&encode_kernel<8, kEncodeVectors>);
-  return launch(fn, dim3(unsigned(p.blocks_x), unsigned(p.H)), dim3(64 * p.M), &a,
-                static_cast<hipStream_t>(stream));
+  return launch(fn, dim3(unsigned(p.blocks_x), unsigned(p.H), unsigned(n)), dim3(64 * p.M), &a,
+                stream);
+}
+
+}  // namespace
+}  // namespace pqattn
+
+extern "C" {
+
+pq_status pq_encode(const pq_encode_desc* desc, const void* x, const void* codebook,
+                    const int64_t* slots, uint8_t* codes, void* stream) {
+  return encode_planes(desc, 1, &x, &codebook, slots, &codes, static_cast<hipStream_t>(stream));
+}
+
+pq_status pq_encode_many(const pq_encode_desc* desc, int32_t n, const void* const* x,
+                         const void* const* codebook, const int64_t* slots,
+                         uint8_t* const* codes, void* stream) {
+  return encode_planes(desc, n, x, codebook, slots, codes, static_cast<hipStream_t>(stream));
 }
 
 const char* pq_status_string(pq_status status) { return status_string(status); }

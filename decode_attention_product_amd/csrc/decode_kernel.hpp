@@ -230,9 +230,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   constexpr float kFix = float(1u << 31) / float(NT * NTHR);
   constexpr float kUnfix = float(NT * NTHR) / float(1u << 31);
 
-  __shared__ __align__(16) float lut[M * K * G];                          // see lut_index
-  __shared__ __align__(16) uint64_t hist64[G >= 2 ? M * GP * K : 2];      // [m][pair][k]
-  __shared__ __align__(16) uint32_t hist32[G == 1 ? M * K : 4];           // [m][k]
+  // The table is read only while scoring and the histogram is written only
+  // after the scores sit in registers, so both live in one LDS region (half
+  // the LDS of separate arrays: two workgroups fit on a CU).
+  // Histogram rows [m][pair] are padded by HPAD words so that the rows a
+  // wave reads side by side in the contraction start on different banks.
+  constexpr int HPAD = 2;
+  constexpr int HROW = K + HPAD;                                           // u64 per row
+  constexpr int LUT_WORDS = M * K * G;
+  constexpr int HIST_WORDS = G >= 2 ? M * GP * HROW * 2 : M * K;
+  __shared__ __align__(16) float lut[LUT_WORDS > HIST_WORDS ? LUT_WORDS : HIST_WORDS];
+  uint64_t* hist64 = reinterpret_cast<uint64_t*>(lut);                    // [m][pair][HROW]
+  uint32_t* hist32 = reinterpret_cast<uint32_t*>(lut);                    // [m][k]
   __shared__ float red[2 * NW * G];
 
   const int tid = threadIdx.x;
@@ -312,23 +321,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   // The MFMA wants, in lane (l16, q4), rows 4*q4..+3 of column l16 of each
   // 16-codeword block; lane (4a + u, q4) loads row 4*q4 + u, columns
   // 4a..4a+3 (8 contiguous bytes) and the quad transposes them.
+  // With 32-codeword steps lane (l16, q4) needs rows 8*q4 .. 8*q4+7 of column
+  // l16; lane (4a + u, q4) loads rows 8*q4 + u and 8*q4 + 4 + u, columns
+  // 4a..4a+3, and two quad transposes deliver the column.
   const int m_v = wave % M;
   const int jt = wave / M;
   const int qu = l16 & 3;
-  uint2 cvr[K / 16];
+  uint2 cvr[K / 32][2];
 #pragma unroll
-  for (int s = 0; s < K / 16; ++s) {
-    const __half* src = cvg + (int64_t(m_v) * K + s * 16 + 4 * q4 + qu) * DS + jt * 16 + 4 * (l16 >> 2);
-    cvr[s] = *reinterpret_cast<const uint2*>(src);
-  }
-
-  // zero the histogram
-  if constexpr (G >= 2) {
-    for (int i = tid; i < M * GP * K / 2; i += NTHR)
-      reinterpret_cast<uint4*>(hist64)[i] = make_uint4(0, 0, 0, 0);
-  } else {
-    for (int i = tid; i < M * K / 4; i += NTHR)
-      reinterpret_cast<uint4*>(hist32)[i] = make_uint4(0, 0, 0, 0);
+  for (int s = 0; s < K / 32; ++s) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const __half* src = cvg + (int64_t(m_v) * K + s * 32 + 8 * q4 + 4 * half + qu) * DS + jt * 16 +
+                          4 * (l16 >> 2);
+      cvr[s][half] = *reinterpret_cast<const uint2*>(src);
+    }
   }
 
   // ---- 1. lookup table on the matrix cores ----------------------------------
@@ -353,6 +360,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
     }
   }
   __syncthreads();
+
+  // B operands of the contraction (they depend only on the prefetched V
+  // codebook rows; done here, off the kernel's tail)
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  f16x8 cvb[K / 32];
+#pragma unroll
+  for (int st = 0; st < K / 32; ++st) {
+    const f16x4 b0 = quad_transpose(cvr[st][0].x, cvr[st][0].y, qu);
+    const f16x4 b1 = quad_transpose(cvr[st][1].x, cvr[st][1].y, qu);
+    cvb[st] = f16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  }
 
   // ---- 2. scores --------------------------------------------------------------
   float s[NT][G];
@@ -391,6 +409,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
     for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red[w * G + h]);
     m_c[h] = mx;
   }
+  // every table read is done (barrier above): clear the region for the histogram
+  for (int i = tid; i < HIST_WORDS / 4; i += NTHR)
+    reinterpret_cast<uint4*>(lut)[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
 
   // ---- 4. V histogram (fixed point, integer LDS atomics) -----------------------
   float l_thr[G];
@@ -414,7 +436,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
 #pragma unroll
           for (int pp = 0; pp < GP; ++pp) {
             const uint64_t w = __builtin_bit_cast(uint64_t, make_uint2(u[2 * pp], u[2 * pp + 1]));
-            atomicAdd(reinterpret_cast<unsigned long long*>(hist64 + (m * GP + pp) * K + code),
+            atomicAdd(reinterpret_cast<unsigned long long*>(hist64 + (m * GP + pp) * HROW + code),
                       (unsigned long long)w);
           }
         } else {
@@ -441,34 +463,55 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   }
 
   // ---- 5. contraction with the V codebook on the matrix cores ----------------
-  // 5b. A[h][k] = Hist[m_v][k][h] (lanes l16 >= G are zero), B[k][j] = Cv[m_v][k][j]
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  // A[i][k]: rows i < 8 carry the fp16 high part of Hist[m_v][k][i], rows
+  // i >= 8 the low part of Hist[m_v][k][i - 8] (zero for heads >= G), so one
+  // 16x16x32 instruction covers both parts; o[h] = C[h] + C[h + 8].
+  const int hh = l16 & 7;
+  const bool lo_row = l16 >= 8;
+  // all of this lane's bins first (one batch of LDS reads), then convert and
+  // multiply
+  uint32_t raw[K / 32][8];
 #pragma unroll
-  for (int st = 0; st < K / 16; ++st) {
-    const int k0 = st * 16 + 4 * q4;
-    float hv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (l16 < G) {
+  for (int st = 0; st < K / 32; ++st) {
+    const int k0 = st * 32 + 8 * q4;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) raw[st][t] = 0;
+    if (hh < G) {
       if constexpr (G >= 2) {
-        const uint64_t* src = hist64 + (m_v * GP + (l16 >> 1)) * K + k0;
-        const uint4 w01 = reinterpret_cast<const uint4*>(src)[0];
-        const uint4 w23 = reinterpret_cast<const uint4*>(src)[1];
-        const bool hi = (l16 & 1) != 0;
-        hv[0] = float(hi ? w01.y : w01.x) * kUnfix;
-        hv[1] = float(hi ? w01.w : w01.z) * kUnfix;
-        hv[2] = float(hi ? w23.y : w23.x) * kUnfix;
-        hv[3] = float(hi ? w23.w : w23.z) * kUnfix;
+        const uint4* src = reinterpret_cast<const uint4*>(hist64 + (m_v * GP + (hh >> 1)) * HROW + k0);
+        const bool odd = (hh & 1) != 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 w = src[v];   // bins k0+2v, k0+2v+1 as (even, odd) head pairs
+          raw[st][2 * v] = odd ? w.y : w.x;
+          raw[st][2 * v + 1] = odd ? w.w : w.z;
+        }
       } else {
-        const uint4 w = *reinterpret_cast<const uint4*>(hist32 + m_v * K + k0);
-        hv[0] = float(w.x) * kUnfix; hv[1] = float(w.y) * kUnfix;
-        hv[2] = float(w.z) * kUnfix; hv[3] = float(w.w) * kUnfix;
+        const uint4* src = reinterpret_cast<const uint4*>(hist32 + m_v * K + k0);
+        const uint4 w0 = src[0], w1 = src[1];
+        raw[st][0] = w0.x; raw[st][1] = w0.y; raw[st][2] = w0.z; raw[st][3] = w0.w;
+        raw[st][4] = w1.x; raw[st][5] = w1.y; raw[st][6] = w1.z; raw[st][7] = w1.w;
       }
     }
-    f16x4 ahi, alo;
+  }
+  f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) { _Float16 x, y; split_f16(hv[t], x, y); ahi[t] = x; alo[t] = y; }
-    const f16x4 cvb = quad_transpose(cvr[st].x, cvr[st].y, qu);
-    o = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, cvb, o, 0, 0, 0);
-    o = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, cvb, o, 0, 0, 0);
+  for (int st = 0; st < K / 32; ++st) {
+    f16x8 av;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float hv = float(raw[st][t]) * kUnfix;
+      const _Float16 hi = (_Float16)hv;
+      av[t] = lo_row ? (_Float16)(hv - (float)hi) : hi;
+    }
+    if (st & 1) ob = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, cvb[st], ob, 0, 0, 0);
+    else        oa = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, cvb[st], oa, 0, 0, 0);
+  }
+  f32x4 o;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float c = oa[r] + ob[r];
+    o[r] = c + __shfl_xor(c, 32, 64);   // rows 4*q4 + r and 4*q4 + r + 8 (lane + 32)
   }
 
   // ---- 6. write (m, l, o) or the normalised output ----------------------------

@@ -28,11 +28,15 @@ namespace pqattn {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+constexpr int kMaxEncodePlanes = 4;
+
+// Up to kMaxEncodePlanes tensors of one shape (e.g. a token's K and V), each
+// with its own codebook and code array; blockIdx.z picks the plane.
 struct EncodeArgs {
-  const __half* x;           // element (n, h, d) at x[n*sxv + h*sxh + d]
-  const __half* cb;          // [H][M][K][DS]
-  const int64_t* slots;      // [N] or null
-  uint8_t* codes;            // code (n, h, m) at codes[s*scs + h*sch + m]
+  const __half* x[kMaxEncodePlanes];       // element (n, h, d) at x[n*sxv + h*sxh + d]
+  const __half* cb[kMaxEncodePlanes];      // [H][M][K][DS]
+  uint8_t* codes[kMaxEncodePlanes];        // code (n, h, m) at codes[s*scs + h*sch + m]
+  const int64_t* slots;                    // [N] or null, shared by the planes
   int64_t N;
   int64_t codes_bytes;       // writes outside [0, codes_bytes) are skipped
   int64_t sxv, sxh, scs, sch;
@@ -69,11 +73,14 @@ __global__ __launch_bounds__(64 * M) void encode_kernel(EncodeArgs a) {
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
   const int h = blockIdx.y;
+  const int plane = blockIdx.z;
+  const __half* xp = a.x[plane];
+  uint8_t* codes = a.codes[plane];
   const int64_t n0 = int64_t(blockIdx.x) * NV;
   const int nv = int(min<int64_t>(NV, a.N - n0));
 
   // ---- codebook of (h, m) as MFMA B operands ------------------------------
-  const __half* cb = a.cb + (int64_t(h) * M + m) * K * DS;
+  const __half* cb = a.cb[plane] + (int64_t(h) * M + m) * K * DS;
   f16x4 bop[NCT][KS];
 #pragma unroll
   for (int nt = 0; nt < NCT; ++nt)
@@ -88,7 +95,7 @@ __global__ __launch_bounds__(64 * M) void encode_kernel(EncodeArgs a) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (v < nv) {
-        dst[s] = *reinterpret_cast<const f16x4*>(a.x + (n0 + v) * a.sxv + int64_t(h) * a.sxh +
+        dst[s] = *reinterpret_cast<const f16x4*>(xp + (n0 + v) * a.sxv + int64_t(h) * a.sxh +
                                                  m * DS + s * 16 + 4 * q4);
       } else {
         dst[s] = f16x4{0, 0, 0, 0};
@@ -162,7 +169,7 @@ __global__ __launch_bounds__(64 * M) void encode_kernel(EncodeArgs a) {
     if (s < 0 || (a.scs > 0 && s > a.codes_bytes / a.scs)) continue;
     const int64_t off = s * a.scs + int64_t(h) * a.sch;
     if (off < 0 || off + M > a.codes_bytes) continue;
-    uint8_t* dst = a.codes + off;
+    uint8_t* dst = codes + off;
     if constexpr (M == 4) {
       *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(cs + v * M);
     } else {

@@ -164,6 +164,15 @@ typedef struct pq_encode_desc {
 pq_status pq_encode(const pq_encode_desc* desc, const void* x, const void* codebook,
                     const int64_t* slots, uint8_t* codes, void* stream);
 
+/* pq_encode for n (1..4) tensors of the same shape and strides in one launch
+ * -- typically a new token's K and V, each with its own codebook and code
+ * array.  x, codebook and codes are host arrays of n device pointers; slots
+ * is shared.  Each plane i gives exactly what pq_encode(desc, x[i],
+ * codebook[i], slots, codes[i]) gives.  n outside 1..4 is PQ_ERR_SHAPE. */
+pq_status pq_encode_many(const pq_encode_desc* desc, int32_t n, const void* const* x,
+                         const void* const* codebook, const int64_t* slots,
+                         uint8_t* const* codes, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* pq_status_string(pq_status status);
 

@@ -160,6 +160,23 @@ def test_bad_encode_descriptor(lib, field, value, status):
     assert lib.pq_encode(ctypes.byref(d), FAKE, FAKE, None, FAKE, None) == status
 
 
+def test_encode_many_checks(lib):
+    arr = ctypes.c_void_p * 4
+    ok = arr(FAKE, FAKE, FAKE, FAKE)
+    d = _edesc(codes_bytes=79)                   # invalid: nothing can launch
+    assert lib.pq_encode_many(ctypes.byref(d), 2, ok, ok, None, ok, None) == 2
+    d = _edesc(n_sub=3)
+    for n in (0, 5, -1):
+        assert lib.pq_encode_many(ctypes.byref(d), n, ok, ok, None, ok, None) == 2
+    d = _edesc()
+    assert lib.pq_encode_many(ctypes.byref(d), 0, ok, ok, None, ok, None) == 2
+    assert lib.pq_encode_many(ctypes.byref(d), 5, ok, ok, None, ok, None) == 2
+    nul = arr(FAKE, None, FAKE, FAKE)
+    assert lib.pq_encode_many(ctypes.byref(d), 2, nul, ok, None, ok, None) == 1
+    mis = arr(FAKE, FAKE + 4, FAKE, FAKE)
+    assert lib.pq_encode_many(ctypes.byref(d), 2, ok, mis, None, ok, None) == 6
+
+
 def test_encode_pointer_checks(lib):
     d = _edesc(codes_bytes=79)        # also invalid: nothing can launch
     assert lib.pq_encode(ctypes.byref(d), None, FAKE, None, FAKE, None) in (1, 2)

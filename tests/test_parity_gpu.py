@@ -336,3 +336,30 @@ def test_encode_ties_lowest_index():
     got = codes.cpu().numpy()
     assert got[0, 1, 2] == 17 and got[1, 0, 0] == 3
     np.testing.assert_array_equal(got, oracle.encode(x, cb))
+
+
+def test_encode_many_matches_single_calls():
+    """K and V of a batch of new tokens in one launch (pq_encode_many) give
+    exactly what two pq_encode calls give, into a cache through slots."""
+    say("encode_many: K and V planes in one launch")
+    rng = np.random.default_rng(602)
+    B, H, L, M = 4, 8, 64, 8
+    kcb = gen.codebooks(rng, H, M, 256, 128 // M)
+    vcb = gen.codebooks(rng, H, M, 256, 128 // M)
+    xk, srck = gen.noisy_codewords(rng, kcb, B, 0.05)
+    xv, srcv = gen.noisy_codewords(rng, vcb, B, 0.05)
+    slots = np.arange(B, dtype=np.int64) * H * L + np.array([0, 5, 63, 17])
+    kc1, vc1 = dev(np.zeros((B, H, L, M), np.uint8)), dev(np.zeros((B, H, L, M), np.uint8))
+    kc2, vc2 = dev(np.zeros((B, H, L, M), np.uint8)), dev(np.zeros((B, H, L, M), np.uint8))
+    desc = pq.cache_encode_desc(B, B, H, L, n_sub=M)
+    s = dev(slots)
+    pq.pq_encode_many([dev(xk), dev(xv)], [dev(kcb), dev(vcb)], [kc1, vc1], slots=s, desc=desc)
+    pq.pq_encode(dev(xk), dev(kcb), kc2, slots=s, desc=desc)
+    pq.pq_encode(dev(xv), dev(vcb), vc2, slots=s, desc=desc)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kc1.cpu().numpy(), kc2.cpu().numpy())
+    np.testing.assert_array_equal(vc1.cpu().numpy(), vc2.cpu().numpy())
+    got_k = kc1.cpu().numpy()[np.arange(B), :, slots % L]
+    np.testing.assert_array_equal(got_k, oracle.encode(xk, kcb))
+    np.testing.assert_array_equal(got_k, srck)
+    np.testing.assert_array_equal(vc1.cpu().numpy()[np.arange(B), :, slots % L], srcv)
