@@ -87,7 +87,8 @@ pq_status launch_partials(const AttnPlan& p, const void* q, const uint8_t* kc, c
   a.qscale = p.scale * kLog2e;
   DecodeFn fn = pick_decode(p.G, p.M, p.T);
   if (!fn) return PQ_ERR_UNSUPPORTED;
-  return launch(reinterpret_cast<const void*>(fn), dim3(unsigned(p.blocks)), dim3(kDecodeThreads),
+  return launch(reinterpret_cast<const void*>(fn), dim3(unsigned(p.Hkv), unsigned(p.C), unsigned(p.B)),
+                dim3(kDecodeThreads),
                 &a, stream, start, stop);
 }
 

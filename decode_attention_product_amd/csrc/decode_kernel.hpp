@@ -4,10 +4,10 @@
 // the G query heads that share g (grouped-query attention, memory-wall
 // chapter section 1.4.3 (1)).  Steps:
 //
-//   0. Every operand the workgroup needs is requested from memory at once:
-//      its K and V codes, the MFMA operands of the K codebook and q (for the
-//      table) and of the V codebook (for the contraction), so HBM/L2 latency
-//      is paid once, not once per phase.
+//   0. The operands are requested in the order they are used: q and the K
+//      codebook (table build) before lens[b] is even waited for, then the
+//      chunk's K and V codes, and -- once the table is built -- the V
+//      codebook operands of the contraction.
 //   1. Lookup table LUT[m][k][h] = q_h[m] . Ck_g[m][k] -- the query's partial
 //      dot product with every K codeword (AQPIM page, section 4.1; kept on
 //      chip as the page's GPU note suggests) -- computed as M small
@@ -115,12 +115,27 @@ template <> struct TokenCodes<4> {
   uint32_t w = 0;
   __device__ __forceinline__ void load(const uint8_t* p) { w = *reinterpret_cast<const uint32_t*>(p); }
   __device__ __forceinline__ int get(int m) const { return (w >> (8 * m)) & 0xff; }
+  // the codes with byte j holding segment (j + r) % 4
+  __device__ __forceinline__ TokenCodes rotated(int r) const {
+    TokenCodes o;
+    o.w = __builtin_amdgcn_alignbit(w, w, 8 * r);
+    return o;
+  }
 };
 template <> struct TokenCodes<8> {
   uint2 w = {0, 0};
   __device__ __forceinline__ void load(const uint8_t* p) { w = *reinterpret_cast<const uint2*>(p); }
   __device__ __forceinline__ int get(int m) const {
     return ((m < 4 ? w.x : w.y) >> (8 * (m & 3))) & 0xff;
+  }
+  // the codes with byte j holding segment (j + r) % 8: a 64-bit rotation
+  __device__ __forceinline__ TokenCodes rotated(int r) const {
+    const uint32_t lo = (r & 4) ? w.y : w.x;
+    const uint32_t hi = (r & 4) ? w.x : w.y;
+    const uint32_t sh = 8 * (r & 3);
+    TokenCodes o;
+    o.w = make_uint2(__builtin_amdgcn_alignbit(hi, lo, sh), __builtin_amdgcn_alignbit(lo, hi, sh));
+    return o;
   }
 };
 
@@ -230,18 +245,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   constexpr float kFix = float(1u << 31) / float(NT * NTHR);
   constexpr float kUnfix = float(NT * NTHR) / float(1u << 31);
 
-  // The table is read only while scoring and the histogram is written only
-  // after the scores sit in registers, so both live in one LDS region (half
-  // the LDS of separate arrays: two workgroups fit on a CU).
-  // Histogram rows [m][pair] are padded by HPAD words so that the rows a
-  // wave reads side by side in the contraction start on different banks.
-  constexpr int HPAD = 2;
-  constexpr int HROW = K + HPAD;                                           // u64 per row
+  // Table and histogram live in separate LDS regions, so the histogram can be
+  // cleared while the workgroup still waits for its operands.
+  // For G >= 2 the histogram is [k][R] 64-bit words, row r = m * GP + pair
+  // holding the bins of two heads: every row of a codeword sits on its own
+  // pair of banks whatever the codeword, so a wave whose lanes update
+  // different rows never conflicts (each lane walks the rows in a
+  // lane-rotated order).  For G = 1 it is [m][k] 32-bit words.
+  constexpr int R = M * GP;                                                // rows per codeword
   constexpr int LUT_WORDS = M * K * G;
-  constexpr int HIST_WORDS = G >= 2 ? M * GP * HROW * 2 : M * K;
-  __shared__ __align__(16) float lut[LUT_WORDS > HIST_WORDS ? LUT_WORDS : HIST_WORDS];
-  uint64_t* hist64 = reinterpret_cast<uint64_t*>(lut);                    // [m][pair][HROW]
-  uint32_t* hist32 = reinterpret_cast<uint32_t*>(lut);                    // [m][k]
+  constexpr int HIST_WORDS = G >= 2 ? K * R * 2 : M * K;
+  __shared__ __align__(16) float lut[LUT_WORDS];
+  __shared__ __align__(16) uint32_t hist[HIST_WORDS];
+  uint32_t* hist32 = hist;                                                 // [m][k] (G = 1)
+  char* hist_bytes = reinterpret_cast<char*>(hist);                        // [k][R] u64 (G >= 2)
   __shared__ float red[2 * NW * G];
 
   const int tid = threadIdx.x;
@@ -250,53 +267,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
 
-  // XCD-aware order: consecutive workgroups go to different XCDs, so the KV
-  // head is the fastest index; with Hkv a multiple of 8 every chunk of one
-  // head lands on the same XCD and shares its L2 copy of the codebooks.
-  const int64_t id = blockIdx.x;
-  const int g = int(id % a.Hkv);
-  const int64_t rest = id / a.Hkv;
-  const int c = int(rest % a.C);
-  const int b = int(rest / a.C);
-
-  int len = a.lens[b];
-  len = len < 0 ? 0 : (len > a.Lmax ? a.Lmax : len);
+  // Grid (Hkv, C, B), dispatched x fastest: consecutive workgroups go to
+  // different XCDs, so with Hkv a multiple of 8 every chunk of one KV head
+  // lands on the same XCD and shares its L2 copy of the codebooks.
+  const int g = blockIdx.x;
+  const int c = blockIdx.y;
+  const int b = blockIdx.z;
   const int t_begin = c * a.T;
-  const int t_end = min(t_begin + a.T, len);
   const int64_t row0 = int64_t(b) * a.Hq + int64_t(g) * G;   // first query row
 
-  if (t_begin >= t_end) {   // empty chunk (uniform over the workgroup)
-    for (int i = tid; i < G * D; i += NTHR) {
-      const int h = i / D, d = i % D;
-      if (a.out != nullptr) {
-        a.out[(row0 + h) * D + d] = 0.0f;
-      } else {
-        a.part_o[((row0 + h) * a.C + c) * D + d] = 0.0f;
-        if (d == 0) {
-          a.part_m[(row0 + h) * a.C + c] = -INFINITY;
-          a.part_l[(row0 + h) * a.C + c] = 0.0f;
-        }
-      }
-    }
-    return;
-  }
-
-  // ---- 0. requests: codes, table operands, contraction operands ------------
-  const int64_t bg = int64_t(b) * a.Hkv + g;
-  const uint8_t* kc = a.k_codes + bg * a.Lmax * M;
-  const uint8_t* vc = a.v_codes + bg * a.Lmax * M;
-  TokenCodes<M> kcode[NT], vcode[NT];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const int t = t_begin + i * NTHR + tid;
-    if (t < t_end) {
-      kcode[i].load(kc + int64_t(t) * M);
-      vcode[i].load(vc + int64_t(t) * M);
-    }
-  }
-
+  // ---- 0. requests --------------------------------------------------------------
+  // What does not depend on lens[b] goes out before its value is waited for:
+  // the query rows and the K codebook operands of the table build.
+  int len = a.lens[b];
   const __half* ckg = a.k_cb + int64_t(g) * M * K * DS;
-  const __half* cvg = a.v_cb + int64_t(g) * M * K * DS;
   // table build: wave w owns segment m_l = w % M and codeword tiles
   // nt = w / M + (NW / M) * i
   const int m_l = wave % M;
@@ -317,26 +301,42 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
 #pragma unroll
     for (int s = 0; s < KSTEP_Q; ++s) ckb[i][s] = *reinterpret_cast<const f16x4*>(row + s * 16);
   }
-  // contraction: wave w owns segment m_v and 16 output columns jt*16..+15.
-  // The MFMA wants, in lane (l16, q4), rows 4*q4..+3 of column l16 of each
-  // 16-codeword block; lane (4a + u, q4) loads row 4*q4 + u, columns
-  // 4a..4a+3 (8 contiguous bytes) and the quad transposes them.
-  // With 32-codeword steps lane (l16, q4) needs rows 8*q4 .. 8*q4+7 of column
-  // l16; lane (4a + u, q4) loads rows 8*q4 + u and 8*q4 + 4 + u, columns
-  // 4a..4a+3, and two quad transposes deliver the column.
-  const int m_v = wave % M;
-  const int jt = wave / M;
-  const int qu = l16 & 3;
-  uint2 cvr[K / 32][2];
+
+  len = len < 0 ? 0 : (len > a.Lmax ? a.Lmax : len);
+  const int t_end = min(t_begin + a.T, len);
+  if (t_begin >= t_end) {   // empty chunk (uniform over the workgroup)
+    for (int i = tid; i < G * D; i += NTHR) {
+      const int h = i / D, d = i % D;
+      if (a.out != nullptr) {
+        a.out[(row0 + h) * D + d] = 0.0f;
+      } else {
+        a.part_o[((row0 + h) * a.C + c) * D + d] = 0.0f;
+        if (d == 0) {
+          a.part_m[(row0 + h) * a.C + c] = -INFINITY;
+          a.part_l[(row0 + h) * a.C + c] = 0.0f;
+        }
+      }
+    }
+    return;
+  }
+
+  // the chunk's K and V codes (only tokens below lens[b] are read)
+  const int64_t bg = int64_t(b) * a.Hkv + g;
+  const uint8_t* kc = a.k_codes + bg * a.Lmax * M;
+  const uint8_t* vc = a.v_codes + bg * a.Lmax * M;
+  TokenCodes<M> kcode[NT], vcode[NT];
 #pragma unroll
-  for (int s = 0; s < K / 32; ++s) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const __half* src = cvg + (int64_t(m_v) * K + s * 32 + 8 * q4 + 4 * half + qu) * DS + jt * 16 +
-                          4 * (l16 >> 2);
-      cvr[s][half] = *reinterpret_cast<const uint2*>(src);
+  for (int i = 0; i < NT; ++i) {
+    const int t = t_begin + i * NTHR + tid;
+    if (t < t_end) {
+      kcode[i].load(kc + int64_t(t) * M);
+      vcode[i].load(vc + int64_t(t) * M);
     }
   }
+
+  // the histogram is cleared while the operands are in flight
+  for (int i = tid; i < HIST_WORDS / 4; i += NTHR)
+    reinterpret_cast<uint4*>(hist)[i] = make_uint4(0, 0, 0, 0);
 
   // ---- 1. lookup table on the matrix cores ----------------------------------
 #pragma unroll
@@ -361,15 +361,26 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   }
   __syncthreads();
 
-  // B operands of the contraction (they depend only on the prefetched V
-  // codebook rows; done here, off the kernel's tail)
-  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-  f16x8 cvb[K / 32];
+  // V codebook operands of the contraction, requested once the table is
+  // built (earlier they would queue ahead of the table operands).
+  // Wave w owns segment m_v and 16 output columns jt*16..+15.  With
+  // 32-codeword steps lane (l16, q4) needs rows 8*q4 .. 8*q4+7 of column l16
+  // of each block; lane (4a + u, q4) loads rows 8*q4 + u and 8*q4 + 4 + u,
+  // columns 4a..4a+3 (8 contiguous bytes each), and two quad transposes
+  // deliver the column.
+  const __half* cvg = a.v_cb + int64_t(g) * M * K * DS;
+  const int m_v = wave % M;
+  const int jt = wave / M;
+  const int qu = l16 & 3;
+  uint2 cvr[K / 32][2];
 #pragma unroll
-  for (int st = 0; st < K / 32; ++st) {
-    const f16x4 b0 = quad_transpose(cvr[st][0].x, cvr[st][0].y, qu);
-    const f16x4 b1 = quad_transpose(cvr[st][1].x, cvr[st][1].y, qu);
-    cvb[st] = f16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  for (int s = 0; s < K / 32; ++s) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const __half* src = cvg + (int64_t(m_v) * K + s * 32 + 8 * q4 + 4 * half + qu) * DS + jt * 16 +
+                          4 * (l16 >> 2);
+      cvr[s][half] = *reinterpret_cast<const uint2*>(src);
+    }
   }
 
   // ---- 2. scores --------------------------------------------------------------
@@ -409,12 +420,26 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
     for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red[w * G + h]);
     m_c[h] = mx;
   }
-  // every table read is done (barrier above): clear the region for the histogram
-  for (int i = tid; i < HIST_WORDS / 4; i += NTHR)
-    reinterpret_cast<uint4*>(lut)[i] = make_uint4(0, 0, 0, 0);
-  __syncthreads();
 
   // ---- 4. V histogram (fixed point, integer LDS atomics) -----------------------
+  // Lane rotation (G >= 2): at step (jm, jp) a lane updates segment
+  // (jm + om) % M, om = lane % M, and head pair jp, or pair jp XOR GP/2 on
+  // lanes whose bit log2(M) is set.  The LDS serves 16 lanes of a 64-bit
+  // atomic together and is conflict-free when they hit 16 different rows:
+  // here 2M of them (all 16 for M = 8).  Codes are rotated once per token
+  // (one 64-bit funnel shift), pairs by one swap; the pair's row offset then
+  // splits into a per-lane base (below) and an immediate.
+  const int om = lane & (M - 1);
+  const bool swap_pairs = GP >= 2 && ((lane / M) & 1) != 0;
+  constexpr int GH = GP >= 2 ? GP / 2 : 1;   // pairs per half
+  uint32_t row_lo[M], row_hi[M];   // byte offsets of the pair halves [0, GH) and [GH, GP)
+#pragma unroll
+  for (int jm = 0; jm < M; ++jm) {
+    const uint32_t rm = uint32_t(((jm + om) & (M - 1)) * GP * 8);
+    row_lo[jm] = rm + (swap_pairs ? GH * 8 : 0);
+    row_hi[jm] = rm + (swap_pairs ? 0 : GH * 8);
+  }
+
   float l_thr[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) l_thr[h] = 0.0f;
@@ -429,22 +454,52 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
         l_thr[h] += p;
         u[h] = uint32_t(fmaf(p, kFix, 0.5f));   // p * kFix <= 2^31 / Tmax, rounded
       }
+      if constexpr (G >= 2) {
+        uint64_t pv[GP];
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const int code = vcode[i].get(m);
-        if constexpr (G >= 2) {
+        for (int pp = 0; pp < GP; ++pp)
+          pv[pp] = __builtin_bit_cast(uint64_t, make_uint2(u[2 * pp], u[2 * pp + 1]));
+        if constexpr (GP >= 2) {   // pv[j] <- pv[(j + GP/2) % GP] on swapping lanes
 #pragma unroll
-          for (int pp = 0; pp < GP; ++pp) {
-            const uint64_t w = __builtin_bit_cast(uint64_t, make_uint2(u[2 * pp], u[2 * pp + 1]));
-            atomicAdd(reinterpret_cast<unsigned long long*>(hist64 + (m * GP + pp) * HROW + code),
-                      (unsigned long long)w);
+          for (int j = 0; j < GP / 2; ++j) {
+            const uint64_t x = pv[j], y = pv[j + GP / 2];
+            pv[j] = swap_pairs ? y : x;
+            pv[j + GP / 2] = swap_pairs ? x : y;
           }
-        } else {
-          atomicAdd(hist32 + m * K + code, u[0]);
         }
+        const TokenCodes<M> rc = vcode[i].rotated(om);
+#pragma unroll
+        for (int jm = 0; jm < M; ++jm) {
+          const uint32_t code_off = uint32_t(rc.get(jm)) * (R * 8);
+          char* lo = hist_bytes + (code_off + row_lo[jm]);
+#pragma unroll
+          for (int jp = 0; jp < GH; ++jp)
+            atomicAdd(reinterpret_cast<unsigned long long*>(lo + jp * 8), (unsigned long long)pv[jp]);
+          if constexpr (GP >= 2) {
+            char* hi = hist_bytes + (code_off + row_hi[jm]);
+#pragma unroll
+            for (int jp = 0; jp < GH; ++jp)
+              atomicAdd(reinterpret_cast<unsigned long long*>(hi + jp * 8),
+                        (unsigned long long)pv[GH + jp]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < M; ++m) atomicAdd(hist32 + m * K + vcode[i].get(m), u[0]);
       }
     }
   }
+  // B operands of the contraction (the prefetched V codebook rows, put
+  // in MFMA order while the LDS drains the atomics)
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  f16x8 cvb[K / 32];
+#pragma unroll
+  for (int st = 0; st < K / 32; ++st) {
+    const f16x4 b0 = quad_transpose(cvr[st][0].x, cvr[st][0].y, qu);
+    const f16x4 b1 = quad_transpose(cvr[st][1].x, cvr[st][1].y, qu);
+    cvb[st] = f16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  }
+
   wave_sum_n<G>(l_thr);
   if (lane < G) {
     float mine = l_thr[0];
@@ -466,44 +521,53 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   // A[i][k]: rows i < 8 carry the fp16 high part of Hist[m_v][k][i], rows
   // i >= 8 the low part of Hist[m_v][k][i - 8] (zero for heads >= G), so one
   // 16x16x32 instruction covers both parts; o[h] = C[h] + C[h + 8].
+  // Lane (i, q4) needs bins 8*q4 .. 8*q4+7 of a 32-bin step.  The lanes i and
+  // i + 8 (same head, hi and lo) each convert half of them -- bins +0..3 on
+  // the hi lane, +4..7 on the lo lane -- into both parts, and swap the part
+  // the other one needs with one DPP move per word.
   const int hh = l16 & 7;
   const bool lo_row = l16 >= 8;
-  // all of this lane's bins first (one batch of LDS reads), then convert and
-  // multiply
-  uint32_t raw[K / 32][8];
+  const int kh = lo_row ? 4 : 0;
+  uint32_t raw[K / 32][4];
 #pragma unroll
   for (int st = 0; st < K / 32; ++st) {
-    const int k0 = st * 32 + 8 * q4;
+    const int k0 = st * 32 + 8 * q4 + kh;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) raw[st][t] = 0;
+    for (int v = 0; v < 4; ++v) raw[st][v] = 0;
     if (hh < G) {
       if constexpr (G >= 2) {
-        const uint4* src = reinterpret_cast<const uint4*>(hist64 + (m_v * GP + (hh >> 1)) * HROW + k0);
-        const bool odd = (hh & 1) != 0;
+        const char* src = hist_bytes + (k0 * R + m_v * GP + (hh >> 1)) * 8 + (hh & 1) * 4;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint4 w = src[v];   // bins k0+2v, k0+2v+1 as (even, odd) head pairs
-          raw[st][2 * v] = odd ? w.y : w.x;
-          raw[st][2 * v + 1] = odd ? w.w : w.z;
-        }
+        for (int v = 0; v < 4; ++v) raw[st][v] = *reinterpret_cast<const uint32_t*>(src + v * R * 8);
       } else {
-        const uint4* src = reinterpret_cast<const uint4*>(hist32 + m_v * K + k0);
-        const uint4 w0 = src[0], w1 = src[1];
-        raw[st][0] = w0.x; raw[st][1] = w0.y; raw[st][2] = w0.z; raw[st][3] = w0.w;
-        raw[st][4] = w1.x; raw[st][5] = w1.y; raw[st][6] = w1.z; raw[st][7] = w1.w;
+        const uint4 w = *reinterpret_cast<const uint4*>(hist32 + m_v * K + k0);
+        raw[st][0] = w.x; raw[st][1] = w.y; raw[st][2] = w.z; raw[st][3] = w.w;
       }
     }
   }
   f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int st = 0; st < K / 32; ++st) {
-    f16x8 av;
+    uint32_t hw[2], lw[2];   // packed fp16 pairs: high parts, low parts
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float hv = float(raw[st][t]) * kUnfix;
-      const _Float16 hi = (_Float16)hv;
-      av[t] = lo_row ? (_Float16)(hv - (float)hi) : hi;
+    for (int v = 0; v < 2; ++v) {
+      const float f0 = float(raw[st][2 * v]) * kUnfix;
+      const float f1 = float(raw[st][2 * v + 1]) * kUnfix;
+      const _Float16 h0 = (_Float16)f0, h1 = (_Float16)f1;
+      const _Float16 e0 = (_Float16)(f0 - (float)h0), e1 = (_Float16)(f1 - (float)h1);
+      hw[v] = uint32_t(__builtin_bit_cast(uint16_t, h0)) | (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
+      lw[v] = uint32_t(__builtin_bit_cast(uint16_t, e0)) | (uint32_t(__builtin_bit_cast(uint16_t, e1)) << 16);
     }
+    // the hi lane sends its low parts, the lo lane its high parts; row_ror:8
+    // delivers lane i+8's word to lane i and lane i's to lane i+8
+    const uint32_t r0 = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_row ? hw[0] : lw[0]), kDppRor8, 0xf, 0xf, false));
+    const uint32_t r1 = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_row ? hw[1] : lw[1]), kDppRor8, 0xf, 0xf, false));
+    uint4 aw;
+    aw.x = lo_row ? r0 : hw[0];
+    aw.y = lo_row ? r1 : hw[1];
+    aw.z = lo_row ? lw[0] : r0;
+    aw.w = lo_row ? lw[1] : r1;
+    const f16x8 av = __builtin_bit_cast(f16x8, aw);
     if (st & 1) ob = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, cvb[st], ob, 0, 0, 0);
     else        oa = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, cvb[st], oa, 0, 0, 0);
   }

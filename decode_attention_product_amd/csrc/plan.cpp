@@ -9,6 +9,7 @@ namespace pqattn {
 namespace {
 
 constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxGridYZ = 65535;
 constexpr int kTargetBlocks = 256;     // one score workgroup per CU (256 CUs)
 constexpr int kChunkGranule = 512;     // one token per thread of a 512-thread workgroup
 
@@ -62,6 +63,8 @@ pq_status plan_attn(const pq_attn_desc* d, AttnPlan* p) {
   p->rows = int64_t(p->B) * p->Hq;
   p->blocks = int64_t(p->B) * p->Hkv * p->C;
   if (p->blocks > kMaxBlocks || p->rows > kMaxBlocks) return PQ_ERR_UNSUPPORTED;
+  // score-kernel grid (Hkv, C, B): the y and z extents are 16-bit
+  if (p->C > kMaxGridYZ || p->B > kMaxGridYZ) return PQ_ERR_UNSUPPORTED;
 
   // workspace: m and l [rows][C], o [rows][C][D], each 256-byte aligned
   const size_t n_stat = size_t(p->rows) * size_t(p->C);

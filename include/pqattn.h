@@ -27,8 +27,9 @@
  *  - Two calls that run at the same time need their own workspaces.
  *  - Supported shapes: head_dim = 128, n_codes = 256, n_sub in {4, 8} (so
  *    segments of 32 or 16 dims), n_q_heads / n_kv_heads in {1, 2, 4, 8},
- *    max_len a multiple of 16; q, code and codebook pointers 16-byte
- *    aligned.  Other valid shapes return PQ_ERR_UNSUPPORTED.
+ *    max_len a multiple of 16, batch and the chunk count C each at most
+ *    65535; q, code and codebook pointers 16-byte aligned.  Other valid
+ *    shapes return PQ_ERR_UNSUPPORTED.
  */
 #ifndef PQATTN_H
 #define PQATTN_H

@@ -58,6 +58,12 @@ int main() {
   d = base(); d.n_q_heads = 8 * 16;             EXPECT(plan_attn(&d, &p) == PQ_ERR_UNSUPPORTED);
   d = base(); d.batch = std::numeric_limits<int32_t>::max(); d.chunk = 1;
   EXPECT(plan_attn(&d, &p) == PQ_ERR_UNSUPPORTED);        // too many workgroups
+  d = base(); d.batch = 65535; d.n_q_heads = 8; d.n_kv_heads = 1;
+  EXPECT(plan_attn(&d, &p) == PQ_OK);                     // largest grid z extent
+  d.batch = 65536;                              EXPECT(plan_attn(&d, &p) == PQ_ERR_UNSUPPORTED);
+  d = base(); d.batch = 1; d.max_len = 16 * 65535; d.chunk = 16;
+  EXPECT(plan_attn(&d, &p) == PQ_OK && p.C == 65535);     // largest grid y extent
+  d.max_len = 16 * 65536;                       EXPECT(plan_attn(&d, &p) == PQ_ERR_UNSUPPORTED);
   EXPECT(plan_attn(nullptr, &p) == PQ_ERR_NULL);
 
   // chunk pick: small problems still get one chunk per 256 tokens at most
