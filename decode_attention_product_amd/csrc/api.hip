@@ -14,7 +14,7 @@
 namespace pqattn {
 namespace {
 
-static_assert(kMaxChunk == 8 * kDecodeThreads, "a chunk is at most 8 token slots per thread");
+static_assert(kMaxChunk == 4 * kDecodeThreads, "a chunk is at most 4 token slots per thread");
 
 constexpr int kReduceThreads = 128;
 constexpr int kEncodeVectors = 256;   // vectors per encode workgroup (one wave per segment)
@@ -26,7 +26,6 @@ DecodeFn pick_nt(int T) {
   if (T <= kDecodeThreads) return &decode_partials_kernel<G, M, 1>;
   if (T <= 2 * kDecodeThreads) return &decode_partials_kernel<G, M, 2>;
   if (T <= 4 * kDecodeThreads) return &decode_partials_kernel<G, M, 4>;
-  if (T <= 8 * kDecodeThreads) return &decode_partials_kernel<G, M, 8>;
   return nullptr;
 }
 

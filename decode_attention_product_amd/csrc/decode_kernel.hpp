@@ -39,7 +39,7 @@ namespace pqattn {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kDecodeThreads = 512;
+constexpr int kDecodeThreads = 1024;
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -109,6 +109,16 @@ __device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
   }
 }
 
+// Float <-> int keys whose signed order is the float order (finite values
+// and infinities), so an LDS integer max can reduce float maxima.
+__device__ __forceinline__ int float_key(float f) {
+  const int b = __builtin_bit_cast(int, f);
+  return b >= 0 ? b : b ^ 0x7fffffff;
+}
+__device__ __forceinline__ float key_float(int k) {
+  return __builtin_bit_cast(float, k >= 0 ? k : k ^ 0x7fffffff);
+}
+
 // Code bytes of one token: M = 4 -> one dword, M = 8 -> two dwords.
 template <int M> struct TokenCodes;
 template <> struct TokenCodes<4> {
@@ -154,20 +164,30 @@ __device__ __forceinline__ int lut_index(int m, int k, int quad) {
 template <int G, int M, int K, typename Codes>
 __device__ __forceinline__ void token_scores(const float* lut, const Codes& code, float* s) {
   if constexpr (G >= 4) {
-    float4 e[M][G / 4];
+    // in groups of 4 segments: 4 * G/4 reads in flight, half the registers
+    // of issuing all M at once
+    float4 acc[G / 4];
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+    for (int m0 = 0; m0 < M; m0 += 4) {
+      float4 e[4][G / 4];
 #pragma unroll
-      for (int v = 0; v < G / 4; ++v)
-        e[m][v] = *reinterpret_cast<const float4*>(lut + lut_index<G, K>(m, code.get(m), v));
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int v = 0; v < G / 4; ++v)
+          e[m][v] = *reinterpret_cast<const float4*>(lut + lut_index<G, K>(m0 + m, code.get(m0 + m), v));
+#pragma unroll
+      for (int v = 0; v < G / 4; ++v) {
+        if (m0 == 0) acc[v] = e[0][v];
+        else { acc[v].x += e[0][v].x; acc[v].y += e[0][v].y; acc[v].z += e[0][v].z; acc[v].w += e[0][v].w; }
+#pragma unroll
+        for (int m = 1; m < 4; ++m) {
+          acc[v].x += e[m][v].x; acc[v].y += e[m][v].y; acc[v].z += e[m][v].z; acc[v].w += e[m][v].w;
+        }
+      }
+    }
 #pragma unroll
     for (int v = 0; v < G / 4; ++v) {
-      float4 acc = e[0][v];
-#pragma unroll
-      for (int m = 1; m < M; ++m) {
-        acc.x += e[m][v].x; acc.y += e[m][v].y; acc.z += e[m][v].z; acc.w += e[m][v].w;
-      }
-      s[4 * v + 0] = acc.x; s[4 * v + 1] = acc.y; s[4 * v + 2] = acc.z; s[4 * v + 3] = acc.w;
+      s[4 * v + 0] = acc[v].x; s[4 * v + 1] = acc[v].y; s[4 * v + 2] = acc[v].z; s[4 * v + 3] = acc[v].w;
     }
   } else if constexpr (G == 2) {
     float2 e[M];
@@ -240,7 +260,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   constexpr int KSTEP_Q = DS / 16;            // MFMA k-steps of the table build
   constexpr int LUT_JOBS = (M * 16) / NW;     // (m, 16-codeword tile) jobs per wave
   constexpr int GP = G >= 2 ? G / 2 : 1;      // 64-bit histogram words per (m, k)
-  static_assert(NW == 8 && (M * DS / 16) == 8, "one contraction job per wave");
+  constexpr int NTILE = M * DS / 16;         // 16-column output tiles of the contraction
+  constexpr int KSPLIT = NW / NTILE;          // waves sharing a tile, each a slice of the bins
+  constexpr int KSL = K / KSPLIT;             // bins per slice
+  static_assert(NTILE == 8 && KSPLIT == 2, "two contraction waves per output tile");
   // fixed point: a bin collects at most NT*NTHR tokens of value <= 1
   constexpr float kFix = float(1u << 31) / float(NT * NTHR);
   constexpr float kUnfix = float(NT * NTHR) / float(1u << 31);
@@ -259,7 +282,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   __shared__ __align__(16) uint32_t hist[HIST_WORDS];
   uint32_t* hist32 = hist;                                                 // [m][k] (G = 1)
   char* hist_bytes = reinterpret_cast<char*>(hist);                        // [k][R] u64 (G >= 2)
-  __shared__ float red[2 * NW * G];
+  __shared__ float lsum[NW * G];              // per-wave partial sums of p
+  __shared__ __align__(16) int mkey[G];       // chunk max per head, as float_key
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -337,6 +361,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   // the histogram is cleared while the operands are in flight
   for (int i = tid; i < HIST_WORDS / 4; i += NTHR)
     reinterpret_cast<uint4*>(hist)[i] = make_uint4(0, 0, 0, 0);
+  if (tid < G) mkey[tid] = float_key(-INFINITY);
 
   // ---- 1. lookup table on the matrix cores ----------------------------------
 #pragma unroll
@@ -361,28 +386,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   }
   __syncthreads();
 
-  // V codebook operands of the contraction, requested once the table is
-  // built (earlier they would queue ahead of the table operands).
-  // Wave w owns segment m_v and 16 output columns jt*16..+15.  With
-  // 32-codeword steps lane (l16, q4) needs rows 8*q4 .. 8*q4+7 of column l16
-  // of each block; lane (4a + u, q4) loads rows 8*q4 + u and 8*q4 + 4 + u,
-  // columns 4a..4a+3 (8 contiguous bytes each), and two quad transposes
-  // deliver the column.
-  const __half* cvg = a.v_cb + int64_t(g) * M * K * DS;
-  const int m_v = wave % M;
-  const int jt = wave / M;
-  const int qu = l16 & 3;
-  uint2 cvr[K / 32][2];
-#pragma unroll
-  for (int s = 0; s < K / 32; ++s) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const __half* src = cvg + (int64_t(m_v) * K + s * 32 + 8 * q4 + 4 * half + qu) * DS + jt * 16 +
-                          4 * (l16 >> 2);
-      cvr[s][half] = *reinterpret_cast<const uint2*>(src);
-    }
-  }
-
   // ---- 2. scores --------------------------------------------------------------
   float s[NT][G];
 #pragma unroll
@@ -406,19 +409,39 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
     m_c[h] = mx;
   }
   wave_max_n<G>(m_c);
-  if (lane < G) {
+  if (lane < G) {   // one integer LDS max per (wave, head)
     float mine = m_c[0];
 #pragma unroll
     for (int h = 1; h < G; ++h) mine = (lane == h) ? m_c[h] : mine;
-    red[wave * G + lane] = mine;
+    atomicMax(&mkey[lane], float_key(mine));
   }
   __syncthreads();
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mx = red[h];
+  for (int h = 0; h < G; ++h) m_c[h] = key_float(mkey[h]);
+
+  // V codebook operands of the contraction, requested once the scores are
+  // in registers (earlier they would queue ahead of the table operands and
+  // hold registers through the gathers).
+  // Wave w owns segment m_v and 16 output columns jt*16..+15.  With
+  // 32-codeword steps lane (l16, q4) needs rows 8*q4 .. 8*q4+7 of column l16
+  // of each block; lane (4a + u, q4) loads rows 8*q4 + u and 8*q4 + 4 + u,
+  // columns 4a..4a+3 (8 contiguous bytes each), and two quad transposes
+  // deliver the column.
+  const __half* cvg = a.v_cb + int64_t(g) * M * K * DS;
+  const int tile = wave % NTILE;
+  const int ksl = wave / NTILE;               // bins [ksl * KSL, (ksl + 1) * KSL)
+  const int m_v = tile % M;
+  const int jt = tile / M;
+  const int qu = l16 & 3;
+  uint2 cvr[KSL / 32][2];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, red[w * G + h]);
-    m_c[h] = mx;
+  for (int s = 0; s < KSL / 32; ++s) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const __half* src = cvg + (int64_t(m_v) * K + ksl * KSL + s * 32 + 8 * q4 + 4 * half + qu) * DS +
+                          jt * 16 + 4 * (l16 >> 2);
+      cvr[s][half] = *reinterpret_cast<const uint2*>(src);
+    }
   }
 
   // ---- 4. V histogram (fixed point, integer LDS atomics) -----------------------
@@ -432,13 +455,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   const int om = lane & (M - 1);
   const bool swap_pairs = GP >= 2 && ((lane / M) & 1) != 0;
   constexpr int GH = GP >= 2 ? GP / 2 : 1;   // pairs per half
-  uint32_t row_lo[M], row_hi[M];   // byte offsets of the pair halves [0, GH) and [GH, GP)
+  // byte offset of the pair half [0, GH) of rotated segment jm; the half
+  // [GH, GP) is at row_lo ^ GH*8 (rows of a segment start 2*GH*8-aligned)
+  uint32_t row_lo[M];
 #pragma unroll
-  for (int jm = 0; jm < M; ++jm) {
-    const uint32_t rm = uint32_t(((jm + om) & (M - 1)) * GP * 8);
-    row_lo[jm] = rm + (swap_pairs ? GH * 8 : 0);
-    row_hi[jm] = rm + (swap_pairs ? 0 : GH * 8);
-  }
+  for (int jm = 0; jm < M; ++jm)
+    row_lo[jm] = uint32_t(((jm + om) & (M - 1)) * GP * 8) + (swap_pairs ? GH * 8 : 0);
 
   float l_thr[G];
 #pragma unroll
@@ -476,7 +498,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
           for (int jp = 0; jp < GH; ++jp)
             atomicAdd(reinterpret_cast<unsigned long long*>(lo + jp * 8), (unsigned long long)pv[jp]);
           if constexpr (GP >= 2) {
-            char* hi = hist_bytes + (code_off + row_hi[jm]);
+            char* hi = hist_bytes + (code_off + (row_lo[jm] ^ uint32_t(GH * 8)));
 #pragma unroll
             for (int jp = 0; jp < GH; ++jp)
               atomicAdd(reinterpret_cast<unsigned long long*>(hi + jp * 8),
@@ -492,9 +514,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   // B operands of the contraction (the prefetched V codebook rows, put
   // in MFMA order while the LDS drains the atomics)
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-  f16x8 cvb[K / 32];
+  f16x8 cvb[KSL / 32];
 #pragma unroll
-  for (int st = 0; st < K / 32; ++st) {
+  for (int st = 0; st < KSL / 32; ++st) {
     const f16x4 b0 = quad_transpose(cvr[st][0].x, cvr[st][0].y, qu);
     const f16x4 b1 = quad_transpose(cvr[st][1].x, cvr[st][1].y, qu);
     cvb[st] = f16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
@@ -505,17 +527,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
     float mine = l_thr[0];
 #pragma unroll
     for (int h = 1; h < G; ++h) mine = (lane == h) ? l_thr[h] : mine;
-    red[NW * G + wave * G + lane] = mine;
+    lsum[wave * G + lane] = mine;
   }
   __syncthreads();   // histogram and partial sums complete
-  float l_c[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float v = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) v += red[NW * G + w * G + h];
-    l_c[h] = v;
-  }
 
   // ---- 5. contraction with the V codebook on the matrix cores ----------------
   // A[i][k]: rows i < 8 carry the fp16 high part of Hist[m_v][k][i], rows
@@ -528,10 +542,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   const int hh = l16 & 7;
   const bool lo_row = l16 >= 8;
   const int kh = lo_row ? 4 : 0;
-  uint32_t raw[K / 32][4];
+  uint32_t raw[KSL / 32][4];
 #pragma unroll
-  for (int st = 0; st < K / 32; ++st) {
-    const int k0 = st * 32 + 8 * q4 + kh;
+  for (int st = 0; st < KSL / 32; ++st) {
+    const int k0 = ksl * KSL + st * 32 + 8 * q4 + kh;
 #pragma unroll
     for (int v = 0; v < 4; ++v) raw[st][v] = 0;
     if (hh < G) {
@@ -547,7 +561,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   }
   f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int st = 0; st < K / 32; ++st) {
+  for (int st = 0; st < KSL / 32; ++st) {
     uint32_t hw[2], lw[2];   // packed fp16 pairs: high parts, low parts
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
@@ -579,21 +593,28 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   }
 
   // ---- 6. write (m, l, o) or the normalised output ----------------------------
-  // lane holds o[h = 4*q4 + r][d = m_v*DS + jt*16 + l16]; the chunk max and
-  // sum of head h are at red[h] and red[NW*G + h] (written below by wave 0's
-  // combine) -- reuse the per-wave slots: every thread already has m_c, l_c.
+  // lane holds the slice's o[h = 4*q4 + r][d = m_v*DS + jt*16 + l16]; the
+  // second slice's waves leave theirs in the (dead) table region and the
+  // first slice's waves add it and write.
+  float4* part_tile = reinterpret_cast<float4*>(lut);                      // [NTILE][64]
+  if (ksl == 1) part_tile[tile * 64 + lane] = make_float4(o[0], o[1], o[2], o[3]);
   __shared__ float fin[2 * G];
-  if (tid < G) {
-    float mh = m_c[0], lh = l_c[0];
+  if (tid < G) {   // head tid: chunk max and the sum of the waves' partial sums
+    float mh = m_c[0];
 #pragma unroll
-    for (int x = 1; x < G; ++x) {
-      mh = (tid == x) ? m_c[x] : mh;
-      lh = (tid == x) ? l_c[x] : lh;
-    }
+    for (int x = 1; x < G; ++x) mh = (tid == x) ? m_c[x] : mh;
+    float lh = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) lh += lsum[w * G + tid];
     fin[tid] = mh;
     fin[G + tid] = lh;
   }
   __syncthreads();
+  if (ksl != 0) return;
+  {
+    const float4 other = part_tile[tile * 64 + lane];
+    o[0] += other.x; o[1] += other.y; o[2] += other.z; o[3] += other.w;
+  }
   const int d = m_v * DS + jt * 16 + l16;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {

@@ -11,7 +11,7 @@ namespace {
 constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxGridYZ = 65535;
 constexpr int kTargetBlocks = 256;     // one score workgroup per CU (256 CUs)
-constexpr int kChunkGranule = 512;     // one token per thread of a 512-thread workgroup
+constexpr int kChunkGranule = 1024;    // one token per thread of a 1024-thread workgroup
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
