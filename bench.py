@@ -1,20 +1,23 @@
 """Benchmark of one decode step over a PQ-coded KV cache on one MI355X.
 
-A step is the whole hot path for one layer and one new token:
-  1. encode the new token's K and V vectors (B*Hkv each, one launch) by
-     nearest codeword straight into the code cache, at position lens[b]-1;
-  2. the fused score kernel (LUT build, code streaming, chunk softmax,
-     V histograms, codebook contraction) -> per-chunk (m, l, o);
-  3. the chunk-merge kernel -> out.
+A step is the whole hot path for one layer and one new token, in one launch
+(pq_attn_decode_step):
+  1. the new token's K and V vectors (B*Hkv each) are encoded by nearest
+     codeword straight into the code cache, at position lens[b]-1;
+  2. lookup-table build, code streaming, chunk softmax, V histograms and
+     codebook contraction -> per-chunk (m, l, o);
+  3. the last workgroup of each (request, KV head) merges the chunks -> out.
+The same step through three launches (pq_encode_many, pq_attn_partials,
+pq_attn_reduce) is timed too and reported under "detail".
 The workload is the GQA decode shape (B=8, Hq=64, Hkv=8, L=8192, M=8,
 K=256).  Inputs live in HBM before timing starts; N seeded replicas of every
 input are rotated so that the working set (>= 512 MiB) is twice the 256 MB
 Infinity Cache and each step reads its codes from HBM.
 
 Prints one JSON line.  `value` = KV tokens scanned per second over the timed
-steps (sum of lens per step / step time).  `roofline` is the score kernel's
+steps (sum of lens per step / step time).  `roofline` is the step kernel's
 algorithmic bytes per launch over its average duration, timed with HIP
-events around each launch on the stream it runs on.  `cpu_baseline` is the
+events the runtime stamps at the kernel's own start and end.  `cpu_baseline` is the
 CPU oracle on the same workload (repeated for 10+ s), on the host cores.
 """
 from __future__ import annotations
@@ -35,14 +38,16 @@ HBM_PEAK_GBS = 8000.0
 WORKLOAD_IDS = {"tiny": 1, "page-sizing": 2, "gqa": 3, "long-splitk": 4, "ragged": 5}
 
 
-def algorithmic_bytes(w, lens):
+def algorithmic_bytes(w, lens, step=True):
     """What the method must move for one decode step: the valid K and V codes,
-    both codebooks once per KV head, q (fp16) and out (fp32)."""
+    both codebooks once per KV head, q (fp16) and out (fp32); with the new
+    token appended, also its K and V vectors (fp16) in and their codes out."""
     codes = int(np.sum(lens)) * w.n_kv_heads * 2 * w.n_sub
     cbs = w.n_kv_heads * 2 * w.n_sub * w.n_codes * w.sub_dim * 2
     q = w.batch * w.n_q_heads * w.head_dim * 2
     out = w.batch * w.n_q_heads * w.head_dim * 4
-    return codes + cbs + q + out
+    new = w.batch * w.n_kv_heads * 2 * (w.head_dim * 2 + w.n_sub) if step else 0
+    return codes + cbs + q + out + new
 
 
 class HipEvents:
@@ -172,8 +177,7 @@ def main():
     for r in range(R):
         inp = base if r == 0 else gen.workload_inputs(wid, replica=r, with_encode=False)
         rng = np.random.default_rng([7000 + wid, r])
-        xk = rng.standard_normal((B, Hkv, D), dtype=np.float32).astype(np.float16)
-        xv = rng.standard_normal((B, Hkv, D), dtype=np.float32).astype(np.float16)
+        xk, _, xv, _ = gen.step_tokens(rng, inp["k_cb"], inp["v_cb"], B)
         t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev)
              for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")}
         t["xk"] = torch.from_numpy(xk).to(dev)
@@ -193,24 +197,28 @@ def main():
     pl = torch.empty((B, Hq, C), dtype=torch.float32, device=dev)
     po = torch.empty((B, Hq, C, D), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    ws = pq.step_workspace(desc, dev)       # zero-filled once; every step leaves it so
 
     def step(t, ev=None):
-        # the new token's K and V, one launch
+        pq.pq_attn_decode_step(t["q"], t["xk"], t["xv"], t["k_codes"], t["v_codes"], t["k_cb"],
+                               t["v_cb"], t["lens"], out, desc=desc, workspace=ws, stream=stream,
+                               events=ev)
+
+    def step_three_launches(t):
         pq.pq_encode_many([t["xk"], t["xv"]], [t["k_cb"], t["v_cb"]], [t["k_codes"], t["v_codes"]],
                           slots=t["slots"], desc=enc_desc, stream=stream)
-        # the score kernel writes the chunk records; the merge kernel reads them
-        # (for C == 1 the merge is a pass over one record per row)
         pq.pq_attn_partials(t["q"], t["k_codes"], t["v_codes"], t["k_cb"], t["v_cb"], t["lens"],
-                            desc=desc, part_m=pm, part_l=pl, part_o=po, stream=stream, events=ev)
+                            desc=desc, part_m=pm, part_l=pl, part_o=po, stream=stream)
         pq.pq_attn_reduce(pm, pl, po, out, stream=stream)
 
     for i in range(args.warmup):
         step(reps[i % R])
+        step_three_launches(reps[i % R])
     torch.cuda.synchronize()
 
     K = args.steps
     # (a) the timed region: K whole steps; the runtime stamps a pair of events
-    # at each score kernel's own start and end
+    # at each step kernel's own start and end
     hip = HipEvents()
     raw = hip.create(2 * K)
     evs = [(raw[2 * i], raw[2 * i + 1]) for i in range(K)]
@@ -237,6 +245,15 @@ def main():
     torch.cuda.synchronize()
     step_ms_plain = start.elapsed_time(end) / K
 
+    # (c) the same step as three launches, for comparison
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        step_three_launches(reps[i % R])
+    end.record(stream)
+    torch.cuda.synchronize()
+    step_ms_three = start.elapsed_time(end) / K
+
     value = tokens_per_step / (step_ms_plain * 1e-3)
     alg = algorithmic_bytes(w, lens_np)
     achieved = alg / (score_ms * 1e-3) / 1e9
@@ -256,13 +273,14 @@ def main():
         "data": "synthetic (seeded generators; codebooks and q fp16 N(0,1), codes uniform uint8)",
         "config": {"workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} L={L} D={D} M={M} K={w.n_codes}",
                    "chunk": int(desc.chunk) or "library", "n_chunks": C, "replicas": R,
-                   "step": "encode new K and V (one launch) -> score kernel -> merge kernel"},
+                   "step": "one launch: encode new K and V into the cache, attend, merge chunks"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(),
-                     "kernel": "decode_partials_kernel", "algorithmic_bytes": alg,
+                     "kernel": "decode_partials_kernel (decode-step variant)", "algorithmic_bytes": alg,
                      "avg_launch_us": score_ms * 1e3},
         "detail": {"step_us_with_kernel_events": step_ms * 1e3, "step_us": step_ms_plain * 1e3,
-                   "score_kernel_us_p50": float(np.median(kern_ms)) * 1e3,
+                   "step_kernel_us_p50": float(np.median(kern_ms)) * 1e3,
+                   "step_us_three_launches": step_ms_three * 1e3,
                    "wall_s": wall, "tokens_per_step": tokens_per_step},
     }
     if args.copy_probe_mib:

@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "PQ_OK", 1: "PQ_ERR_NULL", 2: "PQ_ERR_SHAPE", 3: "PQ_ERR_UNSU
                 4: "PQ_ERR_WORKSPACE", 5: "PQ_ERR_HIP", 6: "PQ_ERR_ALIGN"}
 
 EXPORTED = ("pq_attn_num_chunks", "pq_attn_workspace_bytes", "pq_attn_decode",
-            "pq_attn_partials", "pq_attn_partials_timed", "pq_attn_reduce", "pq_encode",
+            "pq_attn_partials", "pq_attn_partials_timed", "pq_attn_step_workspace_bytes",
+            "pq_attn_decode_step", "pq_attn_decode_step_timed", "pq_attn_reduce", "pq_encode",
             "pq_encode_many", "pq_status_string")
 
 
@@ -73,6 +74,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pq_attn_partials_timed.argtypes = [ctypes.POINTER(PQAttnDesc), P, P, P, P, P, P, P, P, P,
                                            P, P, P]
     lib.pq_attn_partials_timed.restype = ctypes.c_int
+    lib.pq_attn_step_workspace_bytes.argtypes = [ctypes.POINTER(PQAttnDesc)]
+    lib.pq_attn_step_workspace_bytes.restype = ctypes.c_size_t
+    lib.pq_attn_decode_step.argtypes = [ctypes.POINTER(PQAttnDesc), P, P, P, P, P, P, P, P, P,
+                                        P, ctypes.c_size_t, P]
+    lib.pq_attn_decode_step.restype = ctypes.c_int
+    lib.pq_attn_decode_step_timed.argtypes = [ctypes.POINTER(PQAttnDesc), P, P, P, P, P, P, P,
+                                              P, P, P, ctypes.c_size_t, P, P, P]
+    lib.pq_attn_decode_step_timed.restype = ctypes.c_int
     lib.pq_attn_reduce.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
     lib.pq_attn_reduce.restype = ctypes.c_int
     lib.pq_encode.argtypes = [ctypes.POINTER(PQEncodeDesc), P, P, P, P, P]
@@ -209,6 +218,53 @@ def pq_attn_partials(q, k_codes, v_codes, k_cb, v_cb, lens, *, desc=None, chunk=
         st = lib.pq_attn_partials_timed(*args, events[0], events[1])
     _check(st, "pq_attn_partials")
     return part_m, part_l, part_o
+
+
+def pq_attn_step_workspace_bytes(desc: PQAttnDesc) -> int:
+    return int(load_library().pq_attn_step_workspace_bytes(ctypes.byref(desc)))
+
+
+def step_workspace(desc: PQAttnDesc, device):
+    """A zero-filled workspace for pq_attn_decode_step (None when it needs
+    none).  Keep it for later steps: each call leaves it ready."""
+    import torch
+    n = pq_attn_step_workspace_bytes(desc)
+    return None if n == 0 else torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def pq_attn_decode_step(q, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, out=None, *,
+                        desc=None, chunk=0, scale=None, workspace=None, stream=None,
+                        events=None):
+    """One decode step with the new token appended (C entry point
+    pq_attn_decode_step): encodes k_new/v_new [B, Hkv, D] into slot
+    lens[b] - 1 of the code caches (written in place) and returns ``out``
+    (fp32 [B, Hq, D]).  ``workspace`` must come from step_workspace() (or be
+    zero-filled) when the shape needs one; it is created here if omitted.
+    ``events=(start, stop)`` goes through pq_attn_decode_step_timed."""
+    import torch
+    if desc is None:
+        desc = attn_desc(q, k_codes, k_cb, chunk=chunk, scale=scale)
+    _check_attn_inputs(desc, q, k_codes, v_codes, k_cb, v_cb, lens)
+    shape_new = (desc.batch, desc.n_kv_heads, desc.head_dim)
+    _need(k_new, "k_new", torch.float16, shape_new)
+    _need(v_new, "v_new", torch.float16, shape_new)
+    if out is None:
+        out = torch.empty((desc.batch, desc.n_q_heads, desc.head_dim), dtype=torch.float32,
+                          device=q.device)
+    _need(out, "out", torch.float32, (desc.batch, desc.n_q_heads, desc.head_dim))
+    if workspace is None:
+        workspace = step_workspace(desc, q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_codes), _ptr(v_codes),
+            _ptr(k_cb), _ptr(v_cb), _ptr(lens), _ptr(out), _ptr(workspace), nbytes,
+            _stream(stream))
+    if events is None:
+        st = lib.pq_attn_decode_step(*args)
+    else:
+        st = lib.pq_attn_decode_step_timed(*args, events[0], events[1])
+    _check(st, "pq_attn_decode_step")
+    return out
 
 
 def pq_attn_reduce(part_m, part_l, part_o, out=None, *, stream=None):

@@ -21,27 +21,33 @@ constexpr int kEncodeVectors = 256;   // vectors per encode workgroup (one wave 
 
 using DecodeFn = void (*)(DecodeArgs);
 
-template <int G, int M>
+template <int G, int M, bool STEP>
 DecodeFn pick_nt(int T) {
-  if (T <= kDecodeThreads) return &decode_partials_kernel<G, M, 1>;
-  if (T <= 2 * kDecodeThreads) return &decode_partials_kernel<G, M, 2>;
-  if (T <= 4 * kDecodeThreads) return &decode_partials_kernel<G, M, 4>;
+  if (T <= kDecodeThreads) return &decode_partials_kernel<G, M, 1, STEP>;
+  if (T <= 2 * kDecodeThreads) return &decode_partials_kernel<G, M, 2, STEP>;
+  if (T <= 4 * kDecodeThreads) return &decode_partials_kernel<G, M, 4, STEP>;
   return nullptr;
 }
 
-// The kernel instance for (G, M) and the chunk length T (T <= kMaxChunk).
-DecodeFn pick_decode(int G, int M, int T) {
+template <bool STEP>
+DecodeFn pick_gm(int G, int M, int T) {
   switch (M * 16 + G) {
-    case 4 * 16 + 1: return pick_nt<1, 4>(T);
-    case 4 * 16 + 2: return pick_nt<2, 4>(T);
-    case 4 * 16 + 4: return pick_nt<4, 4>(T);
-    case 4 * 16 + 8: return pick_nt<8, 4>(T);
-    case 8 * 16 + 1: return pick_nt<1, 8>(T);
-    case 8 * 16 + 2: return pick_nt<2, 8>(T);
-    case 8 * 16 + 4: return pick_nt<4, 8>(T);
-    case 8 * 16 + 8: return pick_nt<8, 8>(T);
+    case 4 * 16 + 1: return pick_nt<1, 4, STEP>(T);
+    case 4 * 16 + 2: return pick_nt<2, 4, STEP>(T);
+    case 4 * 16 + 4: return pick_nt<4, 4, STEP>(T);
+    case 4 * 16 + 8: return pick_nt<8, 4, STEP>(T);
+    case 8 * 16 + 1: return pick_nt<1, 8, STEP>(T);
+    case 8 * 16 + 2: return pick_nt<2, 8, STEP>(T);
+    case 8 * 16 + 4: return pick_nt<4, 8, STEP>(T);
+    case 8 * 16 + 8: return pick_nt<8, 8, STEP>(T);
   }
   return nullptr;
+}
+
+// The kernel instance for (G, M), the chunk length T (T <= kMaxChunk) and
+// the plain or decode-step variant.
+DecodeFn pick_decode(int G, int M, int T, bool step) {
+  return step ? pick_gm<true>(G, M, T) : pick_gm<false>(G, M, T);
 }
 
 // Launch; with events, the runtime stamps them at the kernel's own start and
@@ -63,14 +69,21 @@ pq_status check_attn_pointers(const void* q, const void* kc, const void* vc, con
   return PQ_OK;
 }
 
+// One score-kernel launch.  pm/pl/po null: the normalised output goes to
+// out (C == 1).  step: the decode-step variant with the new token's K and V
+// (and, with C > 1, the arrival counters of the fused merge).
 pq_status launch_partials(const AttnPlan& p, const void* q, const uint8_t* kc, const uint8_t* vc,
                           const void* kcb, const void* vcb, const int32_t* lens, float* pm,
                           float* pl, float* po, float* out, hipStream_t stream,
-                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr) {
+                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr,
+                          const void* k_new = nullptr, const void* v_new = nullptr,
+                          uint32_t* counters = nullptr) {
+  const bool step = k_new != nullptr;
   DecodeArgs a;
   a.q = static_cast<const __half*>(q);
-  a.k_codes = kc;
-  a.v_codes = vc;
+  // the plain kernel never writes the code arrays
+  a.k_codes = const_cast<uint8_t*>(kc);
+  a.v_codes = const_cast<uint8_t*>(vc);
   a.k_cb = static_cast<const __half*>(kcb);
   a.v_cb = static_cast<const __half*>(vcb);
   a.lens = lens;
@@ -78,13 +91,16 @@ pq_status launch_partials(const AttnPlan& p, const void* q, const uint8_t* kc, c
   a.part_l = pl;
   a.part_o = po;
   a.out = out;
+  a.k_new = static_cast<const __half*>(k_new);
+  a.v_new = static_cast<const __half*>(v_new);
+  a.counters = counters;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.Lmax = p.Lmax;
   a.T = p.T;
   a.C = p.C;
   a.qscale = p.scale * kLog2e;
-  DecodeFn fn = pick_decode(p.G, p.M, p.T);
+  DecodeFn fn = pick_decode(p.G, p.M, p.T, step);
   if (!fn) return PQ_ERR_UNSUPPORTED;
   return launch(reinterpret_cast<const void*>(fn), dim3(unsigned(p.Hkv), unsigned(p.C), unsigned(p.B)),
                 dim3(kDecodeThreads),
@@ -167,6 +183,54 @@ pq_status pq_attn_partials_timed(const pq_attn_desc* desc, const void* q, const 
   return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, part_m, part_l, part_o, nullptr,
                          static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
                          static_cast<hipEvent_t>(stop_event));
+}
+
+size_t pq_attn_step_workspace_bytes(const pq_attn_desc* desc) {
+  AttnPlan p;
+  return plan_attn(desc, &p) == PQ_OK ? p.ws_step_bytes : 0;
+}
+
+static pq_status decode_step(const pq_attn_desc* desc, const void* q, const void* k_new,
+                             const void* v_new, uint8_t* k_codes, uint8_t* v_codes,
+                             const void* k_cb, const void* v_cb, const int32_t* lens, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* start_event, void* stop_event) {
+  AttnPlan p;
+  pq_status st = plan_attn(desc, &p);
+  if (st != PQ_OK) return st;
+  st = check_attn_pointers(q, k_codes, v_codes, k_cb, v_cb, lens);
+  if (st != PQ_OK) return st;
+  if (!out || !k_new || !v_new) return PQ_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return PQ_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
+  if (p.C == 1)
+    return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, nullptr, nullptr, nullptr, out,
+                           s, e0, e1, k_new, v_new, nullptr);
+  if (!workspace || workspace_bytes < p.ws_step_bytes || !aligned16(workspace))
+    return PQ_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens,
+                         reinterpret_cast<float*>(ws + p.ws_m_off), reinterpret_cast<float*>(ws + p.ws_l_off),
+                         reinterpret_cast<float*>(ws + p.ws_o_off), out, s, e0, e1, k_new, v_new,
+                         reinterpret_cast<uint32_t*>(ws + p.ws_cnt_off));
+}
+
+pq_status pq_attn_decode_step(const pq_attn_desc* desc, const void* q, const void* k_new,
+                              const void* v_new, uint8_t* k_codes, uint8_t* v_codes,
+                              const void* k_cb, const void* v_cb, const int32_t* lens, float* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_step(desc, q, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, out, workspace,
+                     workspace_bytes, stream, nullptr, nullptr);
+}
+
+pq_status pq_attn_decode_step_timed(const pq_attn_desc* desc, const void* q, const void* k_new,
+                                    const void* v_new, uint8_t* k_codes, uint8_t* v_codes,
+                                    const void* k_cb, const void* v_cb, const int32_t* lens,
+                                    float* out, void* workspace, size_t workspace_bytes,
+                                    void* stream, void* start_event, void* stop_event) {
+  return decode_step(desc, q, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, out, workspace,
+                     workspace_bytes, stream, start_event, stop_event);
 }
 
 pq_status pq_attn_reduce(int64_t n_rows, int32_t n_chunks, int32_t head_dim, const float* part_m,

@@ -46,16 +46,19 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct DecodeArgs {
   const __half* q;           // [B][Hq][D]
-  const uint8_t* k_codes;    // [B][Hkv][Lmax][M]
-  const uint8_t* v_codes;
+  uint8_t* k_codes;          // [B][Hkv][Lmax][M]; written only by the step
+  uint8_t* v_codes;          //   kernel, at the new token's slot
   const __half* k_cb;        // [Hkv][M][K][DS]
   const __half* v_cb;
   const int32_t* lens;       // [B]
-  float* part_m;             // [B*Hq][C]
-  float* part_l;             // [B*Hq][C]
-  float* part_o;             // [B*Hq][C][D]
-  float* out;                // [B*Hq][D]; when non-null (C == 1) the normalised
-                             // output is written instead of the partials
+  float* part_m;             // [B*Hq][C]     chunk records; all three null:
+  float* part_l;             // [B*Hq][C]     the normalised output is written
+  float* part_o;             // [B*Hq][C][D]  directly (C == 1)
+  float* out;                // [B*Hq][D]
+  const __half* k_new;       // [B][Hkv][D] the new token's K and V (step kernel)
+  const __half* v_new;
+  uint32_t* counters;        // [B*Hkv] chunk arrivals (step kernel with C > 1):
+                             // zero on entry, zero again on exit
   int32_t Hq, Hkv, Lmax, T, C;
   float qscale;              // scale * log2(e)
 };
@@ -71,6 +74,21 @@ constexpr int kDppXor1 = 0xB1;   // quad_perm(1,0,3,2)
 constexpr int kDppXor2 = 0x4E;   // quad_perm(2,3,0,1)
 constexpr int kDppRor4 = 0x124;  // row_ror:4
 constexpr int kDppRor8 = 0x128;  // row_ror:8
+
+// v[l] + v[l ^ 16] and v[l] + v[l ^ 32] in every lane l: the lane-swap
+// instructions return the pair (v[l & ~m], v[l | m]) in their two outputs,
+// and their sum is the same float in both lanes of the pair (VALU only, no
+// LDS traffic).
+__device__ __forceinline__ float pair_sum16(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  return __builtin_bit_cast(float, int(r[0])) + __builtin_bit_cast(float, int(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float v) {
+  const int b = __builtin_bit_cast(int, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __builtin_bit_cast(float, int(r[0])) + __builtin_bit_cast(float, int(r[1]));
+}
 
 // Wave-wide max / sum of N values at once: all-reduce inside each row with
 // DPP, then combine the four rows' results read from lanes 0, 16, 32, 48.
@@ -119,10 +137,114 @@ __device__ __forceinline__ float key_float(int k) {
   return __builtin_bit_cast(float, k >= 0 ? k : k ^ 0x7fffffff);
 }
 
+template <int CTRL>
+__device__ __forceinline__ int dpp_int(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+
+// (score, index) -> the better of the pair and its DPP partner: the larger
+// score, or on equal scores the lower index.
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& s, int& k) {
+  const float os = dpp_f<CTRL>(s);
+  const int ok = dpp_int<CTRL>(k);
+  const bool take = (os > s) || (os == s && ok < k);
+  s = take ? os : s;
+  k = take ? ok : k;
+}
+
+// 64-bit key whose unsigned order is (score, then lower index): the integer
+// LDS max of keys is the argmax with the lowest index among equal scores.
+__device__ __forceinline__ unsigned long long argmax_key(float score, int k) {
+  const uint32_t hi = uint32_t(float_key(score)) ^ 0x80000000u;
+  return (static_cast<unsigned long long>(hi) << 32) | uint32_t(255 - k);
+}
+__device__ __forceinline__ int argmax_key_index(unsigned long long key) {
+  return 255 - int(key & 0xffu);
+}
+
+// Chunk-record access.  COH: agent-scope (device-coherent) atomic stores and
+// loads, which the chip keeps coherent across its per-XCD L2 caches without
+// cache writebacks or invalidations; used where one workgroup reads records
+// that others wrote in the same launch.
+template <bool COH>
+__device__ __forceinline__ void rec_store(float* p, float v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ float rec_load(const float* p) {
+  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+
+// Merge of one output element over C chunk records (m in natural-log units):
+//   sum_c w_c o_c / sum_c w_c l_c,  w_c = exp(m_c - max_c m_c),
+// 0 when every chunk is empty (m = -inf, l = 0).
+template <bool COH = false>
+__device__ __forceinline__ float merge_chunks(const float* pm, const float* pl, const float* po,
+                                              int C, int stride_o) {
+  constexpr int kFew = 8;   // up to this many chunks: every record load issued at once
+  float m_star = -INFINITY, num = 0.0f, den = 0.0f;
+  if (C <= kFew) {
+    float m[kFew], l[kFew], o[kFew];
+#pragma unroll
+    for (int c = 0; c < kFew; ++c) {
+      m[c] = c < C ? rec_load<COH>(pm + c) : -INFINITY;
+      l[c] = c < C ? rec_load<COH>(pl + c) : 0.0f;
+      o[c] = c < C ? rec_load<COH>(po + int64_t(c) * stride_o) : 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < kFew; ++c) m_star = fmaxf(m_star, m[c]);
+    if (m_star != -INFINITY) {
+#pragma unroll
+      for (int c = 0; c < kFew; ++c) {
+        if (m[c] == -INFINITY) continue;
+        const float w = fast_exp2((m[c] - m_star) * kLog2e);
+        num = fmaf(w, o[c], num);
+        den = fmaf(w, l[c], den);
+      }
+    }
+  } else {
+    for (int c = 0; c < C; ++c) m_star = fmaxf(m_star, rec_load<COH>(pm + c));
+    if (m_star != -INFINITY) {
+      for (int c = 0; c < C; ++c) {
+        const float mc = rec_load<COH>(pm + c);
+        if (mc == -INFINITY) continue;
+        const float w = fast_exp2((mc - m_star) * kLog2e);
+        num = fmaf(w, rec_load<COH>(po + int64_t(c) * stride_o), num);
+        den = fmaf(w, rec_load<COH>(pl + c), den);
+      }
+    }
+  }
+  return den > 0.0f ? num / den : 0.0f;
+}
+
+// Chunk-arrival count for one (request, KV head), called by every thread of
+// a workgroup after its chunk record has been stored with rec_store<true>.
+// Every wave first waits until its own stores have completed (vmcnt = 0:
+// acknowledged at the device-coherent level), then thread 0 adds 1 to the
+// counter with a device-scope atomic.  So when a workgroup's add returns
+// C - 1, the C records are complete, and that workgroup -- the only one told
+// so -- reads them with rec_load<true>.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, int C, uint32_t* flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    uint32_t(C - 1) ? 1u : 0u;
+  __syncthreads();
+  return *flag != 0;
+}
+
 // Code bytes of one token: M = 4 -> one dword, M = 8 -> two dwords.
 template <int M> struct TokenCodes;
 template <> struct TokenCodes<4> {
   uint32_t w = 0;
+  __device__ __forceinline__ void set(const int* c) {
+    w = uint32_t(c[0]) | (uint32_t(c[1]) << 8) | (uint32_t(c[2]) << 16) | (uint32_t(c[3]) << 24);
+  }
+  __device__ __forceinline__ void store(uint8_t* p) const { *reinterpret_cast<uint32_t*>(p) = w; }
   __device__ __forceinline__ void load(const uint8_t* p) { w = *reinterpret_cast<const uint32_t*>(p); }
   __device__ __forceinline__ int get(int m) const { return (w >> (8 * m)) & 0xff; }
   // the codes with byte j holding segment (j + r) % 4
@@ -134,6 +256,11 @@ template <> struct TokenCodes<4> {
 };
 template <> struct TokenCodes<8> {
   uint2 w = {0, 0};
+  __device__ __forceinline__ void set(const int* c) {
+    w.x = uint32_t(c[0]) | (uint32_t(c[1]) << 8) | (uint32_t(c[2]) << 16) | (uint32_t(c[3]) << 24);
+    w.y = uint32_t(c[4]) | (uint32_t(c[5]) << 8) | (uint32_t(c[6]) << 16) | (uint32_t(c[7]) << 24);
+  }
+  __device__ __forceinline__ void store(uint8_t* p) const { *reinterpret_cast<uint2*>(p) = w; }
   __device__ __forceinline__ void load(const uint8_t* p) { w = *reinterpret_cast<const uint2*>(p); }
   __device__ __forceinline__ int get(int m) const {
     return ((m < 4 ? w.x : w.y) >> (8 * (m & 3))) & 0xff;
@@ -243,14 +370,70 @@ __device__ __forceinline__ f16x4 quad_transpose(uint32_t w0, uint32_t w1, int u)
   return out;
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// -|c|^2 / 2 of the codeword whose MFMA B-operand pieces this lane holds
+// (4 dims per k-step), summed over the four lanes l16, l16+16, l16+32,
+// l16+48 that hold the rest of it.
+template <int KS>
+__device__ __forceinline__ float neg_half_norm2(const f16x4 (&b)[KS]) {
+  float p = 0.0f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const f16x2 lo = {b[s][0], b[s][1]};
+    const f16x2 hi = {b[s][2], b[s][3]};
+    p = __builtin_amdgcn_fdot2(lo, lo, p, false);
+    p = __builtin_amdgcn_fdot2(hi, hi, p, false);
+  }
+  p = pair_sum16(p);
+  p = pair_sum32(p);
+  return -0.5f * p;
+}
+
+// The new token's codes from the per-wave argmax keys: waves m, m + M, ...
+// searched segment m's codewords.
+template <int M, int NW>
+__device__ __forceinline__ TokenCodes<M> combine_new_codes(const unsigned long long* keys) {
+  int code[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    unsigned long long best = keys[m];
+#pragma unroll
+    for (int w = m + M; w < NW; w += M) best = keys[w] > best ? keys[w] : best;
+    code[m] = argmax_key_index(best);
+  }
+  TokenCodes<M> t;
+  t.set(code);
+  return t;
+}
+
+// The last workgroup of (request, KV head) bg: the normalised output of its
+// G query rows from the C chunk records.
+template <int G>
+__device__ __forceinline__ void merge_rows(const DecodeArgs& a, int64_t row0, int64_t bg) {
+  constexpr int D = 128;
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    const int64_t row = row0 + i / D;
+    const int d = i % D;
+    a.out[row * D + d] = merge_chunks<true>(a.part_m + row * a.C, a.part_l + row * a.C,
+                                            a.part_o + row * a.C * D + d, a.C, D);
+  }
+  if (threadIdx.x == 0)   // ready for the next call
+    __hip_atomic_store(a.counters + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Two fp16 halves of an fp32 value: v ~= hi + lo to about 22 bits.
 __device__ __forceinline__ void split_f16(float v, _Float16& hi, _Float16& lo) {
   hi = (_Float16)v;
   lo = (_Float16)(v - (float)hi);
 }
 
-// G query heads per KV head, M segments, NT token slots per thread.
-template <int G, int M, int NT>
+// G query heads per KV head, M segments, NT token slots per thread.  STEP:
+// the decode-step variant -- the workgroup whose chunk holds the new token
+// (slot lens[b] - 1) encodes the token's K and V into the cache first, and
+// with C > 1 the last workgroup of each (request, KV head) merges the chunk
+// records into the output.
+template <int G, int M, int NT, bool STEP>
 __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeArgs a) {
   constexpr int NTHR = kDecodeThreads;
   constexpr int D = 128;
@@ -284,6 +467,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   char* hist_bytes = reinterpret_cast<char*>(hist);                        // [k][R] u64 (G >= 2)
   __shared__ float lsum[NW * G];              // per-wave partial sums of p
   __shared__ __align__(16) int mkey[G];       // chunk max per head, as float_key
+  __shared__ unsigned long long new_key[2][NW];  // step: per-wave argmax keys of the new K, V
+  __shared__ uint32_t arrive_flag;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -308,13 +493,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   // table build: wave w owns segment m_l = w % M and codeword tiles
   // nt = w / M + (NW / M) * i
   const int m_l = wave % M;
-  f16x4 qa[KSTEP_Q];
+  // Row 8 of the table build's A operand (unused by the <= 8 heads) carries
+  // segment m_l of the new token's K in the step kernel, and xv that of its
+  // V, so the same instructions score the token against the codewords.
+  constexpr int kNewRow = 8;
+  const int64_t bg = int64_t(b) * a.Hkv + g;
+  f16x4 qa[KSTEP_Q], xv[KSTEP_Q];
 #pragma unroll
   for (int s = 0; s < KSTEP_Q; ++s) {
+    qa[s] = f16x4{0, 0, 0, 0};
+    xv[s] = f16x4{0, 0, 0, 0};
     if (l16 < G) {
       qa[s] = *reinterpret_cast<const f16x4*>(a.q + (row0 + l16) * D + m_l * DS + s * 16 + 4 * q4);
-    } else {
-      qa[s] = f16x4{0, 0, 0, 0};
+    } else if (STEP && l16 == kNewRow) {
+      qa[s] = *reinterpret_cast<const f16x4*>(a.k_new + bg * D + m_l * DS + s * 16 + 4 * q4);
+      xv[s] = *reinterpret_cast<const f16x4*>(a.v_new + bg * D + m_l * DS + s * 16 + 4 * q4);
     }
   }
   f16x4 ckb[LUT_JOBS][KSTEP_Q];
@@ -331,21 +524,26 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   if (t_begin >= t_end) {   // empty chunk (uniform over the workgroup)
     for (int i = tid; i < G * D; i += NTHR) {
       const int h = i / D, d = i % D;
-      if (a.out != nullptr) {
+      if (a.part_o == nullptr) {
         a.out[(row0 + h) * D + d] = 0.0f;
       } else {
-        a.part_o[((row0 + h) * a.C + c) * D + d] = 0.0f;
+        rec_store<STEP>(a.part_o + ((row0 + h) * a.C + c) * D + d, 0.0f);
         if (d == 0) {
-          a.part_m[(row0 + h) * a.C + c] = -INFINITY;
-          a.part_l[(row0 + h) * a.C + c] = 0.0f;
+          rec_store<STEP>(a.part_m + (row0 + h) * a.C + c, -INFINITY);
+          rec_store<STEP>(a.part_l + (row0 + h) * a.C + c, 0.0f);
         }
       }
+    }
+    if constexpr (STEP) {
+      if (a.part_o != nullptr && arrive_last(a.counters + bg, a.C, &arrive_flag)) merge_rows<G>(a, row0, bg);
     }
     return;
   }
 
+  // step kernel: does this chunk hold the new token (slot lens[b] - 1)?
+  const int t_new = STEP ? len - 1 : -1;
+  const bool has_new = STEP && t_new >= t_begin && t_new < t_end;   // uniform
   // the chunk's K and V codes (only tokens below lens[b] are read)
-  const int64_t bg = int64_t(b) * a.Hkv + g;
   const uint8_t* kc = a.k_codes + bg * a.Lmax * M;
   const uint8_t* vc = a.v_codes + bg * a.Lmax * M;
   TokenCodes<M> kcode[NT], vcode[NT];
@@ -364,15 +562,31 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   if (tid < G) mkey[tid] = float_key(-INFINITY);
 
   // ---- 1. lookup table on the matrix cores ----------------------------------
+  // Step kernel, chunk with the new token: row 8 of every product starts at
+  // -|c|^2/2 of its codeword c, so it ends at x.c - |c|^2/2, whose argmax is
+  // the nearest codeword (the arithmetic of pq_encode, decision for decision).
+  // The K code is needed by the scores, so it is found here; the V code only
+  // by the histogram, so it is found while the scores are gathered.
+  float best_k = -INFINITY;
+  int idx_k = 0;
 #pragma unroll
   for (int i = 0; i < LUT_JOBS; ++i) {
     const int nt = wave / M + (NW / M) * i;
+    const int k = nt * 16 + l16;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (STEP) {
+      if (has_new) {   // (all lanes: the norm sums across lanes)
+        const float cn = neg_half_norm2<KSTEP_Q>(ckb[i]);
+        if (q4 == kNewRow / 4) acc[0] = cn;
+      }
+    }
 #pragma unroll
     for (int s = 0; s < KSTEP_Q; ++s)
       acc = __builtin_amdgcn_mfma_f32_16x16x16f16(qa[s], ckb[i][s], acc, 0, 0, 0);
+    if constexpr (STEP) {
+      if (has_new && acc[0] > best_k) { best_k = acc[0]; idx_k = k; }   // ascending k: ties keep the lower
+    }
     // lane holds LUT[h = 4*q4 + r][k = nt*16 + l16], r < 4
-    const int k = nt * 16 + l16;
     if constexpr (G >= 4) {
       if (4 * q4 < G)
         *reinterpret_cast<float4*>(lut + lut_index<G, K>(m_l, k, q4)) =
@@ -384,7 +598,41 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
       if (q4 == 0) lut[lut_index<G, K>(m_l, k, 0)] = acc[0] * a.qscale;
     }
   }
+  if constexpr (STEP) {
+    if (has_new) {   // argmax over the row's 16 lanes; the segment's waves are combined below
+      argmax_step<kDppXor1>(best_k, idx_k); argmax_step<kDppXor2>(best_k, idx_k);
+      argmax_step<kDppRor4>(best_k, idx_k); argmax_step<kDppRor8>(best_k, idx_k);
+      if (lane == 16 * (kNewRow / 4)) new_key[0][wave] = argmax_key(best_k, idx_k);
+    }
+  }
   __syncthreads();
+
+  if constexpr (STEP) {
+    if (has_new) {   // the new token's K codes: into the cache and into its slot's registers
+      TokenCodes<M> nk = combine_new_codes<M, NW>(new_key[0]);
+      if (tid == 0) nk.store(a.k_codes + (bg * a.Lmax + t_new) * M);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        if (t_begin + i * NTHR + tid == t_new) kcode[i] = nk;
+      }
+    }
+  }
+
+  // step kernel: the V codebook in the table build's B layout, for the new
+  // token's V code (its latency overlaps the gathers below)
+  f16x4 cvl[STEP ? LUT_JOBS : 1][KSTEP_Q];
+  if constexpr (STEP) {
+    if (has_new) {
+      const __half* cvg_l = a.v_cb + int64_t(g) * M * K * DS;
+#pragma unroll
+      for (int i = 0; i < LUT_JOBS; ++i) {
+        const int nt = wave / M + (NW / M) * i;
+        const __half* row = cvg_l + (int64_t(m_l) * K + nt * 16 + l16) * DS + 4 * q4;
+#pragma unroll
+        for (int s = 0; s < KSTEP_Q; ++s) cvl[i][s] = *reinterpret_cast<const f16x4*>(row + s * 16);
+      }
+    }
+  }
 
   // ---- 2. scores --------------------------------------------------------------
   float s[NT][G];
@@ -396,6 +644,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
     } else {
 #pragma unroll
       for (int h = 0; h < G; ++h) s[i][h] = -INFINITY;
+    }
+  }
+
+  if constexpr (STEP) {
+    if (has_new) {   // the new token's V: same products as its K above, per-wave argmax
+      float best_v = -INFINITY;
+      int idx_v = 0;
+#pragma unroll
+      for (int i = 0; i < LUT_JOBS; ++i) {
+        const int nt = wave / M + (NW / M) * i;
+        f32x4 accv = {0.f, 0.f, 0.f, 0.f};
+        const float cn = neg_half_norm2<KSTEP_Q>(cvl[i]);   // all lanes: sums across lanes
+        if (q4 == kNewRow / 4) accv[0] = cn;
+#pragma unroll
+        for (int s = 0; s < KSTEP_Q; ++s)
+          accv = __builtin_amdgcn_mfma_f32_16x16x16f16(xv[s], cvl[i][s], accv, 0, 0, 0);
+        if (accv[0] > best_v) { best_v = accv[0]; idx_v = nt * 16 + l16; }
+      }
+      argmax_step<kDppXor1>(best_v, idx_v); argmax_step<kDppXor2>(best_v, idx_v);
+      argmax_step<kDppRor4>(best_v, idx_v); argmax_step<kDppRor8>(best_v, idx_v);
+      if (lane == 16 * (kNewRow / 4)) new_key[1][wave] = argmax_key(best_v, idx_v);
     }
   }
 
@@ -418,6 +687,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < G; ++h) m_c[h] = key_float(mkey[h]);
+  if constexpr (STEP) {
+    if (has_new) {   // the new token's V codes (per-wave keys written before the barrier above)
+      TokenCodes<M> nv = combine_new_codes<M, NW>(new_key[1]);
+      if (tid == 0) nv.store(a.v_codes + (bg * a.Lmax + t_new) * M);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        if (t_begin + i * NTHR + tid == t_new) vcode[i] = nv;
+      }
+    }
+  }
 
   // V codebook operands of the contraction, requested once the scores are
   // in registers (earlier they would queue ahead of the table operands and
@@ -588,8 +867,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   f32x4 o;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float c = oa[r] + ob[r];
-    o[r] = c + __shfl_xor(c, 32, 64);   // rows 4*q4 + r and 4*q4 + r + 8 (lane + 32)
+    o[r] = pair_sum32(oa[r] + ob[r]);   // rows 4*q4 + r and 4*q4 + r + 8 (lane + 32)
   }
 
   // ---- 6. write (m, l, o) or the normalised output ----------------------------
@@ -610,27 +888,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
     fin[G + tid] = lh;
   }
   __syncthreads();
-  if (ksl != 0) return;
-  {
+  if (ksl == 0) {
     const float4 other = part_tile[tile * 64 + lane];
     o[0] += other.x; o[1] += other.y; o[2] += other.z; o[3] += other.w;
-  }
-  const int d = m_v * DS + jt * 16 + l16;
+    const int d = m_v * DS + jt * 16 + l16;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * q4 + r;
-    if (h < G) {
-      const float mh = fin[h], lh = fin[G + h];
-      if (a.out != nullptr) {
-        a.out[(row0 + h) * D + d] = lh > 0.0f ? o[r] * __builtin_amdgcn_rcpf(lh) : 0.0f;
-      } else {
-        a.part_o[((row0 + h) * a.C + c) * D + d] = o[r];
-        if (d == 0) {
-          a.part_m[(row0 + h) * a.C + c] = mh * kLn2;
-          a.part_l[(row0 + h) * a.C + c] = lh;
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * q4 + r;
+      if (h < G) {
+        const float mh = fin[h], lh = fin[G + h];
+        if (a.part_o == nullptr) {
+          a.out[(row0 + h) * D + d] = lh > 0.0f ? o[r] * __builtin_amdgcn_rcpf(lh) : 0.0f;
+        } else {
+          rec_store<STEP>(a.part_o + ((row0 + h) * a.C + c) * D + d, o[r]);
+          if (d == 0) {
+            rec_store<STEP>(a.part_m + (row0 + h) * a.C + c, mh * kLn2);
+            rec_store<STEP>(a.part_l + (row0 + h) * a.C + c, lh);
+          }
         }
       }
     }
+  }
+  if constexpr (STEP) {
+    if (a.part_o != nullptr && arrive_last(a.counters + bg, a.C, &arrive_flag)) merge_rows<G>(a, row0, bg);
   }
 }
 
@@ -647,22 +927,8 @@ __global__ __launch_bounds__(128) void reduce_kernel(ReduceArgs a) {
   constexpr int D = 128;
   const int64_t row = blockIdx.x;
   const int d = threadIdx.x;
-  const float* pm = a.part_m + row * a.C;
-  const float* pl = a.part_l + row * a.C;
-  const float* po = a.part_o + row * a.C * D + d;
-  float m_star = -INFINITY;
-  for (int c = 0; c < a.C; ++c) m_star = fmaxf(m_star, pm[c]);
-  float num = 0.0f, den = 0.0f;
-  if (m_star != -INFINITY) {
-    for (int c = 0; c < a.C; ++c) {
-      const float mc = pm[c];
-      if (mc == -INFINITY) continue;
-      const float w = fast_exp2((mc - m_star) * kLog2e);
-      num = fmaf(w, po[int64_t(c) * D], num);
-      den = fmaf(w, pl[c], den);
-    }
-  }
-  a.out[row * D + d] = den > 0.0f ? num / den : 0.0f;
+  a.out[row * D + d] = merge_chunks(a.part_m + row * a.C, a.part_l + row * a.C,
+                                    a.part_o + row * a.C * D + d, a.C, D);
 }
 
 }  // namespace pqattn

@@ -22,11 +22,9 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
-#include "decode_kernel.hpp"   // f16x4, f32x4, DPP helpers
+#include "decode_kernel.hpp"   // f16x4, f32x4, DPP and argmax helpers
 
 namespace pqattn {
-
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxEncodePlanes = 4;
 
@@ -41,21 +39,6 @@ struct EncodeArgs {
   int64_t codes_bytes;       // writes outside [0, codes_bytes) are skipped
   int64_t sxv, sxh, scs, sch;
 };
-
-template <int CTRL>
-__device__ __forceinline__ int dpp_int(int v) {
-  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
-}
-
-// (score, index) -> the better of the pair and its DPP partner.
-template <int CTRL>
-__device__ __forceinline__ void argmax_step(float& s, int& k) {
-  const float os = dpp_f<CTRL>(s);
-  const int ok = dpp_int<CTRL>(k);
-  const bool take = (os > s) || (os == s && ok < k);
-  s = take ? os : s;
-  k = take ? ok : k;
-}
 
 template <int M, int NV>
 __global__ __launch_bounds__(64 * M) void encode_kernel(EncodeArgs a) {
@@ -109,19 +92,7 @@ __global__ __launch_bounds__(64 * M) void encode_kernel(EncodeArgs a) {
   // four lanes l16, l16+16, l16+32, l16+48 that share the codeword
   float cinit[NCT];
 #pragma unroll
-  for (int nt = 0; nt < NCT; ++nt) {
-    float p = 0.0f;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const f16x2 lo = {bop[nt][s][0], bop[nt][s][1]};
-      const f16x2 hi = {bop[nt][s][2], bop[nt][s][3]};
-      p = __builtin_amdgcn_fdot2(lo, lo, p, false);
-      p = __builtin_amdgcn_fdot2(hi, hi, p, false);
-    }
-    p += __shfl_xor(p, 16, 64);
-    p += __shfl_xor(p, 32, 64);
-    cinit[nt] = -0.5f * p;
-  }
+  for (int nt = 0; nt < NCT; ++nt) cinit[nt] = neg_half_norm2<KS>(bop[nt]);
 
   // ---- scores, running argmax, row reduction ------------------------------
   for (int t = 0; t < NTILE; ++t) {

@@ -78,6 +78,14 @@ pq_status plan_attn(const pq_attn_desc* d, AttnPlan* p) {
     p->ws_o_off = p->ws_l_off + round_up(n_stat * 4, 256);
     p->ws_bytes = p->ws_o_off + round_up(n_stat * size_t(p->D) * 4, 256);
   }
+  // decode step: the chunk records plus one arrival counter per (b, kv head)
+  if (p->C == 1) {
+    p->ws_cnt_off = 0;
+    p->ws_step_bytes = 0;
+  } else {
+    p->ws_cnt_off = p->ws_bytes;
+    p->ws_step_bytes = p->ws_cnt_off + round_up(size_t(p->B) * size_t(p->Hkv) * 4, 256);
+  }
   return PQ_OK;
 }
 

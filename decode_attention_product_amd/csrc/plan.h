@@ -22,6 +22,7 @@ struct AttnPlan {
   int64_t rows;         // B * Hq
   int64_t blocks;       // score-kernel workgroups, B * Hkv * C
   size_t ws_m_off, ws_l_off, ws_o_off, ws_bytes;   // workspace carve-up (C > 1)
+  size_t ws_cnt_off, ws_step_bytes;                // decode step: + arrival counters (C > 1)
 };
 
 // Checks *d and fills *p.  Returns PQ_OK, PQ_ERR_NULL, PQ_ERR_SHAPE or

@@ -119,6 +119,51 @@ pq_status pq_attn_partials_timed(const pq_attn_desc* desc, const void* q,
                                  float* part_m, float* part_l, float* part_o, void* stream,
                                  void* start_event, void* stop_event);
 
+/* Workspace pq_attn_decode_step needs: 0 when C == 1, else the chunk
+ * records of pq_attn_workspace_bytes() followed by one 32-bit arrival counter
+ * per (b, KV head), rounded up to 256-byte blocks.  0 for an invalid
+ * descriptor as well. */
+size_t pq_attn_step_workspace_bytes(const pq_attn_desc* desc);
+
+/* One decode step with the new token appended, in one kernel launch.  For
+ * every request b with lens[b] >= 1 and every KV head g, the new token's K
+ * and V (k_new[b][g], v_new[b][g]) are encoded by nearest codeword -- the
+ * same decisions pq_encode takes (AQPIM page, sections 3.1 and 5.2 (2)) --
+ * and written at slot t = lens[b] - 1 of k_codes and v_codes; out[b][h] is
+ * then what pq_attn_decode gives over the cache that now holds the token
+ * (scores from the lookup table, AQPIM page, section 4.1; chunked softmax
+ * and merge, PAM page, section 2.2.3).
+ *
+ *  k_new, v_new      fp16  [B][Hkv][D], 16-byte aligned
+ *  k_codes, v_codes  uint8 [B][Hkv][max_len][M]; only the new token's slots
+ *                    are written
+ *  lens              int32 [B]; counts the new token.  lens[b] = 0: nothing
+ *                    is written for b and its output is 0.  Clamped to
+ *                    [0, max_len] like pq_attn_decode's.
+ *  workspace         at least pq_attn_step_workspace_bytes(); may be NULL
+ *                    when that is 0.  When it is not 0 the buffer must be
+ *                    zero-filled before its first use (e.g. hipMemsetAsync);
+ *                    every call leaves it ready for the next one (its
+ *                    counters back at zero), and a call that returns a
+ *                    non-zero status does not touch it.  Two calls that may
+ *                    run at the same time need their own workspaces.
+ * Other arguments as for pq_attn_decode.  The workgroup whose chunk holds
+ * the new token encodes it; with C > 1 the last workgroup of each (b, KV
+ * head) to finish merges the chunk records into out. */
+pq_status pq_attn_decode_step(const pq_attn_desc* desc, const void* q, const void* k_new,
+                              const void* v_new, uint8_t* k_codes, uint8_t* v_codes,
+                              const void* k_cb, const void* v_cb, const int32_t* lens, float* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* pq_attn_decode_step for kernel timing: start_event and stop_event
+ * (hipEvent_t, either may be NULL) are stamped at the kernel's own start and
+ * end, as in pq_attn_partials_timed. */
+pq_status pq_attn_decode_step_timed(const pq_attn_desc* desc, const void* q, const void* k_new,
+                                    const void* v_new, uint8_t* k_codes, uint8_t* v_codes,
+                                    const void* k_cb, const void* v_cb, const int32_t* lens,
+                                    float* out, void* workspace, size_t workspace_bytes,
+                                    void* stream, void* start_event, void* stop_event);
+
 /* Merge chunk statistics (PAM page, section 2.2.3 (3); the rescaling of the
  * memory-wall chapter's online softmax, section 1.4.3 (5.1)):
  *   out[r] = sum_c w_c o[r][c] / sum_c w_c l[r][c],  w_c = exp(m[r][c] - max_c m[r][c])

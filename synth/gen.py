@@ -145,6 +145,16 @@ def make_inputs(w: Workload, rng: np.random.Generator, *, with_encode=True):
     return out
 
 
+def step_tokens(rng, k_cb, v_cb, batch, sigma=0.05):
+    """The K and V of the next token of every request for one decode step:
+    fp16 [B][Hkv][D] each, a random codeword per subspace plus
+    N(0, sigma^2) noise (as ``noisy_codewords``).  Returns
+    (x_k, src_k, x_v, src_v)."""
+    x_k, src_k = noisy_codewords(rng, k_cb, batch, sigma)
+    x_v, src_v = noisy_codewords(rng, v_cb, batch, sigma)
+    return x_k, src_k, x_v, src_v
+
+
 def workload_inputs(wid: int, replica: int = 0, *, with_encode=True):
     return make_inputs(WORKLOADS[wid], rng_for(wid, replica), with_encode=with_encode)
 

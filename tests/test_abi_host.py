@@ -125,6 +125,49 @@ def test_chunking_and_workspace_sizes(lib):
     assert 8 * 8 * C3 >= 256 and 8192 % C3 == 0
 
 
+def test_step_workspace_sizes(lib):
+    # records of pq_attn_workspace_bytes plus one 32-bit counter per (b, kv head)
+    d = _desc(batch=8, n_q_heads=64, n_kv_heads=8, n_sub=8, max_len=8192)
+    rec = lib.pq_attn_workspace_bytes(ctypes.byref(d))
+    step = lib.pq_attn_step_workspace_bytes(ctypes.byref(d))
+    assert rec > 0 and step >= rec + 8 * 8 * 4 and step <= rec + 8 * 8 * 4 + 256
+    assert step % 256 == 0
+    d1 = _desc(max_len=512, chunk=512)          # one chunk: no records, no counters
+    assert lib.pq_attn_step_workspace_bytes(ctypes.byref(d1)) == 0
+    assert lib.pq_attn_step_workspace_bytes(ctypes.byref(_desc(n_kv_heads=3))) == 0
+
+
+@pytest.mark.parametrize("which", range(9))
+def test_step_null_pointer(lib, which):
+    # q, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, out
+    ptrs = [FAKE] * 9
+    ptrs[which] = None
+    assert lib.pq_attn_decode_step(ctypes.byref(_desc()), *ptrs, FAKE, 1 << 30, None) == 1
+    assert lib.pq_attn_decode_step_timed(ctypes.byref(_desc()), *ptrs, FAKE, 1 << 30, None,
+                                         None, None) == 1
+
+
+def test_step_alignment_and_workspace(lib):
+    ptrs = [FAKE] * 9
+    ptrs[1] = FAKE + 8                           # k_new
+    assert lib.pq_attn_decode_step(ctypes.byref(_desc()), *ptrs, FAKE, 1 << 30, None) == 6
+    ptrs = [FAKE] * 9
+    ptrs[2] = FAKE + 2                           # v_new
+    assert lib.pq_attn_decode_step(ctypes.byref(_desc()), *ptrs, FAKE, 1 << 30, None) == 6
+    d = _desc(max_len=4096, chunk=256)
+    need = lib.pq_attn_step_workspace_bytes(ctypes.byref(d))
+    ptrs = [FAKE] * 9
+    assert lib.pq_attn_decode_step(ctypes.byref(d), *ptrs, None, need, None) == 4
+    assert lib.pq_attn_decode_step(ctypes.byref(d), *ptrs, FAKE, need - 1, None) == 4
+    # the record-only size is not enough for the step
+    rec = lib.pq_attn_workspace_bytes(ctypes.byref(d))
+    assert lib.pq_attn_decode_step(ctypes.byref(d), *ptrs, FAKE, rec, None) == 4
+    bad = _desc(n_q_heads=7)                     # not a multiple of n_kv_heads
+    assert lib.pq_attn_decode_step(ctypes.byref(bad), *ptrs, FAKE, need, None) == 2
+    odd = _desc(n_q_heads=6)                     # G = 3: consistent, not built
+    assert lib.pq_attn_decode_step(ctypes.byref(odd), *ptrs, FAKE, need, None) == 3
+
+
 def test_chunk_longer_than_a_workgroup_takes(lib):
     d = _desc(max_len=8192, chunk=4097)
     assert lib.pq_attn_num_chunks(ctypes.byref(d)) == -1

@@ -363,3 +363,143 @@ def test_encode_many_matches_single_calls():
     np.testing.assert_array_equal(got_k, oracle.encode(xk, kcb))
     np.testing.assert_array_equal(got_k, srck)
     np.testing.assert_array_equal(vc1.cpu().numpy()[np.arange(B), :, slots % L], srcv)
+
+
+# --------------------------------------------------------------------------
+# Decode step with the new token appended (one launch: encode + attend + merge)
+# --------------------------------------------------------------------------
+
+def step_expected(inp, xk, xv, lens):
+    """The cache after appending the new token at slot lens[b] - 1 (codes from
+    the oracle's encode) and the oracle's attention over it."""
+    exp_k, exp_v = inp["k_codes"].copy(), inp["v_codes"].copy()
+    ck, cv = oracle.encode(xk, inp["k_cb"]), oracle.encode(xv, inp["v_cb"])
+    L = exp_k.shape[2]
+    for b, l in enumerate(lens):
+        l = min(max(int(l), 0), L)
+        if l >= 1:
+            exp_k[b, :, l - 1] = ck[b]
+            exp_v[b, :, l - 1] = cv[b]
+    ref = oracle.decode_attention(inp["q"], exp_k, exp_v, inp["k_cb"], inp["v_cb"], lens)
+    return exp_k, exp_v, ref
+
+
+def run_step(inp, xk, xv, lens, chunk=0, ws=None):
+    q, kcb, vcb = dev(inp["q"]), dev(inp["k_cb"]), dev(inp["v_cb"])
+    kc, vc = dev(inp["k_codes"]), dev(inp["v_codes"])
+    desc = pq.attn_desc(q, kc, kcb, chunk=chunk)
+    if ws is None:
+        ws = pq.step_workspace(desc, q.device)
+    out = pq.pq_attn_decode_step(q, dev(xk), dev(xv), kc, vc, kcb, vcb, dev(np.asarray(lens, np.int32)),
+                                 desc=desc, workspace=ws)
+    torch.cuda.synchronize()
+    return desc, ws, kc.cpu().numpy(), vc.cpu().numpy(), out.cpu().numpy()
+
+
+def check_counters_zero(desc, ws):
+    if ws is None:
+        return
+    rec = pq.pq_attn_workspace_bytes(desc)
+    n = desc.batch * desc.n_kv_heads * 4
+    assert (ws[rec:rec + n] == 0).all(), "arrival counters not left at zero"
+
+
+def test_step_gqa_workload():
+    say("step on the gqa workload (B=8 Hq=64 Hkv=8 L=8192 M=8, library chunks): encode + attend + merge")
+    inp = gen.workload_inputs(3, with_encode=False)
+    xk, sk, xv, sv = gen.step_tokens(np.random.default_rng(3001), inp["k_cb"], inp["v_cb"], 8)
+    lens = inp["lens"]
+    desc, ws, kc, vc, out = run_step(inp, xk, xv, lens)
+    assert pq.pq_attn_num_chunks(desc) > 1
+    exp_k, exp_v, ref = step_expected(inp, xk, xv, lens)
+    np.testing.assert_array_equal(kc, exp_k)
+    np.testing.assert_array_equal(vc, exp_v)
+    np.testing.assert_array_equal(kc[np.arange(8), :, lens - 1], sk)
+    assert_attn_close(out, ref, "gqa step")
+    check_counters_zero(desc, ws)
+
+
+def test_step_matches_encode_then_decode():
+    """The fused step gives the codes of pq_encode_many and the output of
+    pq_attn_decode over the same cache."""
+    say("step vs encode_many + decode (tiny and page-sizing shapes)")
+    for wid, chunk in ((1, 0), (2, 256)):
+        inp = gen.workload_inputs(wid, with_encode=False)
+        B, Hkv, L, M = inp["k_codes"].shape
+        xk, _, xv, _ = gen.step_tokens(np.random.default_rng(3100 + wid), inp["k_cb"], inp["v_cb"], B)
+        lens = np.minimum(inp["lens"], L - 3)
+        desc, ws, kc, vc, out = run_step(inp, xk, xv, lens, chunk=chunk)
+        kc2, vc2 = dev(inp["k_codes"]), dev(inp["v_codes"])
+        edesc = pq.cache_encode_desc(B, B, Hkv, L, n_sub=M)
+        slots = dev(np.arange(B, dtype=np.int64) * Hkv * L + (lens.astype(np.int64) - 1))
+        pq.pq_encode_many([dev(xk), dev(xv)], [dev(inp["k_cb"]), dev(inp["v_cb"])], [kc2, vc2],
+                          slots=slots, desc=edesc)
+        out2 = pq.pq_attn_decode(dev(inp["q"]), kc2, vc2, dev(inp["k_cb"]), dev(inp["v_cb"]),
+                                 dev(lens), chunk=chunk)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(kc, kc2.cpu().numpy())
+        np.testing.assert_array_equal(vc, vc2.cpu().numpy())
+        _, _, ref = step_expected(inp, xk, xv, lens)
+        assert_attn_close(out, ref, f"step wid={wid}")
+        assert_attn_close(out, out2.cpu().numpy().astype(np.float64), f"step vs two calls wid={wid}")
+        check_counters_zero(desc, ws)
+
+
+STEP_EDGE = [
+    # (G, M, Lmax, chunk, lens): the new token at chunk starts and ends, empty requests
+    (8, 8, 4096, 1024, [1, 1024, 1025, 4096]),
+    (8, 4, 3072, 1024, [0, 2048, 2049, 3000]),
+    (4, 8, 2048, 512, [512, 513, 0, 7]),
+    (2, 4, 1024, 256, [256, 1, 1024, 300]),
+    (1, 8, 512, 0, [512, 1, 0, 255]),
+    (1, 4, 4096, 2048, [4096, 2048, 2049, 0]),
+]
+
+
+@pytest.mark.parametrize("G,M,Lmax,chunk,lens", STEP_EDGE)
+def test_step_edges(G, M, Lmax, chunk, lens):
+    say(f"step edge G={G} M={M} Lmax={Lmax} chunk={chunk} lens={lens}")
+    Hkv = 2
+    _, inp = gen.random_case(3200 + G * 10 + M, batch=len(lens), n_q_heads=G * Hkv,
+                             n_kv_heads=Hkv, max_len=Lmax, n_sub=M, lens=lens)
+    xk, _, xv, _ = gen.step_tokens(np.random.default_rng(3300 + G + M), inp["k_cb"], inp["v_cb"],
+                                   len(lens))
+    lens = np.asarray(lens, np.int32)
+    desc, ws, kc, vc, out = run_step(inp, xk, xv, lens, chunk=chunk)
+    exp_k, exp_v, ref = step_expected(inp, xk, xv, lens)
+    np.testing.assert_array_equal(kc, exp_k)
+    np.testing.assert_array_equal(vc, exp_v)
+    assert_attn_close(out, ref, f"step edge G={G} M={M}")
+    for b, l in enumerate(lens):
+        if l == 0:
+            assert (out[b] == 0).all()
+    check_counters_zero(desc, ws)
+
+
+def test_step_twice_reuses_workspace():
+    """Two consecutive steps through one workspace: the second appends after
+    the first and sees both new tokens."""
+    say("two steps, one workspace")
+    B, Hq, Hkv, L, M = 3, 16, 2, 2048, 8
+    _, inp = gen.random_case(3400, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, max_len=L, n_sub=M,
+                             lens=[1000, 2047, 3])
+    rng = np.random.default_rng(3401)
+    xk1, _, xv1, _ = gen.step_tokens(rng, inp["k_cb"], inp["v_cb"], B)
+    xk2, _, xv2, _ = gen.step_tokens(rng, inp["k_cb"], inp["v_cb"], B)
+    lens1 = inp["lens"].astype(np.int32)
+    lens2 = lens1 + 1
+    q, kcb, vcb = dev(inp["q"]), dev(inp["k_cb"]), dev(inp["v_cb"])
+    kc, vc = dev(inp["k_codes"]), dev(inp["v_codes"])
+    desc = pq.attn_desc(q, kc, kcb, chunk=512)
+    ws = pq.step_workspace(desc, q.device)
+    pq.pq_attn_decode_step(q, dev(xk1), dev(xv1), kc, vc, kcb, vcb, dev(lens1), desc=desc, workspace=ws)
+    out = pq.pq_attn_decode_step(q, dev(xk2), dev(xv2), kc, vc, kcb, vcb, dev(lens2), desc=desc,
+                                 workspace=ws)
+    torch.cuda.synchronize()
+    exp_k1, exp_v1, _ = step_expected(inp, xk1, xv1, lens1)
+    inp2 = dict(inp, k_codes=exp_k1, v_codes=exp_v1)
+    exp_k, exp_v, ref = step_expected(inp2, xk2, xv2, lens2)
+    np.testing.assert_array_equal(kc.cpu().numpy(), exp_k)
+    np.testing.assert_array_equal(vc.cpu().numpy(), exp_v)
+    assert_attn_close(out.cpu().numpy(), ref, "second step")
+    check_counters_zero(desc, ws)
