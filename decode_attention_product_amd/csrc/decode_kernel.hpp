@@ -390,6 +390,31 @@ __device__ __forceinline__ float neg_half_norm2(const f16x4 (&b)[KS]) {
   return -0.5f * p;
 }
 
+// neg_half_norm2 of N codewords at once: every lane's partial sums first,
+// then each round of cross-lane swaps for all N, so the swaps' latencies
+// overlap instead of chaining.  Same operations per codeword, same result.
+template <int KS, int N>
+__device__ __forceinline__ void neg_half_norm2_n(const f16x4 (*b)[KS], float (&out)[N]) {
+  float p[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    p[n] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const f16x2 lo = {b[n][s][0], b[n][s][1]};
+      const f16x2 hi = {b[n][s][2], b[n][s][3]};
+      p[n] = __builtin_amdgcn_fdot2(lo, lo, p[n], false);
+      p[n] = __builtin_amdgcn_fdot2(hi, hi, p[n], false);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < N; ++n) p[n] = pair_sum16(p[n]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) p[n] = pair_sum32(p[n]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) out[n] = -0.5f * p[n];
+}
+
 // The new token's codes from the per-wave argmax keys: waves m, m + M, ...
 // searched segment m's codewords.
 template <int M, int NW>
@@ -453,11 +478,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
 
   // Table and histogram live in separate LDS regions, so the histogram can be
   // cleared while the workgroup still waits for its operands.
-  // For G >= 2 the histogram is [k][R] 64-bit words, row r = m * GP + pair
-  // holding the bins of two heads: every row of a codeword sits on its own
-  // pair of banks whatever the codeword, so a wave whose lanes update
-  // different rows never conflicts (each lane walks the rows in a
-  // lane-rotated order).  For G = 1 it is [m][k] 32-bit words.
+  // For G >= 2 the histogram is [k][pair][m] 64-bit words (row r = pair * M
+  // + m, each word the bins of two heads): a row's banks do not depend on the
+  // codeword, so lanes that update different rows do not conflict.  The LDS
+  // takes a 64-bit atomic 16 lanes at a time over 32 banks, so 16 lanes must
+  // hit rows that differ mod 16; each lane walks the rows in a lane-rotated
+  // order that guarantees it (step 4).  For G = 1 it is [m][k] 32-bit words.
   constexpr int R = M * GP;                                                // rows per codeword
   constexpr int LUT_WORDS = M * K * G;
   constexpr int HIST_WORDS = G >= 2 ? K * R * 2 : M * K;
@@ -569,16 +595,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   // by the histogram, so it is found while the scores are gathered.
   float best_k = -INFINITY;
   int idx_k = 0;
+  float cnorm[STEP ? LUT_JOBS : 1];   // -|c|^2/2 of this lane's codeword per job, all first
+  if constexpr (STEP) {
+    if (has_new) {
+      neg_half_norm2_n<KSTEP_Q, LUT_JOBS>(ckb, cnorm);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < LUT_JOBS; ++i) {
     const int nt = wave / M + (NW / M) * i;
     const int k = nt * 16 + l16;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (STEP) {
-      if (has_new) {   // (all lanes: the norm sums across lanes)
-        const float cn = neg_half_norm2<KSTEP_Q>(ckb[i]);
-        if (q4 == kNewRow / 4) acc[0] = cn;
-      }
+      if (has_new && q4 == kNewRow / 4) acc[0] = cnorm[i];
     }
 #pragma unroll
     for (int s = 0; s < KSTEP_Q; ++s)
@@ -619,19 +648,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   }
 
   // step kernel: the V codebook in the table build's B layout, for the new
-  // token's V code (its latency overlaps the gathers below)
+  // token's V code.  Requested here so its latency overlaps the gathers
+  // below, except with four token slots per thread, where the registers
+  // are needed by the scores and it is requested after them.
   f16x4 cvl[STEP ? LUT_JOBS : 1][KSTEP_Q];
-  if constexpr (STEP) {
-    if (has_new) {
-      const __half* cvg_l = a.v_cb + int64_t(g) * M * K * DS;
+  auto load_cvl = [&]() {
+    const __half* cvg_l = a.v_cb + int64_t(g) * M * K * DS;
 #pragma unroll
-      for (int i = 0; i < LUT_JOBS; ++i) {
-        const int nt = wave / M + (NW / M) * i;
-        const __half* row = cvg_l + (int64_t(m_l) * K + nt * 16 + l16) * DS + 4 * q4;
+    for (int i = 0; i < LUT_JOBS; ++i) {
+      const int nt = wave / M + (NW / M) * i;
+      const __half* row = cvg_l + (int64_t(m_l) * K + nt * 16 + l16) * DS + 4 * q4;
 #pragma unroll
-        for (int s = 0; s < KSTEP_Q; ++s) cvl[i][s] = *reinterpret_cast<const f16x4*>(row + s * 16);
-      }
+      for (int s = 0; s < KSTEP_Q; ++s) cvl[i][s] = *reinterpret_cast<const f16x4*>(row + s * 16);
     }
+  };
+  constexpr bool kCvlEarly = NT <= 2;
+  if constexpr (STEP && kCvlEarly) {
+    if (has_new) load_cvl();
   }
 
   // ---- 2. scores --------------------------------------------------------------
@@ -649,18 +682,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
 
   if constexpr (STEP) {
     if (has_new) {   // the new token's V: same products as its K above, per-wave argmax
+      if constexpr (!kCvlEarly) load_cvl();
       float best_v = -INFINITY;
       int idx_v = 0;
+      // four jobs at a time: norms (cross-lane sums), products, then compares
+      constexpr int VB = NT >= 4 ? 2 : (LUT_JOBS < 4 ? LUT_JOBS : 4);
 #pragma unroll
-      for (int i = 0; i < LUT_JOBS; ++i) {
-        const int nt = wave / M + (NW / M) * i;
-        f32x4 accv = {0.f, 0.f, 0.f, 0.f};
-        const float cn = neg_half_norm2<KSTEP_Q>(cvl[i]);   // all lanes: sums across lanes
-        if (q4 == kNewRow / 4) accv[0] = cn;
+      for (int i0 = 0; i0 < LUT_JOBS; i0 += VB) {
+        float vn[VB];
+        neg_half_norm2_n<KSTEP_Q, VB>(cvl + i0, vn);
+        f32x4 accv[VB];
 #pragma unroll
-        for (int s = 0; s < KSTEP_Q; ++s)
-          accv = __builtin_amdgcn_mfma_f32_16x16x16f16(xv[s], cvl[i][s], accv, 0, 0, 0);
-        if (accv[0] > best_v) { best_v = accv[0]; idx_v = nt * 16 + l16; }
+        for (int j = 0; j < VB; ++j) {
+          accv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (q4 == kNewRow / 4) accv[j][0] = vn[j];
+#pragma unroll
+          for (int s = 0; s < KSTEP_Q; ++s)
+            accv[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(xv[s], cvl[i0 + j][s], accv[j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < VB; ++j) {   // ascending codewords: ties keep the lower
+          const int nt = wave / M + (NW / M) * (i0 + j);
+          if (accv[j][0] > best_v) { best_v = accv[j][0]; idx_v = nt * 16 + l16; }
+        }
       }
       argmax_step<kDppXor1>(best_v, idx_v); argmax_step<kDppXor2>(best_v, idx_v);
       argmax_step<kDppRor4>(best_v, idx_v); argmax_step<kDppRor8>(best_v, idx_v);
@@ -689,7 +733,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   for (int h = 0; h < G; ++h) m_c[h] = key_float(mkey[h]);
   if constexpr (STEP) {
     if (has_new) {   // the new token's V codes (per-wave keys written before the barrier above)
-      TokenCodes<M> nv = combine_new_codes<M, NW>(new_key[1]);
+      const TokenCodes<M> nv = combine_new_codes<M, NW>(new_key[1]);
       if (tid == 0) nv.store(a.v_codes + (bg * a.Lmax + t_new) * M);
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
@@ -697,7 +741,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
       }
     }
   }
-
   // V codebook operands of the contraction, requested once the scores are
   // in registers (earlier they would queue ahead of the table operands and
   // hold registers through the gathers).
@@ -725,21 +768,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
 
   // ---- 4. V histogram (fixed point, integer LDS atomics) -----------------------
   // Lane rotation (G >= 2): at step (jm, jp) a lane updates segment
-  // (jm + om) % M, om = lane % M, and head pair jp, or pair jp XOR GP/2 on
-  // lanes whose bit log2(M) is set.  The LDS serves 16 lanes of a 64-bit
-  // atomic together and is conflict-free when they hit 16 different rows:
-  // here 2M of them (all 16 for M = 8).  Codes are rotated once per token
-  // (one 64-bit funnel shift), pairs by one swap; the pair's row offset then
-  // splits into a per-lane base (below) and an immediate.
+  // (jm + om) % M, om = lane % M, and head pair jp, or pair jp XOR 1 on the
+  // lanes whose bit log2(M) is set.  With rows pair * M + m, the 16 lanes of
+  // a group then hit 2M rows that differ mod 16 (all 16 lanes for M = 8).
+  // Codes are rotated once per token (one 64-bit funnel shift), pairs by one
+  // swap of neighbours; the address is a per-lane base per segment plus an
+  // immediate per pair.
   const int om = lane & (M - 1);
   const bool swap_pairs = GP >= 2 && ((lane / M) & 1) != 0;
-  constexpr int GH = GP >= 2 ? GP / 2 : 1;   // pairs per half
-  // byte offset of the pair half [0, GH) of rotated segment jm; the half
-  // [GH, GP) is at row_lo ^ GH*8 (rows of a segment start 2*GH*8-aligned)
-  uint32_t row_lo[M];
+  // byte offset of rotated segment jm in the row of pair 0 (or pair 1 when
+  // swapping); pair 2q + b lives at (this ^ b*8M) + q*16M
+  uint32_t row_m[M];
 #pragma unroll
   for (int jm = 0; jm < M; ++jm)
-    row_lo[jm] = uint32_t(((jm + om) & (M - 1)) * GP * 8) + (swap_pairs ? GH * 8 : 0);
+    row_m[jm] = uint32_t(((jm + om) & (M - 1)) * 8) + (swap_pairs ? M * 8 : 0);
 
   float l_thr[G];
 #pragma unroll
@@ -760,28 +802,28 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
 #pragma unroll
         for (int pp = 0; pp < GP; ++pp)
           pv[pp] = __builtin_bit_cast(uint64_t, make_uint2(u[2 * pp], u[2 * pp + 1]));
-        if constexpr (GP >= 2) {   // pv[j] <- pv[(j + GP/2) % GP] on swapping lanes
+        if constexpr (GP >= 2) {   // pv[j] <- pv[j ^ 1] on swapping lanes
 #pragma unroll
-          for (int j = 0; j < GP / 2; ++j) {
-            const uint64_t x = pv[j], y = pv[j + GP / 2];
+          for (int j = 0; j < GP; j += 2) {
+            const uint64_t x = pv[j], y = pv[j + 1];
             pv[j] = swap_pairs ? y : x;
-            pv[j + GP / 2] = swap_pairs ? x : y;
+            pv[j + 1] = swap_pairs ? x : y;
           }
         }
         const TokenCodes<M> rc = vcode[i].rotated(om);
 #pragma unroll
         for (int jm = 0; jm < M; ++jm) {
-          const uint32_t code_off = uint32_t(rc.get(jm)) * (R * 8);
-          char* lo = hist_bytes + (code_off + row_lo[jm]);
+          const uint32_t b0 = uint32_t(rc.get(jm)) * (R * 8) + row_m[jm];
+          char* p0 = hist_bytes + b0;
+          if constexpr (GP == 1) {
+            atomicAdd(reinterpret_cast<unsigned long long*>(p0), (unsigned long long)pv[0]);
+          } else {
+            char* p1 = hist_bytes + (b0 ^ uint32_t(M * 8));
 #pragma unroll
-          for (int jp = 0; jp < GH; ++jp)
-            atomicAdd(reinterpret_cast<unsigned long long*>(lo + jp * 8), (unsigned long long)pv[jp]);
-          if constexpr (GP >= 2) {
-            char* hi = hist_bytes + (code_off + (row_lo[jm] ^ uint32_t(GH * 8)));
-#pragma unroll
-            for (int jp = 0; jp < GH; ++jp)
-              atomicAdd(reinterpret_cast<unsigned long long*>(hi + jp * 8),
-                        (unsigned long long)pv[GH + jp]);
+            for (int q = 0; q < GP / 2; ++q) {
+              atomicAdd(reinterpret_cast<unsigned long long*>(p0 + q * 16 * M), (unsigned long long)pv[2 * q]);
+              atomicAdd(reinterpret_cast<unsigned long long*>(p1 + q * 16 * M), (unsigned long long)pv[2 * q + 1]);
+            }
           }
         }
       } else {
@@ -829,7 +871,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
     for (int v = 0; v < 4; ++v) raw[st][v] = 0;
     if (hh < G) {
       if constexpr (G >= 2) {
-        const char* src = hist_bytes + (k0 * R + m_v * GP + (hh >> 1)) * 8 + (hh & 1) * 4;
+        const char* src = hist_bytes + (k0 * R + (hh >> 1) * M + m_v) * 8 + (hh & 1) * 4;
 #pragma unroll
         for (int v = 0; v < 4; ++v) raw[st][v] = *reinterpret_cast<const uint32_t*>(src + v * R * 8);
       } else {
