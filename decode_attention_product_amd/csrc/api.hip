@@ -281,7 +281,7 @@ pq_status encode_planes(const pq_encode_desc* desc, int32_t n, const void* const
   a.sch = desc->codes_stride_head;
   const void* fn = p.M == 4 ? reinterpret_cast<const void*>(&encode_kernel<4, kEncodeVectors>)
                             : reinterpret_cast<const void*>(&encode_kernel<8, kEncodeVectors>);
-  return launch(fn, dim3(unsigned(p.blocks_x), unsigned(p.H), unsigned(n)), dim3(64 * p.M), &a,
+  return launch(fn, dim3(unsigned(p.H), unsigned(p.blocks_x), unsigned(n)), dim3(128 * p.M), &a,
                 stream);
 }
 

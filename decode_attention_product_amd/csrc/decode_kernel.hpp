@@ -148,9 +148,29 @@ template <int CTRL>
 __device__ __forceinline__ void argmax_step(float& s, int& k) {
   const float os = dpp_f<CTRL>(s);
   const int ok = dpp_int<CTRL>(k);
-  const bool take = (os > s) || (os == s && ok < k);
+  // bitwise, not short-circuit: three compares and two mask operations, no
+  // branches
+  const bool take = (os > s) | ((os == s) & (ok < k));
   s = take ? os : s;
   k = take ? ok : k;
+}
+
+// The same across rows: lanes l and l ^ 16 (resp. l ^ 32) both end with the
+// better (score, index) of the two, taken from the lane-swap pair.
+__device__ __forceinline__ void argmax_pick(float& s, int& k, float s0, int k0, float s1, int k1) {
+  const bool one = (s1 > s0) | ((s1 == s0) & (k1 < k0));
+  s = one ? s1 : s0;
+  k = one ? k1 : k0;
+}
+__device__ __forceinline__ void argmax_pair16(float& s, int& k) {
+  const auto rs = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, s), __builtin_bit_cast(int, s), false, false);
+  const auto rk = __builtin_amdgcn_permlane16_swap(k, k, false, false);
+  argmax_pick(s, k, __builtin_bit_cast(float, int(rs[0])), int(rk[0]), __builtin_bit_cast(float, int(rs[1])), int(rk[1]));
+}
+__device__ __forceinline__ void argmax_pair32(float& s, int& k) {
+  const auto rs = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, s), __builtin_bit_cast(int, s), false, false);
+  const auto rk = __builtin_amdgcn_permlane32_swap(k, k, false, false);
+  argmax_pick(s, k, __builtin_bit_cast(float, int(rs[0])), int(rk[0]), __builtin_bit_cast(float, int(rs[1])), int(rk[1]));
 }
 
 // 64-bit key whose unsigned order is (score, then lower index): the integer

@@ -9,13 +9,16 @@
 // matrix-core instruction (fp16 inputs, exact products, fp32 sums) whose
 // accumulator starts at -|c|^2/2, so the scores come out ready to compare.
 //
-// Workgroup = one head and a tile of NV vectors; wave w handles segment
-// m = w, holding that segment's 256 codewords in registers as MFMA B
-// operands for the whole tile.  Lane (l16, q4) of an instruction's result
-// holds vectors 4*q4 .. 4*q4+3 against codeword nt*16 + l16; each lane keeps
-// a running best over the 16 codeword tiles, then the 16 lanes of a row
-// reduce (score, index) with DPP -- larger score, or equal score and lower
-// index, wins.
+// Workgroup = one head and a tile of NV vectors (grid: heads fastest, then
+// tiles, then planes), 2M waves: wave w handles segment m = w % M against
+// codeword half w / M (codewords 128*(w/M) .. +127), holding those 128
+// codewords in registers as MFMA B operands for the whole tile -- half the
+// registers of a whole codebook, so four waves fit on a SIMD.  Lane
+// (l16, q4) of an instruction's result holds vectors 4*q4 .. 4*q4+3
+// against codeword nt*16 + l16; each lane keeps a running best over its
+// half's 8 codeword tiles, the 16 lanes of a row reduce (score, index) with
+// DPP -- larger score, or equal score and lower index, wins -- and the two
+// halves meet in LDS as order-preserving 64-bit keys.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -41,29 +44,32 @@ struct EncodeArgs {
 };
 
 template <int M, int NV>
-__global__ __launch_bounds__(64 * M) void encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
   constexpr int D = 128;
   constexpr int K = 256;
   constexpr int DS = D / M;
   constexpr int KS = DS / 16;          // MFMA k-steps per segment
   constexpr int NTILE = NV / 16;       // 16-vector tiles
-  constexpr int NCT = K / 16;          // 16-codeword tiles
+  constexpr int NCT = K / 32;          // 16-codeword tiles per half
 
-  __shared__ __align__(16) uint8_t cs[NV * M];   // chosen codes [v][m]
+  // per (vector, segment, half): the half's best as an argmax key
+  __shared__ unsigned long long keys[NV][M][2];
 
   const int lane = threadIdx.x & 63;
-  const int m = threadIdx.x >> 6;      // this wave's segment
+  const int wave = threadIdx.x >> 6;
+  const int m = wave % M;              // this wave's segment
+  const int half = wave / M;           // and codeword half
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
-  const int h = blockIdx.y;
+  const int h = blockIdx.x;            // heads fastest: the heads of one vector row are read together
   const int plane = blockIdx.z;
   const __half* xp = a.x[plane];
   uint8_t* codes = a.codes[plane];
-  const int64_t n0 = int64_t(blockIdx.x) * NV;
+  const int64_t n0 = int64_t(blockIdx.y) * NV;
   const int nv = int(min<int64_t>(NV, a.N - n0));
 
-  // ---- codebook of (h, m) as MFMA B operands ------------------------------
-  const __half* cb = a.cb[plane] + (int64_t(h) * M + m) * K * DS;
+  // ---- this half of the codebook of (h, m) as MFMA B operands ----------------
+  const __half* cb = a.cb[plane] + (int64_t(h) * M + m) * K * DS + int64_t(half) * (K / 2) * DS;
   f16x4 bop[NCT][KS];
 #pragma unroll
   for (int nt = 0; nt < NCT; ++nt)
@@ -88,64 +94,72 @@ __global__ __launch_bounds__(64 * M) void encode_kernel(EncodeArgs a) {
   f16x4 acur[KS], anext[KS];
   load_a(0, acur);
 
-  // -|c|^2 / 2 of codeword nt*16 + l16: this lane's 4*KS elements, then the
-  // four lanes l16, l16+16, l16+32, l16+48 that share the codeword
-  float cinit[NCT];
+  // -|c|^2 / 2 of codeword nt*16 + l16 of this half (the B-operand layout),
+  // then, as the accumulator inputs of the transposed products below, lane
+  // (j, q4) needs those of codewords nt*16 + 4*q4 + r, r = 0..3
+  float cn[NCT];
+  neg_half_norm2_n<KS, NCT>(bop, cn);
+  f32x4 cinit[NCT];
 #pragma unroll
-  for (int nt = 0; nt < NCT; ++nt) cinit[nt] = neg_half_norm2<KS>(bop[nt]);
+  for (int nt = 0; nt < NCT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cinit[nt][r] = __shfl(cn[nt], 4 * q4 + r, 64);
 
-  // ---- scores, running argmax, row reduction ------------------------------
+  // ---- scores, running argmax, cross-row reduction ---------------------------
+  // Transposed products C[i = codeword][j = vector] (the codeword operands
+  // are the A side, the vectors the B side; same registers): lane (j, q4)
+  // holds vector j against codewords nt*16 + 4*q4 + r, so its running best
+  // walks codewords in ascending order within the lane, and the four rows
+  // q4 meet in two lane-swap steps.
+  const int kbase = half * (K / 2);
   for (int t = 0; t < NTILE; ++t) {
     if (t * 16 >= nv) break;           // uniform over the workgroup
     if (t + 1 < NTILE) load_a(t + 1, anext);
-    float best[4];
-    int bk[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) { best[r] = -INFINITY; bk[r] = l16; }
+    f32x4 acc[NCT];
 #pragma unroll
     for (int nt = 0; nt < NCT; ++nt) {
-      f32x4 acc = {cinit[nt], cinit[nt], cinit[nt], cinit[nt]};
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(bop[nt][0], acur[0], cinit[nt], 0, 0, 0);
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(acur[s], bop[nt][s], acc, 0, 0, 0);
+      for (int s = 1; s < KS; ++s)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(bop[nt][s], acur[s], acc[nt], 0, 0, 0);
+    }
+    float best = acc[0][0];
+    int bk = kbase + 4 * q4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool take = acc[r] > best[r];   // ascending codewords: ties keep the lower
-        best[r] = take ? acc[r] : best[r];
-        bk[r] = take ? nt * 16 + l16 : bk[r];
+    for (int nt = 0; nt < NCT; ++nt) {
+#pragma unroll
+      for (int r = (nt == 0 ? 1 : 0); r < 4; ++r) {
+        const bool take = acc[nt][r] > best;   // ascending codewords: ties keep the lower
+        best = take ? acc[nt][r] : best;
+        bk = take ? kbase + nt * 16 + 4 * q4 + r : bk;
       }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      argmax_step<kDppXor1>(best[r], bk[r]);
-      argmax_step<kDppXor2>(best[r], bk[r]);
-      argmax_step<kDppRor4>(best[r], bk[r]);
-      argmax_step<kDppRor8>(best[r], bk[r]);
-    }
-    if (l16 == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int v = t * 16 + 4 * q4 + r;
-        if (v < nv) cs[v * M + m] = uint8_t(bk[r]);
-      }
+    argmax_pair16(best, bk);   // rows q4 and q4 ^ 1
+    argmax_pair32(best, bk);   // rows q4 and q4 ^ 2
+    if (q4 == 0) {
+      const int v = t * 16 + l16;
+      if (v < nv) keys[v][m][half] = argmax_key(best, bk);
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) acur[s] = anext[s];
   }
   __syncthreads();
 
-  for (int v = threadIdx.x; v < nv; v += 64 * M) {
+  for (int v = threadIdx.x; v < nv; v += 128 * M) {
     const int64_t n = n0 + v;
     const int64_t s = a.slots ? a.slots[n] : n;
     if (s < 0 || (a.scs > 0 && s > a.codes_bytes / a.scs)) continue;
     const int64_t off = s * a.scs + int64_t(h) * a.sch;
     if (off < 0 || off + M > a.codes_bytes) continue;
-    uint8_t* dst = codes + off;
-    if constexpr (M == 4) {
-      *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(cs + v * M);
-    } else {
-      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(cs + v * M);
+    int code[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) {
+      const unsigned long long k0 = keys[v][j][0], k1 = keys[v][j][1];
+      code[j] = argmax_key_index(k1 > k0 ? k1 : k0);
     }
+    TokenCodes<M> tc;
+    tc.set(code);
+    tc.store(codes + off);
   }
 }
 

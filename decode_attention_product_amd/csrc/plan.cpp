@@ -110,7 +110,8 @@ pq_status plan_encode(const pq_encode_desc* d, int32_t vec_per_block, EncodePlan
   p->DS = d->head_dim / d->n_sub;
   p->K = d->n_codes;
   p->blocks_x = (d->n_vec + vec_per_block - 1) / vec_per_block;
-  if (p->blocks_x > kMaxBlocks || d->n_heads > 65535) return PQ_ERR_UNSUPPORTED;
+  // encode grid (H, tiles, planes): the tile count is a 16-bit y extent
+  if (p->blocks_x > kMaxGridYZ || d->n_heads > 65535) return PQ_ERR_UNSUPPORTED;
   return PQ_OK;
 }
 

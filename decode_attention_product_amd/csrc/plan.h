@@ -37,7 +37,7 @@ int32_t pick_chunk(int32_t B, int32_t Hkv, int32_t Lmax, int32_t target_blocks, 
 struct EncodePlan {
   int64_t N;
   int32_t H, D, M, DS, K;
-  int64_t blocks_x;     // vector tiles
+  int64_t blocks_x;     // vector tiles (grid y extent, at most 65535)
 };
 
 pq_status plan_encode(const pq_encode_desc* d, int32_t vec_per_block, EncodePlan* p);

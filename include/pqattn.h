@@ -199,7 +199,8 @@ typedef struct pq_encode_desc {
 /* Nearest-codeword encode (AQPIM page, sections 3.1 and 5.2 (2)): for every
  * vector n, head h and segment m, the index k minimising the squared
  * Euclidean distance between segment m of x[n][h] and codebook[h][m][k]; the
- * lowest index wins a tie.  Distances are decided in fp32.
+ * lowest index wins a tie.  Distances are decided in fp32.  Up to
+ * 65535 * 256 = 16,776,960 vectors per call (more: PQ_ERR_UNSUPPORTED).
  *  x         fp16  strided as above; rows 16-byte aligned
  *  codebook  fp16  [H][M][K][D/M]
  *  slots     int64 [N] destination token slot per vector, or NULL

@@ -86,6 +86,8 @@ int main() {
   e.n_vec = 100; e.x_stride_head = 12;  EXPECT(plan_encode(&e, 128, &ep) == PQ_ERR_ALIGN);
   e.x_stride_head = 128; e.codes_stride_slot = 6; EXPECT(plan_encode(&e, 128, &ep) == PQ_ERR_ALIGN);
   e.codes_stride_slot = 4; e.n_codes = 128; EXPECT(plan_encode(&e, 128, &ep) == PQ_ERR_UNSUPPORTED);
+  e.n_codes = 256; e.n_vec = int64_t(65535) * 256; EXPECT(plan_encode(&e, 256, &ep) == PQ_OK && ep.blocks_x == 65535);
+  e.n_vec += 1;       EXPECT(plan_encode(&e, 256, &ep) == PQ_ERR_UNSUPPORTED);
 
   // reduce
   EXPECT(check_reduce(10, 1, 128) == PQ_OK);

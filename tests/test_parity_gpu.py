@@ -503,3 +503,26 @@ def test_step_twice_reuses_workspace():
     np.testing.assert_array_equal(vc.cpu().numpy(), exp_v)
     assert_attn_close(out.cpu().numpy(), ref, "second step")
     check_counters_zero(desc, ws)
+
+
+def test_step_codes_equal_pq_encode_on_unstructured_vectors():
+    """The step kernel's in-kernel encode and pq_encode take the same
+    decisions even without generated margins: N(0, 1) vectors, whose nearest
+    codewords can be close calls, encoded both ways."""
+    say("step encode vs pq_encode on N(0,1) vectors (no margins)")
+    B, Hq, Hkv, L = 64, 64, 8, 256
+    for M in (4, 8):
+        _, inp = gen.random_case(3500 + M, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, max_len=L,
+                                 n_sub=M, lens=[L] * B)
+        rng = np.random.default_rng(3600 + M)
+        xk = rng.standard_normal((B, Hkv, 128), dtype=np.float32).astype(np.float16)
+        xv = rng.standard_normal((B, Hkv, 128), dtype=np.float32).astype(np.float16)
+        lens = np.full(B, L, np.int32)
+        _, _, kc, vc, _ = run_step(inp, xk, xv, lens, chunk=128)
+        ek = torch.empty((B, Hkv, M), dtype=torch.uint8, device="cuda")
+        ev = torch.empty((B, Hkv, M), dtype=torch.uint8, device="cuda")
+        pq.pq_encode(dev(xk), dev(inp["k_cb"]), ek)
+        pq.pq_encode(dev(xv), dev(inp["v_cb"]), ev)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(kc[:, :, L - 1], ek.cpu().numpy())
+        np.testing.assert_array_equal(vc[:, :, L - 1], ev.cpu().numpy())
