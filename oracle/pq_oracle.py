@@ -26,6 +26,11 @@ decision in float32, the precision the GPU kernel decides in):
 * Encode (AQPIM page, sections 3.1 and 5.2 (2)): per segment, the index of
   the codeword at the smallest squared Euclidean distance; the lowest index
   wins a tie.
+* Paged code cache (AQPIM page, section 5.1 (4): the index cache managed in
+  pages as in vLLM; PAM page, section 2.2.2 (2): paged KV management with a
+  global block table of where each token lives): token t of request b sits
+  in page block_table[b][t // P] at offset t % P.  Attention over it is the
+  same definition as above with the codes read through the table.
 
 Readings where the pages are silent (the scale 1/sqrt(D), lens = 0 gives a
 zero output, the head -> KV head map) are listed with the rest of the design
@@ -185,3 +190,52 @@ def encode(x, cb, block=4096):
                 d2 = np.einsum("nkj,nkj->nk", diff, diff)
                 codes[lo:hi, h, m] = np.argmin(d2, axis=1).astype(np.uint8)
     return codes
+
+
+def paged_slots(block_table, lens, b, page_tokens, max_len):
+    """Pool slots of tokens t < lens[b] of request b (PAM page, section
+    2.2.2 (2): a block table records where each token lives).
+
+    block_table int [B, max_pages]; page_tokens P.  Token t lives in page
+    block_table[b, t // P] at offset t % P, i.e. pool slot
+    block_table[b, t // P] * P + t % P.  Table entries past the request's
+    last token are never read.
+    """
+    L = _valid_len(lens, b, max_len)
+    t = np.arange(L)
+    pages = np.asarray(block_table[b], dtype=np.int64)[t // page_tokens]
+    return pages * page_tokens + t % page_tokens
+
+
+def decode_attention_paged(q, k_pool, v_pool, k_cb, v_cb, block_table, lens, page_tokens,
+                           scale=None):
+    """Single-token decode attention over a paged PQ code cache (AQPIM page,
+    sections 4 and 5.1 (4); PAM page, section 2.2.2 (2)).
+
+    q            fp16 [B, Hq, D]
+    k_pool       uint8 [Hkv, n_pages * P, M]: KV head g's pages side by side,
+                 page p holding slots p*P .. p*P + P - 1      (v_pool the same)
+    k_cb, v_cb   fp16 [Hkv, M, K, D/M]
+    block_table  int [B, max_pages]: page of each P-token block of request b
+    lens         int [B], clamped to [0, max_pages * P]
+    returns float64 [B, Hq, D]: softmax_t(scale q . K_t) V_t over t < lens[b],
+    K_t and V_t rebuilt from the codes at token t's slot; zeros for lens 0.
+    """
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[0]
+    G = Hq // Hkv
+    max_len = block_table.shape[1] * page_tokens
+    if scale is None:
+        scale = default_scale(D)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        slots = paged_slots(block_table, lens, b, page_tokens, max_len)
+        if slots.size == 0:
+            continue
+        for g in range(Hkv):
+            k_hat = reconstruct(k_pool[g, slots], k_cb[g])
+            v_hat = reconstruct(v_pool[g, slots], v_cb[g])
+            for h in range(g * G, (g + 1) * G):
+                p = attention_weights(q[b, h], k_hat, scale)
+                out[b, h] = p @ v_hat
+    return out

@@ -18,6 +18,10 @@ Workloads (one layer, one decode step each):
                 70/30 mix of the PAM page, section 4.1), H=32, M=4, with raw
                 K/V vectors for every prefill token (codeword + N(0, 0.1^2))
 
+Paged caches (``paged_cache``) hold the same codes in fixed-size pages of a
+per-head pool, in a seeded random page order, with a block table per
+request; unused table entries hold an out-of-range page id.
+
 Draw order per workload: k codebook, v codebook, k codes, v codes, q, then
 request order (ragged), then encode data.  Codebooks and q are fp16 drawn
 from N(0, 1); codes are uniform over 0..255.  Cache positions at or beyond
@@ -178,3 +182,36 @@ def random_case(seed, *, batch, n_q_heads, n_kv_heads, max_len, n_sub=4,
     if lens is not None:
         inp["lens"] = np.asarray(lens, dtype=np.int32)
     return w, inp
+
+
+def paged_cache(rng, k_codes, v_codes, lens, page_tokens, *, spare_pages=3, fill=-1):
+    """Scatter dense caches [B, Hkv, Lmax, M] into paged pools.
+
+    Request b needs ceil(lens[b] / P) pages.  Those pages are taken in a
+    seeded random order from a pool of (pages needed + spare_pages) pages;
+    page j of request b (tokens j*P .. j*P + P - 1) is copied into pool slots
+    page*P .. page*P + P - 1 of every KV head.  Pages nobody uses hold random
+    codes.  Table entries past a request's pages hold ``fill``.
+
+    Returns (k_pool, v_pool, block_table, n_pages) with pools uint8
+    [Hkv, n_pages * P, M] and block_table int32 [B, Lmax // P].
+    """
+    B, Hkv, Lmax, M = k_codes.shape
+    P = int(page_tokens)
+    assert Lmax % P == 0
+    max_pages = Lmax // P
+    need = [-(-int(min(max(int(x), 0), Lmax)) // P) for x in lens]
+    n_pages = sum(need) + int(spare_pages)
+    order = rng.permutation(n_pages)
+    k_pool = rng.integers(0, 256, size=(Hkv, n_pages * P, M), dtype=np.uint8)
+    v_pool = rng.integers(0, 256, size=(Hkv, n_pages * P, M), dtype=np.uint8)
+    table = np.full((B, max_pages), fill, dtype=np.int32)
+    nxt = 0
+    for b in range(B):
+        for j in range(need[b]):
+            page = int(order[nxt])
+            nxt += 1
+            table[b, j] = page
+            k_pool[:, page * P:(page + 1) * P] = k_codes[b, :, j * P:(j + 1) * P]
+            v_pool[:, page * P:(page + 1) * P] = v_codes[b, :, j * P:(j + 1) * P]
+    return k_pool, v_pool, table, n_pages

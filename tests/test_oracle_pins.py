@@ -409,3 +409,76 @@ def test_tiny_workload_shapes():
     assert out.shape == (1, 8, 128)
     assert np.isfinite(out).all()
     assert abs(oracle.default_scale(128) - 1 / math.sqrt(128)) < 1e-15
+
+
+# --------------------------------------------------------------------------
+# Paged code cache: the same attention with codes read through a block table
+# --------------------------------------------------------------------------
+
+_ATTN = ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")
+
+
+@pytest.mark.parametrize("P", [1, 4, 16])
+def test_paged_equals_dense_through_shuffled_pages(P):
+    """Pages scattered in random order by the generator and read back through
+    the table give exactly the dense cache's attention (ragged lens, an empty
+    request, a full one)."""
+    inp = _small(seed=60 + P, B=4, Hq=4, Hkv=2, L=48, lens=[48, 0, 17, 33])
+    dense = oracle.decode_attention(*(inp[k] for k in _ATTN))
+    kp, vp, table, _ = gen.paged_cache(np.random.default_rng(70 + P), inp["k_codes"],
+                                       inp["v_codes"], inp["lens"], P)
+    paged = oracle.decode_attention_paged(inp["q"], kp, vp, inp["k_cb"], inp["v_cb"],
+                                          table, inp["lens"], P)
+    np.testing.assert_array_equal(paged, dense)
+
+
+def test_paged_tiny_loops():
+    """B=1, H=1, M=2, K=4, D=4, P=2, 3 tokens in pages [3, 0] of a 4-page
+    pool, written as plain loops over the pool."""
+    rng = np.random.default_rng(80)
+    D, M, K, P = 4, 2, 4, 2
+    ds = D // M
+    kcb = rng.standard_normal((1, M, K, ds)).astype(np.float16)
+    vcb = rng.standard_normal((1, M, K, ds)).astype(np.float16)
+    q = rng.standard_normal((1, 1, D)).astype(np.float16)
+    kp = rng.integers(0, K, (1, 4 * P, M), dtype=np.uint8)
+    vp = rng.integers(0, K, (1, 4 * P, M), dtype=np.uint8)
+    table = np.array([[3, 0, 99]], dtype=np.int32)      # third entry unused
+    where = [6, 7, 0]                                    # token -> pool slot, by hand
+    scores = []
+    for t in range(3):
+        acc = 0.0
+        for d in range(D):
+            m, j = divmod(d, ds)
+            acc += float(q[0, 0, d]) * float(kcb[0, m, kp[0, where[t], m], j])
+        scores.append(acc / math.sqrt(D))
+    mx = max(scores)
+    w = [math.exp(s - mx) for s in scores]
+    expect = [0.0] * D
+    for t in range(3):
+        for d in range(D):
+            m, j = divmod(d, ds)
+            expect[d] += w[t] / sum(w) * float(vcb[0, m, vp[0, where[t], m], j])
+    got = oracle.decode_attention_paged(q, kp, vp, kcb, vcb, table, np.array([3]), P)
+    np.testing.assert_allclose(got[0, 0], expect, rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(oracle.paged_slots(table, np.array([3]), 0, P, 6), where)
+
+
+def test_paged_shared_page_and_unused_entries():
+    """Two requests may name the same page (a shared prefix); entries past a
+    request's last page are never read, whatever they hold."""
+    inp = _small(seed=81, B=2, Hq=2, Hkv=1, L=32, lens=[20, 9])
+    inp["k_codes"][1, :, :8] = inp["k_codes"][0, :, :8]   # request 1 shares request 0's first page
+    inp["v_codes"][1, :, :8] = inp["v_codes"][0, :, :8]
+    dense = oracle.decode_attention(*(inp[k] for k in _ATTN))
+    P = 8
+    kp = np.zeros((1, 5 * P, 4), np.uint8)
+    vp = np.zeros((1, 5 * P, 4), np.uint8)
+    table = np.array([[2, 4, 0, 2**31 - 1], [2, 1, -7, 12345]], dtype=np.int32)
+    for b, pages in ((0, [2, 4, 0]), (1, [2, 1])):
+        for j, page in enumerate(pages):
+            kp[0, page * P:(page + 1) * P] = inp["k_codes"][b, 0, j * P:(j + 1) * P]
+            vp[0, page * P:(page + 1) * P] = inp["v_codes"][b, 0, j * P:(j + 1) * P]
+    paged = oracle.decode_attention_paged(inp["q"], kp, vp, inp["k_cb"], inp["v_cb"], table,
+                                          inp["lens"], P)
+    np.testing.assert_array_equal(paged, dense)
