@@ -22,8 +22,9 @@ STATUS_NAMES = {0: "PQ_OK", 1: "PQ_ERR_NULL", 2: "PQ_ERR_SHAPE", 3: "PQ_ERR_UNSU
 
 EXPORTED = ("pq_attn_num_chunks", "pq_attn_workspace_bytes", "pq_attn_decode",
             "pq_attn_partials", "pq_attn_partials_timed", "pq_attn_step_workspace_bytes",
-            "pq_attn_decode_step", "pq_attn_decode_step_timed", "pq_attn_reduce", "pq_encode",
-            "pq_encode_many", "pq_status_string")
+            "pq_attn_decode_step", "pq_attn_decode_step_timed", "pq_attn_decode_paged",
+            "pq_attn_decode_step_paged", "pq_attn_decode_step_paged_timed", "pq_attn_reduce",
+            "pq_encode", "pq_encode_many", "pq_status_string")
 
 
 class PQError(RuntimeError):
@@ -46,6 +47,11 @@ class PQEncodeDesc(ctypes.Structure):
                 ("n_codes", ctypes.c_int32), ("x_stride_vec", ctypes.c_int64),
                 ("x_stride_head", ctypes.c_int64), ("codes_stride_slot", ctypes.c_int64),
                 ("codes_stride_head", ctypes.c_int64), ("codes_bytes", ctypes.c_int64)]
+
+
+class PQPageTable(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("page_tokens", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
 
 
 _lib = None
@@ -82,6 +88,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pq_attn_decode_step_timed.argtypes = [ctypes.POINTER(PQAttnDesc), P, P, P, P, P, P, P,
                                               P, P, P, ctypes.c_size_t, P, P, P]
     lib.pq_attn_decode_step_timed.restype = ctypes.c_int
+    PT = ctypes.POINTER(PQPageTable)
+    lib.pq_attn_decode_paged.argtypes = [ctypes.POINTER(PQAttnDesc), PT, P, P, P, P, P, P, P, P,
+                                         ctypes.c_size_t, P]
+    lib.pq_attn_decode_paged.restype = ctypes.c_int
+    lib.pq_attn_decode_step_paged.argtypes = [ctypes.POINTER(PQAttnDesc), PT, P, P, P, P, P, P,
+                                              P, P, P, P, ctypes.c_size_t, P]
+    lib.pq_attn_decode_step_paged.restype = ctypes.c_int
+    lib.pq_attn_decode_step_paged_timed.argtypes = [ctypes.POINTER(PQAttnDesc), PT, P, P, P, P,
+                                                    P, P, P, P, P, P, ctypes.c_size_t, P, P, P]
+    lib.pq_attn_decode_step_paged_timed.restype = ctypes.c_int
     lib.pq_attn_reduce.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
     lib.pq_attn_reduce.restype = ctypes.c_int
     lib.pq_encode.argtypes = [ctypes.POINTER(PQEncodeDesc), P, P, P, P, P]
@@ -267,6 +283,91 @@ def pq_attn_decode_step(q, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, out
     return out
 
 
+def paged_desc(q, k_pool, k_cb, block_table, page_tokens, *, chunk=0, scale=None):
+    """(attention descriptor, page table) from tensor shapes: q [B,Hq,D],
+    k_pool [Hkv, n_pages*P, M], block_table int32 [B, max_pages]."""
+    B, Hq, D = q.shape
+    Hkv, slots, M = k_pool.shape
+    P = int(page_tokens)
+    max_pages = block_table.shape[1]
+    desc = PQAttnDesc(B, Hq, Hkv, D, M, k_cb.shape[2], max_pages * P, int(chunk),
+                      float(scale if scale is not None else 1.0 / math.sqrt(D)))
+    table = PQPageTable(block_table.data_ptr(), P, max_pages, slots // P if P > 0 else 0)
+    return desc, table
+
+
+def _check_paged_inputs(desc, table, q, k_pool, v_pool, k_cb, v_cb, block_table, lens):
+    import torch
+    B, Hq, Hkv, D = desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim
+    M, K = desc.n_sub, desc.n_codes
+    P, n_pages = table.page_tokens, table.n_pages
+    _need(q, "q", torch.float16, (B, Hq, D))
+    _need(k_pool, "k_pool", torch.uint8, (Hkv, n_pages * P, M))
+    _need(v_pool, "v_pool", torch.uint8, (Hkv, n_pages * P, M))
+    _need(k_cb, "k_cb", torch.float16, (Hkv, M, K, D // M))
+    _need(v_cb, "v_cb", torch.float16, (Hkv, M, K, D // M))
+    _need(block_table, "block_table", torch.int32, (B, table.max_pages))
+    _need(lens, "lens", torch.int32, (B,))
+    if table.block_table != block_table.data_ptr():
+        raise ValueError("the page table does not point at block_table")
+
+
+def pq_attn_decode_paged(q, k_pool, v_pool, k_cb, v_cb, block_table, lens, out=None, *,
+                         page_tokens, chunk=0, scale=None, workspace=None, stream=None):
+    """Decode over a paged cache (C entry point pq_attn_decode_paged): pools
+    uint8 [Hkv, n_pages * P, M] (page p = slots p*P .. p*P + P - 1),
+    block_table int32 [B, max_pages].  Returns ``out`` fp32 [B, Hq, D]."""
+    import torch
+    desc, table = paged_desc(q, k_pool, k_cb, block_table, page_tokens, chunk=chunk, scale=scale)
+    _check_paged_inputs(desc, table, q, k_pool, v_pool, k_cb, v_cb, block_table, lens)
+    if out is None:
+        out = torch.empty((desc.batch, desc.n_q_heads, desc.head_dim), dtype=torch.float32,
+                          device=q.device)
+    _need(out, "out", torch.float32, (desc.batch, desc.n_q_heads, desc.head_dim))
+    ws_bytes = pq_attn_workspace_bytes(desc)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().pq_attn_decode_paged(
+        ctypes.byref(desc), ctypes.byref(table), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_cb),
+        _ptr(v_cb), _ptr(lens), _ptr(out), _ptr(workspace), nbytes, _stream(stream))
+    _check(st, "pq_attn_decode_paged")
+    return out
+
+
+def pq_attn_decode_step_paged(q, k_new, v_new, k_pool, v_pool, k_cb, v_cb, block_table, lens,
+                              out=None, *, page_tokens, chunk=0, scale=None, workspace=None,
+                              stream=None, events=None):
+    """Decode step over a paged cache (C entry point pq_attn_decode_step_paged):
+    encodes k_new/v_new [B, Hkv, D] into the slot of token lens[b] - 1 (its page
+    must be in block_table) and returns ``out`` (fp32 [B, Hq, D]).  Workspace
+    as for pq_attn_decode_step (from step_workspace(desc), zero-filled);
+    ``events=(start, stop)`` goes through pq_attn_decode_step_paged_timed."""
+    import torch
+    desc, table = paged_desc(q, k_pool, k_cb, block_table, page_tokens, chunk=chunk, scale=scale)
+    _check_paged_inputs(desc, table, q, k_pool, v_pool, k_cb, v_cb, block_table, lens)
+    shape_new = (desc.batch, desc.n_kv_heads, desc.head_dim)
+    _need(k_new, "k_new", torch.float16, shape_new)
+    _need(v_new, "v_new", torch.float16, shape_new)
+    if out is None:
+        out = torch.empty((desc.batch, desc.n_q_heads, desc.head_dim), dtype=torch.float32,
+                          device=q.device)
+    _need(out, "out", torch.float32, (desc.batch, desc.n_q_heads, desc.head_dim))
+    if workspace is None:
+        workspace = step_workspace(desc, q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load_library()
+    args = (ctypes.byref(desc), ctypes.byref(table), _ptr(q), _ptr(k_new), _ptr(v_new),
+            _ptr(k_pool), _ptr(v_pool), _ptr(k_cb), _ptr(v_cb), _ptr(lens), _ptr(out),
+            _ptr(workspace), nbytes, _stream(stream))
+    if events is None:
+        st = lib.pq_attn_decode_step_paged(*args)
+    else:
+        st = lib.pq_attn_decode_step_paged_timed(*args, events[0], events[1])
+    _check(st, "pq_attn_decode_step_paged")
+    return out
+
+
 def pq_attn_reduce(part_m, part_l, part_o, out=None, *, stream=None):
     """Merge chunk statistics (C entry point pq_attn_reduce).  part_m and
     part_l [..., C], part_o [..., C, D]; returns out [..., D] fp32."""
@@ -344,3 +445,15 @@ def cache_encode_desc(n_vec, batch, n_kv_heads, max_len, head_dim=128, n_sub=4, 
         x_stride_vec = n_kv_heads * head_dim
     return PQEncodeDesc(n_vec, n_kv_heads, head_dim, n_sub, n_codes, x_stride_vec, head_dim,
                         n_sub, max_len * n_sub, batch * n_kv_heads * max_len * n_sub)
+
+
+def paged_encode_desc(n_vec, n_kv_heads, n_pages, page_tokens, head_dim=128, n_sub=4,
+                      n_codes=256, x_stride_vec=None):
+    """Descriptor that writes the codes of x [N, Hkv, D] into paged pools
+    [Hkv, n_pages * P, M] at pool slots s = page * P + offset (pass them as the
+    slots tensor; the same slot in every KV head's pool)."""
+    if x_stride_vec is None:
+        x_stride_vec = n_kv_heads * head_dim
+    pool_head = n_pages * page_tokens * n_sub
+    return PQEncodeDesc(n_vec, n_kv_heads, head_dim, n_sub, n_codes, x_stride_vec, head_dim,
+                        n_sub, pool_head, n_kv_heads * pool_head)

@@ -21,33 +21,40 @@ constexpr int kEncodeVectors = 256;   // vectors per encode workgroup (one wave 
 
 using DecodeFn = void (*)(DecodeArgs);
 
-template <int G, int M, bool STEP>
+template <int G, int M, int NT, bool STEP, bool PAGED>
+DecodeFn kernel_for() {
+  if constexpr (PAGED) return &decode_paged_kernel<G, M, NT, STEP>;
+  else return &decode_partials_kernel<G, M, NT, STEP>;
+}
+
+template <int G, int M, bool STEP, bool PAGED>
 DecodeFn pick_nt(int T) {
-  if (T <= kDecodeThreads) return &decode_partials_kernel<G, M, 1, STEP>;
-  if (T <= 2 * kDecodeThreads) return &decode_partials_kernel<G, M, 2, STEP>;
-  if (T <= 4 * kDecodeThreads) return &decode_partials_kernel<G, M, 4, STEP>;
+  if (T <= kDecodeThreads) return kernel_for<G, M, 1, STEP, PAGED>();
+  if (T <= 2 * kDecodeThreads) return kernel_for<G, M, 2, STEP, PAGED>();
+  if (T <= 4 * kDecodeThreads) return kernel_for<G, M, 4, STEP, PAGED>();
   return nullptr;
 }
 
-template <bool STEP>
+template <bool STEP, bool PAGED>
 DecodeFn pick_gm(int G, int M, int T) {
   switch (M * 16 + G) {
-    case 4 * 16 + 1: return pick_nt<1, 4, STEP>(T);
-    case 4 * 16 + 2: return pick_nt<2, 4, STEP>(T);
-    case 4 * 16 + 4: return pick_nt<4, 4, STEP>(T);
-    case 4 * 16 + 8: return pick_nt<8, 4, STEP>(T);
-    case 8 * 16 + 1: return pick_nt<1, 8, STEP>(T);
-    case 8 * 16 + 2: return pick_nt<2, 8, STEP>(T);
-    case 8 * 16 + 4: return pick_nt<4, 8, STEP>(T);
-    case 8 * 16 + 8: return pick_nt<8, 8, STEP>(T);
+    case 4 * 16 + 1: return pick_nt<1, 4, STEP, PAGED>(T);
+    case 4 * 16 + 2: return pick_nt<2, 4, STEP, PAGED>(T);
+    case 4 * 16 + 4: return pick_nt<4, 4, STEP, PAGED>(T);
+    case 4 * 16 + 8: return pick_nt<8, 4, STEP, PAGED>(T);
+    case 8 * 16 + 1: return pick_nt<1, 8, STEP, PAGED>(T);
+    case 8 * 16 + 2: return pick_nt<2, 8, STEP, PAGED>(T);
+    case 8 * 16 + 4: return pick_nt<4, 8, STEP, PAGED>(T);
+    case 8 * 16 + 8: return pick_nt<8, 8, STEP, PAGED>(T);
   }
   return nullptr;
 }
 
-// The kernel instance for (G, M), the chunk length T (T <= kMaxChunk) and
-// the plain or decode-step variant.
-DecodeFn pick_decode(int G, int M, int T, bool step) {
-  return step ? pick_gm<true>(G, M, T) : pick_gm<false>(G, M, T);
+// The kernel instance for (G, M), the chunk length T (T <= kMaxChunk), the
+// plain or decode-step variant and the dense or paged cache.
+DecodeFn pick_decode(int G, int M, int T, bool step, bool paged) {
+  if (paged) return step ? pick_gm<true, true>(G, M, T) : pick_gm<false, true>(G, M, T);
+  return step ? pick_gm<true, false>(G, M, T) : pick_gm<false, false>(G, M, T);
 }
 
 // Launch; with events, the runtime stamps them at the kernel's own start and
@@ -77,9 +84,9 @@ pq_status launch_partials(const AttnPlan& p, const void* q, const uint8_t* kc, c
                           float* pl, float* po, float* out, hipStream_t stream,
                           hipEvent_t start = nullptr, hipEvent_t stop = nullptr,
                           const void* k_new = nullptr, const void* v_new = nullptr,
-                          uint32_t* counters = nullptr) {
+                          uint32_t* counters = nullptr, const PagePlan* pages = nullptr) {
   const bool step = k_new != nullptr;
-  DecodeArgs a;
+  DecodeArgs a{};
   a.q = static_cast<const __half*>(q);
   // the plain kernel never writes the code arrays
   a.k_codes = const_cast<uint8_t*>(kc);
@@ -100,7 +107,14 @@ pq_status launch_partials(const AttnPlan& p, const void* q, const uint8_t* kc, c
   a.T = p.T;
   a.C = p.C;
   a.qscale = p.scale * kLog2e;
-  DecodeFn fn = pick_decode(p.G, p.M, p.T, step);
+  if (pages != nullptr) {
+    a.block_table = pages->block_table;
+    a.pool_head_bytes = pages->pool_head_bytes;
+    a.page_shift = pages->shift;
+    a.max_pages = pages->max_pages;
+    a.n_pages = uint32_t(pages->n_pages);
+  }
+  DecodeFn fn = pick_decode(p.G, p.M, p.T, step, pages != nullptr);
   if (!fn) return PQ_ERR_UNSUPPORTED;
   return launch(reinterpret_cast<const void*>(fn), dim3(unsigned(p.Hkv), unsigned(p.C), unsigned(p.B)),
                 dim3(kDecodeThreads),
@@ -132,28 +146,49 @@ size_t pq_attn_workspace_bytes(const pq_attn_desc* desc) {
   return plan_attn(desc, &p) == PQ_OK ? p.ws_bytes : 0;
 }
 
-pq_status pq_attn_decode(const pq_attn_desc* desc, const void* q, const uint8_t* k_codes,
-                         const uint8_t* v_codes, const void* k_cb, const void* v_cb,
-                         const int32_t* lens, float* out, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+// pq_attn_decode over a dense cache (pages NULL) or a paged one.
+static pq_status attn_decode(const pq_attn_desc* desc, const pq_page_table* pages, const void* q,
+                             const uint8_t* k_codes, const uint8_t* v_codes, const void* k_cb,
+                             const void* v_cb, const int32_t* lens, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream, bool paged) {
   AttnPlan p;
   pq_status st = plan_attn(desc, &p);
   if (st != PQ_OK) return st;
+  PagePlan pg;
+  if (paged && (st = plan_pages(p, pages, &pg)) != PQ_OK) return st;
+  const PagePlan* pgp = paged ? &pg : nullptr;
   st = check_attn_pointers(q, k_codes, v_codes, k_cb, v_cb, lens);
   if (st != PQ_OK) return st;
   if (!out) return PQ_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.C == 1)
     return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, nullptr, nullptr, nullptr,
-                           out, s);
+                           out, s, nullptr, nullptr, nullptr, nullptr, nullptr, pgp);
   if (!workspace || workspace_bytes < p.ws_bytes || !aligned16(workspace)) return PQ_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   float* pm = reinterpret_cast<float*>(ws + p.ws_m_off);
   float* pl = reinterpret_cast<float*>(ws + p.ws_l_off);
   float* po = reinterpret_cast<float*>(ws + p.ws_o_off);
-  st = launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, pm, pl, po, nullptr, s);
+  st = launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, pm, pl, po, nullptr, s, nullptr,
+                       nullptr, nullptr, nullptr, nullptr, pgp);
   if (st != PQ_OK) return st;
   return launch_reduce(p.rows, p.C, pm, pl, po, out, s);
+}
+
+pq_status pq_attn_decode(const pq_attn_desc* desc, const void* q, const uint8_t* k_codes,
+                         const uint8_t* v_codes, const void* k_cb, const void* v_cb,
+                         const int32_t* lens, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return attn_decode(desc, nullptr, q, k_codes, v_codes, k_cb, v_cb, lens, out, workspace,
+                     workspace_bytes, stream, false);
+}
+
+pq_status pq_attn_decode_paged(const pq_attn_desc* desc, const pq_page_table* pages,
+                               const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                               const void* k_cb, const void* v_cb, const int32_t* lens, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_decode(desc, pages, q, k_pool, v_pool, k_cb, v_cb, lens, out, workspace,
+                     workspace_bytes, stream, true);
 }
 
 pq_status pq_attn_partials(const pq_attn_desc* desc, const void* q, const uint8_t* k_codes,
@@ -190,14 +225,19 @@ size_t pq_attn_step_workspace_bytes(const pq_attn_desc* desc) {
   return plan_attn(desc, &p) == PQ_OK ? p.ws_step_bytes : 0;
 }
 
+// The decode step over a dense cache (pages NULL, paged false) or a paged one.
 static pq_status decode_step(const pq_attn_desc* desc, const void* q, const void* k_new,
                              const void* v_new, uint8_t* k_codes, uint8_t* v_codes,
                              const void* k_cb, const void* v_cb, const int32_t* lens, float* out,
                              void* workspace, size_t workspace_bytes, void* stream,
-                             void* start_event, void* stop_event) {
+                             void* start_event, void* stop_event,
+                             const pq_page_table* pages = nullptr, bool paged = false) {
   AttnPlan p;
   pq_status st = plan_attn(desc, &p);
   if (st != PQ_OK) return st;
+  PagePlan pg;
+  if (paged && (st = plan_pages(p, pages, &pg)) != PQ_OK) return st;
+  const PagePlan* pgp = paged ? &pg : nullptr;
   st = check_attn_pointers(q, k_codes, v_codes, k_cb, v_cb, lens);
   if (st != PQ_OK) return st;
   if (!out || !k_new || !v_new) return PQ_ERR_NULL;
@@ -206,14 +246,14 @@ static pq_status decode_step(const pq_attn_desc* desc, const void* q, const void
   hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
   if (p.C == 1)
     return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, nullptr, nullptr, nullptr, out,
-                           s, e0, e1, k_new, v_new, nullptr);
+                           s, e0, e1, k_new, v_new, nullptr, pgp);
   if (!workspace || workspace_bytes < p.ws_step_bytes || !aligned16(workspace))
     return PQ_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens,
                          reinterpret_cast<float*>(ws + p.ws_m_off), reinterpret_cast<float*>(ws + p.ws_l_off),
                          reinterpret_cast<float*>(ws + p.ws_o_off), out, s, e0, e1, k_new, v_new,
-                         reinterpret_cast<uint32_t*>(ws + p.ws_cnt_off));
+                         reinterpret_cast<uint32_t*>(ws + p.ws_cnt_off), pgp);
 }
 
 pq_status pq_attn_decode_step(const pq_attn_desc* desc, const void* q, const void* k_new,
@@ -231,6 +271,25 @@ pq_status pq_attn_decode_step_timed(const pq_attn_desc* desc, const void* q, con
                                     void* stream, void* start_event, void* stop_event) {
   return decode_step(desc, q, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, out, workspace,
                      workspace_bytes, stream, start_event, stop_event);
+}
+
+pq_status pq_attn_decode_step_paged(const pq_attn_desc* desc, const pq_page_table* pages,
+                                    const void* q, const void* k_new, const void* v_new,
+                                    uint8_t* k_pool, uint8_t* v_pool, const void* k_cb,
+                                    const void* v_cb, const int32_t* lens, float* out,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_step(desc, q, k_new, v_new, k_pool, v_pool, k_cb, v_cb, lens, out, workspace,
+                     workspace_bytes, stream, nullptr, nullptr, pages, true);
+}
+
+pq_status pq_attn_decode_step_paged_timed(const pq_attn_desc* desc, const pq_page_table* pages,
+                                          const void* q, const void* k_new, const void* v_new,
+                                          uint8_t* k_pool, uint8_t* v_pool, const void* k_cb,
+                                          const void* v_cb, const int32_t* lens, float* out,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          void* start_event, void* stop_event) {
+  return decode_step(desc, q, k_new, v_new, k_pool, v_pool, k_cb, v_cb, lens, out, workspace,
+                     workspace_bytes, stream, start_event, stop_event, pages, true);
 }
 
 pq_status pq_attn_reduce(int64_t n_rows, int32_t n_chunks, int32_t head_dim, const float* part_m,

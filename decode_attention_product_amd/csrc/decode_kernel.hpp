@@ -1,8 +1,12 @@
 // Fused PQ decode-attention score kernel and chunk-merge kernel (gfx950).
 //
-// One workgroup of 512 threads owns one (request b, KV head g, chunk c) and
+// One workgroup of 1024 threads owns one (request b, KV head g, chunk c) and
 // the G query heads that share g (grouped-query attention, memory-wall
-// chapter section 1.4.3 (1)).  Steps:
+// chapter section 1.4.3 (1)).  The codes come from a dense cache
+// [B][Hkv][Lmax][M] or from a paged one (decode_paged_kernel): per-head
+// pools of P-token pages and a block table naming the page of every P
+// tokens of a request (AQPIM page, section 5.1 (4); PAM page, section
+// 2.2.2 (2)).  Steps:
 //
 //   0. The operands are requested in the order they are used: q and the K
 //      codebook (table build) before lens[b] is even waited for, then the
@@ -61,6 +65,14 @@ struct DecodeArgs {
                              // zero on entry, zero again on exit
   int32_t Hq, Hkv, Lmax, T, C;
   float qscale;              // scale * log2(e)
+  // Paged cache only: k_codes and v_codes are pools [Hkv][n_pages][P][M] and
+  // token t of request b lives at slot block_table[b][t >> page_shift] * P +
+  // (t & (P - 1)) of its KV head's pool.  Lmax = max_pages * P.
+  const int32_t* block_table;  // [B][max_pages]
+  int64_t pool_head_bytes;     // n_pages * P * M
+  int32_t page_shift;          // log2(P)
+  int32_t max_pages;
+  uint32_t n_pages;            // page ids are clamped to [0, n_pages)
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -478,8 +490,10 @@ __device__ __forceinline__ void split_f16(float v, _Float16& hi, _Float16& lo) {
 // (slot lens[b] - 1) encodes the token's K and V into the cache first, and
 // with C > 1 the last workgroup of each (request, KV head) merges the chunk
 // records into the output.
-template <int G, int M, int NT, bool STEP>
-__global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeArgs a) {
+// PAGED: the codes are read (and the new token's written) through the block
+// table of a paged cache.
+template <int G, int M, int NT, bool STEP, bool PAGED>
+__device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   constexpr int NTHR = kDecodeThreads;
   constexpr int D = 128;
   constexpr int K = 256;
@@ -535,6 +549,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   // What does not depend on lens[b] goes out before its value is waited for:
   // the query rows and the K codebook operands of the table build.
   int len = a.lens[b];
+  // paged cache: the page of each of this thread's token slots, requested
+  // with lens[b] (entries past the request's pages are loaded, never used)
+  int32_t page[PAGED ? NT : 1];
+  if constexpr (PAGED) {
+    const int32_t* row = a.block_table + int64_t(b) * a.max_pages;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int t = t_begin + i * NTHR + tid;
+      page[i] = t < a.Lmax ? row[t >> a.page_shift] : 0;
+    }
+  }
   const __half* ckg = a.k_cb + int64_t(g) * M * K * DS;
   // table build: wave w owns segment m_l = w % M and codeword tiles
   // nt = w / M + (NW / M) * i
@@ -589,16 +614,32 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   // step kernel: does this chunk hold the new token (slot lens[b] - 1)?
   const int t_new = STEP ? len - 1 : -1;
   const bool has_new = STEP && t_new >= t_begin && t_new < t_end;   // uniform
+  // this (b, KV head)'s codes: a row of the dense cache, or a head's pool
+  const int64_t code_base = PAGED ? int64_t(g) * a.pool_head_bytes : bg * a.Lmax * M;
+  uint8_t* const kc = a.k_codes + code_base;
+  uint8_t* const vc = a.v_codes + code_base;
+  // the slot of token t; pg is the table entry of its page (paged cache)
+  auto slot = [&](int t, int32_t pg) -> int64_t {
+    if constexpr (PAGED) {
+      const uint32_t p = min(uint32_t(pg), a.n_pages - 1u);
+      return (int64_t(p) << a.page_shift) | int64_t(t & ((1 << a.page_shift) - 1));
+    } else {
+      return t;
+    }
+  };
+  int32_t page_new = 0;   // step kernel, paged: the new token's page (thread 0)
+  if constexpr (STEP && PAGED) {
+    if (has_new && tid == 0) page_new = a.block_table[int64_t(b) * a.max_pages + (t_new >> a.page_shift)];
+  }
   // the chunk's K and V codes (only tokens below lens[b] are read)
-  const uint8_t* kc = a.k_codes + bg * a.Lmax * M;
-  const uint8_t* vc = a.v_codes + bg * a.Lmax * M;
   TokenCodes<M> kcode[NT], vcode[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     const int t = t_begin + i * NTHR + tid;
     if (t < t_end) {
-      kcode[i].load(kc + int64_t(t) * M);
-      vcode[i].load(vc + int64_t(t) * M);
+      const int64_t off = slot(t, PAGED ? page[i] : 0) * M;
+      kcode[i].load(kc + off);
+      vcode[i].load(vc + off);
     }
   }
 
@@ -659,7 +700,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   if constexpr (STEP) {
     if (has_new) {   // the new token's K codes: into the cache and into its slot's registers
       TokenCodes<M> nk = combine_new_codes<M, NW>(new_key[0]);
-      if (tid == 0) nk.store(a.k_codes + (bg * a.Lmax + t_new) * M);
+      if (tid == 0) nk.store(kc + slot(t_new, page_new) * M);
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         if (t_begin + i * NTHR + tid == t_new) kcode[i] = nk;
@@ -754,7 +795,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   if constexpr (STEP) {
     if (has_new) {   // the new token's V codes (per-wave keys written before the barrier above)
       const TokenCodes<M> nv = combine_new_codes<M, NW>(new_key[1]);
-      if (tid == 0) nv.store(a.v_codes + (bg * a.Lmax + t_new) * M);
+      if (tid == 0) nv.store(vc + slot(t_new, page_new) * M);
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         if (t_begin + i * NTHR + tid == t_new) vcode[i] = nv;
@@ -974,6 +1015,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeA
   if constexpr (STEP) {
     if (a.part_o != nullptr && arrive_last(a.counters + bg, a.C, &arrive_flag)) merge_rows<G>(a, row0, bg);
   }
+}
+
+// G query heads per KV head, M segments, NT token slots per thread, STEP as
+// above; the codes in a dense [B][Hkv][Lmax][M] cache.
+template <int G, int M, int NT, bool STEP>
+__global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeArgs a) {
+  score_chunk<G, M, NT, STEP, false>(a);
+}
+
+// The same over a paged cache (block table and per-head page pools).
+template <int G, int M, int NT, bool STEP>
+__global__ __launch_bounds__(kDecodeThreads) void decode_paged_kernel(DecodeArgs a) {
+  score_chunk<G, M, NT, STEP, true>(a);
 }
 
 // Merge of chunk statistics: one workgroup of D threads per row.

@@ -115,6 +115,26 @@ pq_status plan_encode(const pq_encode_desc* d, int32_t vec_per_block, EncodePlan
   return PQ_OK;
 }
 
+pq_status plan_pages(const AttnPlan& p, const pq_page_table* t, PagePlan* out) {
+  if (t == nullptr || out == nullptr || t->block_table == nullptr) return PQ_ERR_NULL;
+  const int32_t P = t->page_tokens;
+  if (P < kMinPageTokens || P > kMaxPageTokens || (P & (P - 1)) != 0) return PQ_ERR_SHAPE;
+  if (t->max_pages < 1 || t->n_pages < 1) return PQ_ERR_SHAPE;
+  if (int64_t(t->max_pages) * P != p.Lmax) return PQ_ERR_SHAPE;
+  // every pool offset (and Hkv pools side by side) must fit in 62 bits
+  const int64_t head_bytes = int64_t(t->n_pages) * P * p.M;
+  if (head_bytes > (int64_t(1) << 62) / p.Hkv) return PQ_ERR_SHAPE;
+  out->block_table = t->block_table;
+  out->P = P;
+  int shift = 0;
+  while ((1 << shift) < P) ++shift;
+  out->shift = shift;
+  out->max_pages = t->max_pages;
+  out->n_pages = t->n_pages;
+  out->pool_head_bytes = head_bytes;
+  return PQ_OK;
+}
+
 pq_status check_reduce(int64_t n_rows, int32_t n_chunks, int32_t head_dim) {
   if (n_rows < 0 || n_chunks < 1 || head_dim < 1) return PQ_ERR_SHAPE;
   if (head_dim != kHeadDim) return PQ_ERR_UNSUPPORTED;

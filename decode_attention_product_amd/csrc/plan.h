@@ -44,6 +44,20 @@ pq_status plan_encode(const pq_encode_desc* d, int32_t vec_per_block, EncodePlan
 
 pq_status check_reduce(int64_t n_rows, int32_t n_chunks, int32_t head_dim);
 
+// A checked paged-cache description for an attention plan.
+struct PagePlan {
+  const int32_t* block_table;
+  int32_t P, shift, max_pages, n_pages;
+  int64_t pool_head_bytes;   // n_pages * P * M: one KV head's pool
+};
+
+// Checks *t against the plan (max_len == max_pages * page_tokens, page_tokens
+// a power of two in [kMinPageTokens, kMaxPageTokens]) and fills *out.
+// Returns PQ_OK, PQ_ERR_NULL or PQ_ERR_SHAPE.  Never touches the GPU.
+constexpr int kMinPageTokens = 16;
+constexpr int kMaxPageTokens = 65536;
+pq_status plan_pages(const AttnPlan& p, const pq_page_table* t, PagePlan* out);
+
 inline bool aligned16(const void* ptr) {
   return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0;
 }

@@ -164,6 +164,62 @@ pq_status pq_attn_decode_step_timed(const pq_attn_desc* desc, const void* q, con
                                     float* out, void* workspace, size_t workspace_bytes,
                                     void* stream, void* start_event, void* stop_event);
 
+/* A paged code cache (AQPIM page, section 5.1 (4): the index cache kept in
+ * pages that grow and are reclaimed as in vLLM; PAM page, section 2.2.2 (2):
+ * a global block table records where every token lives).  Each of the K and
+ * V caches is a pool of pages per KV head:
+ *    pool  uint8 [Hkv][n_pages][page_tokens][M]
+ * and token t of request b lives in page block_table[b][t / page_tokens] at
+ * offset t % page_tokens.  Pages are shared by all KV heads of a request (one
+ * table row per request) and may be shared between requests (a common
+ * prefix).  In the pool of KV head g, token t's codes sit at slot
+ *    s = block_table[b][t / page_tokens] * page_tokens + t % page_tokens,
+ * so pq_encode with those slots, codes_stride_slot = M and codes_stride_head
+ * = n_pages * page_tokens * M writes a prefill straight into the pages. */
+typedef struct pq_page_table {
+  const int32_t* block_table; /* DEVICE int32 [B][max_pages]; entries for the
+                                 blocks below lens[b] must name pages in
+                                 [0, n_pages); later entries are never used.
+                                 An out-of-range entry is clamped into the
+                                 pool: no memory outside it is touched, but
+                                 the result is unspecified.                   */
+  int32_t page_tokens;        /* P: a power of two in [16, 65536]            */
+  int32_t max_pages;          /* table row length; the attention descriptor's
+                                 max_len must equal max_pages * page_tokens  */
+  int32_t n_pages;            /* pages per KV head in each pool, >= 1        */
+} pq_page_table;
+
+/* pq_attn_decode over a paged cache: out[b][h] is exactly what pq_attn_decode
+ * gives for a dense cache holding, at token t of (b, g), the codes the table
+ * names.  k_pool and v_pool are uint8 [Hkv][n_pages][P][M], 16-byte aligned;
+ * pages is a host pointer read during the call.  Workspace as for
+ * pq_attn_decode with the same descriptor.  A NULL pages or block_table is
+ * PQ_ERR_NULL; a page size or table shape outside the rules above is
+ * PQ_ERR_SHAPE. */
+pq_status pq_attn_decode_paged(const pq_attn_desc* desc, const pq_page_table* pages,
+                               const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                               const void* k_cb, const void* v_cb, const int32_t* lens, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* pq_attn_decode_step over a paged cache: the new token's K and V codes go to
+ * the slot of token lens[b] - 1 (its page must already be in the table), and
+ * out is pq_attn_decode_paged's over the cache that now holds the token.
+ * Workspace (zero-filled before first use) as for pq_attn_decode_step. */
+pq_status pq_attn_decode_step_paged(const pq_attn_desc* desc, const pq_page_table* pages,
+                                    const void* q, const void* k_new, const void* v_new,
+                                    uint8_t* k_pool, uint8_t* v_pool, const void* k_cb,
+                                    const void* v_cb, const int32_t* lens, float* out,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* pq_attn_decode_step_paged with kernel-stamped events, as in
+ * pq_attn_partials_timed. */
+pq_status pq_attn_decode_step_paged_timed(const pq_attn_desc* desc, const pq_page_table* pages,
+                                          const void* q, const void* k_new, const void* v_new,
+                                          uint8_t* k_pool, uint8_t* v_pool, const void* k_cb,
+                                          const void* v_cb, const int32_t* lens, float* out,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          void* start_event, void* stop_event);
+
 /* Merge chunk statistics (PAM page, section 2.2.3 (3); the rescaling of the
  * memory-wall chapter's online softmax, section 1.4.3 (5.1)):
  *   out[r] = sum_c w_c o[r][c] / sum_c w_c l[r][c],  w_c = exp(m[r][c] - max_c m[r][c])

@@ -89,6 +89,35 @@ int main() {
   e.n_codes = 256; e.n_vec = int64_t(65535) * 256; EXPECT(plan_encode(&e, 256, &ep) == PQ_OK && ep.blocks_x == 65535);
   e.n_vec += 1;       EXPECT(plan_encode(&e, 256, &ep) == PQ_ERR_UNSUPPORTED);
 
+  // paged cache
+  {
+    pq_attn_desc pd = base();              // max_len 8192
+    AttnPlan pp;
+    EXPECT(plan_attn(&pd, &pp) == PQ_OK);
+    int32_t dummy = 0;
+    pq_page_table t{&dummy, 256, 32, 1000};
+    PagePlan pg;
+    EXPECT(plan_pages(pp, &t, &pg) == PQ_OK && pg.shift == 8 && pg.P == 256);
+    EXPECT(pg.pool_head_bytes == int64_t(1000) * 256 * 8);
+    t.page_tokens = 16; t.max_pages = 512;
+    EXPECT(plan_pages(pp, &t, &pg) == PQ_OK && pg.shift == 4);
+    t.page_tokens = 65536; t.max_pages = 1;   // one page longer than the cache: shape
+    EXPECT(plan_pages(pp, &t, &pg) == PQ_ERR_SHAPE);
+    t.page_tokens = 8192; t.max_pages = 1;
+    EXPECT(plan_pages(pp, &t, &pg) == PQ_OK && pg.shift == 13);
+    t.page_tokens = 96; t.max_pages = 85;     // not a power of two
+    EXPECT(plan_pages(pp, &t, &pg) == PQ_ERR_SHAPE);
+    t.page_tokens = 8; t.max_pages = 1024;    // below the minimum
+    EXPECT(plan_pages(pp, &t, &pg) == PQ_ERR_SHAPE);
+    t.page_tokens = 256; t.max_pages = 32; t.n_pages = 0;
+    EXPECT(plan_pages(pp, &t, &pg) == PQ_ERR_SHAPE);
+    t.n_pages = std::numeric_limits<int32_t>::max();   // 2^31 pages of 2 KB per head still fit
+    EXPECT(plan_pages(pp, &t, &pg) == PQ_OK && pg.pool_head_bytes == int64_t(t.n_pages) * 256 * 8);
+    t.block_table = nullptr;
+    EXPECT(plan_pages(pp, &t, &pg) == PQ_ERR_NULL);
+    EXPECT(plan_pages(pp, nullptr, &pg) == PQ_ERR_NULL);
+  }
+
   // reduce
   EXPECT(check_reduce(10, 1, 128) == PQ_OK);
   EXPECT(check_reduce(10, 0, 128) == PQ_ERR_SHAPE);

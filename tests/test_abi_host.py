@@ -240,3 +240,65 @@ def test_plan_unit_with_sanitizers(tmp_path):
                        env={**os.environ, "ASAN_OPTIONS": "detect_leaks=1"})
     assert r.returncode == 0, r.stdout + r.stderr
     assert "plan_unit: all" in r.stdout
+
+
+def _pages(**kw):
+    t = dict(block_table=FAKE, page_tokens=16, max_pages=4, n_pages=9)
+    t.update(kw)
+    return pq.PQPageTable(**t)
+
+
+def test_paged_null_and_shape_checks(lib):
+    d = _desc()                                  # max_len 64 = 4 pages of 16
+    ptrs = [FAKE] * 8                            # q, k_pool, v_pool, k_cb, v_cb, lens, out, ws
+    ok = _pages()
+    assert lib.pq_attn_decode_paged(ctypes.byref(d), None, *ptrs[:7], None, 0, None) == 1
+    assert lib.pq_attn_decode_paged(ctypes.byref(d), ctypes.byref(_pages(block_table=None)),
+                                    *ptrs[:7], None, 0, None) == 1
+    for bad in (_pages(page_tokens=24), _pages(page_tokens=8), _pages(page_tokens=1 << 17),
+                _pages(max_pages=3), _pages(n_pages=0), _pages(page_tokens=32)):
+        assert lib.pq_attn_decode_paged(ctypes.byref(d), ctypes.byref(bad), *ptrs[:7], None, 0,
+                                        None) == 2
+    for which in range(7):
+        p = list(ptrs[:7])
+        p[which] = None
+        assert lib.pq_attn_decode_paged(ctypes.byref(d), ctypes.byref(ok), *p, FAKE, 1 << 30,
+                                        None) == 1
+    p = list(ptrs[:7])
+    p[1] = FAKE + 4                              # k_pool
+    assert lib.pq_attn_decode_paged(ctypes.byref(d), ctypes.byref(ok), *p, FAKE, 1 << 30,
+                                    None) == 6
+    # four chunks of 16 tokens need records
+    d4 = _desc(chunk=16)
+    need = lib.pq_attn_workspace_bytes(ctypes.byref(d4))
+    assert need > 0
+    assert lib.pq_attn_decode_paged(ctypes.byref(d4), ctypes.byref(ok), *ptrs[:7], FAKE, need - 1,
+                                    None) == 4
+
+
+def test_paged_step_checks(lib):
+    d = _desc(chunk=16)
+    need = lib.pq_attn_step_workspace_bytes(ctypes.byref(d))
+    ptrs = [FAKE] * 10       # q, k_new, v_new, k_pool, v_pool, k_cb, v_cb, lens, out
+    ok = _pages()
+    for which in range(9):
+        p = list(ptrs[:9])
+        p[which] = None
+        assert lib.pq_attn_decode_step_paged(ctypes.byref(d), ctypes.byref(ok), *p, FAKE, need,
+                                             None) == 1
+        assert lib.pq_attn_decode_step_paged_timed(ctypes.byref(d), ctypes.byref(ok), *p, FAKE,
+                                                   need, None, None, None) == 1
+    assert lib.pq_attn_decode_step_paged(ctypes.byref(d), ctypes.byref(_pages(max_pages=5)),
+                                         *ptrs[:9], FAKE, need, None) == 2
+    assert lib.pq_attn_decode_step_paged(ctypes.byref(d), ctypes.byref(ok), *ptrs[:9], FAKE,
+                                         need - 1, None) == 4
+    p = list(ptrs[:9])
+    p[2] = FAKE + 2                              # v_new
+    assert lib.pq_attn_decode_step_paged(ctypes.byref(d), ctypes.byref(ok), *p, FAKE, need,
+                                         None) == 6
+
+
+def test_paged_encode_desc_matches_pool_layout():
+    d = pq.paged_encode_desc(10, n_kv_heads=3, n_pages=7, page_tokens=16, n_sub=8)
+    assert d.codes_stride_slot == 8 and d.codes_stride_head == 7 * 16 * 8
+    assert d.codes_bytes == 3 * 7 * 16 * 8
