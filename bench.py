@@ -146,6 +146,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--no-encode", action="store_true", help="skip the prefill-encode leg")
     ap.add_argument("--encode-reps", type=int, default=5)
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache leg")
+    ap.add_argument("--paged-steps", type=int, default=500)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run 3 device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -292,11 +294,126 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         result["copy_probe_bytes"] = n
+    if not args.no_paged:
+        result["paged"] = paged_leg(pq, torch, dev, args.paged_steps, args.warmup,
+                                    step_ms_plain * 1e3 if wid == 3 else None)
     if not args.no_encode:
         result["encode"] = encode_leg(pq, torch, dev, args.encode_reps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wid)
     print(json.dumps(result), flush=True)
+
+
+def to_pages(torch, dense, lens, P, perm):
+    """Device gather of a dense code cache [B, Hkv, L, M] into a pool
+    [Hkv, n_pages * P, M] of P-token pages: the used pages of every request,
+    in the physical order `perm` (logical page i -> physical page perm[i]).
+    Returns (pool, block_table int32 [B, L // P], n_pages); table entries
+    past a request's pages hold -1."""
+    B, Hkv, L, M = dense.shape
+    need = [-(-int(x) // P) for x in lens]
+    n_pages = sum(need)
+    table = np.full((B, L // P), -1, dtype=np.int32)
+    src = np.empty(n_pages * P, dtype=np.int64)
+    i = 0
+    for b in range(B):
+        for j in range(need[b]):
+            page = int(perm[i])
+            table[b, j] = page
+            src[page * P:(page + 1) * P] = b * L + j * P + np.arange(P)
+            i += 1
+    flat = dense.permute(1, 0, 2, 3).reshape(Hkv, B * L, M)
+    pool = flat[:, torch.from_numpy(src).to(dense.device)].contiguous()
+    return pool, torch.from_numpy(table).to(dense.device), n_pages
+
+
+def paged_leg(pq, torch, dev, steps, warmup, dense_gqa_us):
+    """Decode steps over paged code caches (256-token pages in a seeded
+    shuffled order), timed like the headline step: kernel-stamped events for
+    the kernel, plain back-to-back steps for the step time.
+      gqa     the headline workload on pages (paging overhead vs. dense)
+      ragged  64 requests of 512 or 4096 tokens, Lmax 4096: the paged and the
+              dense (padded) step on the same cache, and the capacity each
+              layout needs."""
+    from synth import gen
+    P = 256
+    stream = torch.cuda.current_stream()
+    res = {"page_tokens": P}
+    for name, wid in (("gqa", 3), ("ragged", 5)):
+        w = gen.WORKLOADS[wid]
+        B, Hq, Hkv, L, M, D = w.batch, w.n_q_heads, w.n_kv_heads, w.max_len, w.n_sub, w.head_dim
+        base = gen.workload_inputs(wid, with_encode=False)
+        lens_np = base["lens"]
+        alg = algorithmic_bytes(w, lens_np) + B * (L // P) * 4          # + the block table
+        R = max(2, math.ceil((512 << 20) / alg))
+        reps = []
+        for r in range(R):
+            inp = base if r == 0 else gen.workload_inputs(wid, replica=r, with_encode=False)
+            rng = np.random.default_rng([7100 + wid, r])
+            xk, _, xv, _ = gen.step_tokens(rng, inp["k_cb"], inp["v_cb"], B)
+            t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev)
+                 for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")}
+            t["xk"], t["xv"] = torch.from_numpy(xk).to(dev), torch.from_numpy(xv).to(dev)
+            n_used = sum(-(-int(x) // P) for x in inp["lens"])
+            perm = rng.permutation(n_used)
+            t["k_pool"], t["table"], n_pages = to_pages(torch, t["k_codes"], inp["lens"], P, perm)
+            t["v_pool"], _, _ = to_pages(torch, t["v_codes"], inp["lens"], P, perm)
+            if name == "gqa":       # only the pools are read in this leg
+                del t["k_codes"], t["v_codes"]
+            reps.append(t)
+        desc, _ = pq.paged_desc(reps[0]["q"], reps[0]["k_pool"], reps[0]["k_cb"], reps[0]["table"], P)
+        ws = pq.step_workspace(desc, dev)
+        ws_dense = pq.step_workspace(desc, dev)
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+
+        def paged(t, ev=None):
+            pq.pq_attn_decode_step_paged(t["q"], t["xk"], t["xv"], t["k_pool"], t["v_pool"], t["k_cb"],
+                                         t["v_cb"], t["table"], t["lens"], out, page_tokens=P,
+                                         workspace=ws, stream=stream, events=ev)
+
+        def dense(t):
+            pq.pq_attn_decode_step(t["q"], t["xk"], t["xv"], t["k_codes"], t["v_codes"], t["k_cb"],
+                                   t["v_cb"], t["lens"], out, desc=desc, workspace=ws_dense,
+                                   stream=stream)
+
+        def timed(fn):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for i in range(steps):
+                fn(reps[i % R])
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / steps
+
+        for i in range(warmup):
+            paged(reps[i % R])
+            if name == "ragged":
+                dense(reps[i % R])
+        hip = HipEvents()
+        raw = hip.create(2 * steps)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            paged(reps[i % R], (raw[2 * i], raw[2 * i + 1]))
+        torch.cuda.synchronize()
+        kern_us = float(np.mean([hip.elapsed_ms(raw[2 * i], raw[2 * i + 1]) for i in range(steps)])) * 1e3
+        hip.destroy(raw)
+        step_us = timed(paged)
+        tokens = int(lens_np.sum())
+        achieved = alg / (kern_us * 1e-6) / 1e9
+        leg = {"workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} Lmax={L} M={M}, {tokens} tokens",
+               "value": tokens / (step_us * 1e-6), "unit": "KV tokens/s", "step_us": step_us,
+               "kernel_us": kern_us, "replicas": R,
+               "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": alg,
+                            "kernel": "decode_paged_kernel (decode-step variant)"},
+               "pool_slots_per_head": n_pages * P, "padded_slots_per_head": B * L}
+        if name == "gqa" and dense_gqa_us is not None:
+            leg["dense_step_us"] = dense_gqa_us
+        if name == "ragged":
+            leg["dense_step_us"] = timed(dense)
+        res[name] = leg
+    return res
 
 
 def encode_leg(pq, torch, dev, reps):
