@@ -26,6 +26,14 @@ decision in float32, the precision the GPU kernel decides in):
 * Encode (AQPIM page, sections 3.1 and 5.2 (2)): per segment, the index of
   the codeword at the smallest squared Euclidean distance; the lowest index
   wins a tie.
+* Codebook learning (AQPIM page, section 3.2 (2): codebooks fitted online
+  to the first vectors of a sequence; section 5.2 (1): a fast K-means on a
+  small sample such as 32 vectors; section 6.1 (3): a few K-means updates
+  every so many tokens): Lloyd's algorithm per head and segment.  Each
+  iteration assigns every vector's segment to its nearest codeword (the
+  encode above), then moves every codeword that received vectors to their
+  mean -- the exact sum divided by the count in float64, rounded to the fp16
+  codebook; a codeword that received none keeps its value.
 * Paged code cache (AQPIM page, section 5.1 (4): the index cache managed in
   pages as in vLLM; PAM page, section 2.2.2 (2): paged KV management with a
   global block table of where each token lives): token t of request b sits
@@ -239,3 +247,44 @@ def decode_attention_paged(q, k_pool, v_pool, k_cb, v_cb, block_table, lens, pag
                 p = attention_weights(q[b, h], k_hat, scale)
                 out[b, h] = p @ v_hat
     return out
+
+
+def codebook_update(x, codes, cb):
+    """The update step of one Lloyd iteration for every head and segment
+    (AQPIM page, sections 3.2 (2), 5.2 (1) and 6.1 (3)).
+
+    x      fp16 [N, H, D]    the sample vectors
+    codes  uint8 [N, H, M]   their current assignment (nearest codewords)
+    cb     fp16 [H, M, K, ds]
+    returns (new codebook fp16 [H, M, K, ds], counts int64 [H, M, K]):
+    codeword k of (h, m) becomes the mean of the segments assigned to it,
+    math.fsum (the exactly rounded sum) divided by the count in float64 and
+    rounded to fp16; a codeword with no segment keeps its value.
+    """
+    N, H, D = x.shape
+    _, M, K, ds = cb.shape
+    new = cb.copy()
+    counts = np.zeros((H, M, K), dtype=np.int64)
+    x64 = x.astype(np.float64)
+    for h in range(H):
+        for m in range(M):
+            seg = x64[:, h, m * ds:(m + 1) * ds]
+            c = codes[:, h, m].astype(np.intp)
+            for k in np.unique(c):
+                members = seg[c == k]
+                n = members.shape[0]
+                counts[h, m, k] = n
+                mean = np.array([math.fsum(members[:, j]) / n for j in range(ds)])
+                new[h, m, k] = mean.astype(np.float16)
+    return new, counts
+
+
+def kmeans(x, cb_init, n_iter):
+    """n_iter Lloyd iterations from cb_init (assign with encode, then
+    codebook_update), then the assignment to the final codebook.
+
+    Returns (codebook fp16 [H, M, K, ds], codes uint8 [N, H, M])."""
+    cb = cb_init.copy()
+    for _ in range(int(n_iter)):
+        cb, _ = codebook_update(x, encode(x, cb), cb)
+    return cb, encode(x, cb)

@@ -215,3 +215,28 @@ def paged_cache(rng, k_codes, v_codes, lens, page_tokens, *, spare_pages=3, fill
             k_pool[:, page * P:(page + 1) * P] = k_codes[b, :, j * P:(j + 1) * P]
             v_pool[:, page * P:(page + 1) * P] = v_codes[b, :, j * P:(j + 1) * P]
     return k_pool, v_pool, table, n_pages
+
+
+def kmeans_case(rng, n_vec, n_heads, n_sub, *, n_codes=256, head_dim=128, sigma=0.05,
+                init_sigma=0.3, n_used=None):
+    """Inputs for codebook learning: a generating codebook (fp16 N(0,1)), a
+    sample of ``n_vec`` vectors per head drawn around its codewords (R12's
+    "codeword + noise", only the first ``n_used`` codewords of each segment
+    when given), and a starting codebook = generating codebook + iid
+    N(0, init_sigma^2), rounded to fp16.
+
+    Returns dict(x fp16 [N, H, D], src uint8 [N, H, M], cb_true, cb_init
+    fp16 [H, M, K, D/M])."""
+    ds = head_dim // n_sub
+    cb_true = codebooks(rng, n_heads, n_sub, n_codes, ds)
+    x, src = noisy_codewords(rng, cb_true, n_vec, sigma)
+    if n_used is not None:
+        src = (src.astype(np.int64) % int(n_used)).astype(np.uint8)
+        picked = cb_true[np.arange(n_heads)[None, :, None], np.arange(n_sub)[None, None, :],
+                         src.astype(np.intp)]
+        noise = rng.standard_normal((n_vec, n_heads, head_dim), dtype=np.float32) * np.float32(sigma)
+        x = (picked.reshape(n_vec, n_heads, head_dim).astype(np.float32) + noise).astype(np.float16)
+    cb_init = (cb_true.astype(np.float32)
+               + rng.standard_normal(cb_true.shape, dtype=np.float32) * np.float32(init_sigma)
+               ).astype(np.float16)
+    return {"x": x, "src": src, "cb_true": cb_true, "cb_init": cb_init}

@@ -482,3 +482,92 @@ def test_paged_shared_page_and_unused_entries():
     paged = oracle.decode_attention_paged(inp["q"], kp, vp, inp["k_cb"], inp["v_cb"], table,
                                           inp["lens"], P)
     np.testing.assert_array_equal(paged, dense)
+
+
+# --------------------------------------------------------------------------
+# Codebook learning: Lloyd iterations per head and segment
+# --------------------------------------------------------------------------
+
+def test_codebook_update_by_hand():
+    """H=1, M=1, D=2, K=4: means of hand-placed points, an empty codeword that
+    keeps its value, and a mean that needs rounding to fp16."""
+    x = np.array([[[0, 0]], [[0, 2]], [[10, 0]], [[10, 2]], [[5, 5]],
+                  [[1, 1]], [[2, 2]], [[2, 2]]], dtype=np.float16)
+    codes = np.array([0, 0, 1, 1, 3, 2, 2, 2], dtype=np.uint8).reshape(8, 1, 1)
+    cb = np.array([[[[0, 0], [9, 9], [7, 7], [6, 6]]]], dtype=np.float16)
+    new, counts = oracle.codebook_update(x[:5], codes[:5], cb)
+    np.testing.assert_array_equal(new[0, 0], np.array([[0, 1], [10, 1], [7, 7], [5, 5]], np.float16))
+    np.testing.assert_array_equal(counts[0, 0], [2, 2, 0, 1])
+    new, counts = oracle.codebook_update(x, codes, cb)
+    # (1 + 2 + 2) / 3 = 5/3 lies between fp16 neighbours 1706/1024 and 1707/1024 and nearer the second
+    assert float(new[0, 0, 2, 0]) == 1 + 683 / 1024
+    assert counts[0, 0, 2] == 3
+
+
+def _objective(x, cb, codes):
+    """Sum of squared distances of every segment to its codeword, in fp64."""
+    N, H, D = x.shape
+    _, M, K, ds = cb.shape
+    xs = x.astype(np.float64).reshape(N, H, M, ds)
+    c = cb.astype(np.float64)[np.arange(H)[None, :, None], np.arange(M)[None, None, :],
+                              codes.astype(np.intp)]
+    return float(((xs - c) ** 2).sum())
+
+
+def test_codebook_update_matches_sklearn_lloyd():
+    """One Lloyd iteration of scikit-learn's KMeans from the same start, per
+    (head, segment), on data where no cluster goes empty: the same labels
+    and, after rounding to fp16, centres within one fp16 step."""
+    skc = pytest.importorskip("sklearn.cluster")
+    rng = np.random.default_rng(90)
+    case = gen.kmeans_case(rng, 480, 2, 4, n_codes=16, sigma=0.2, init_sigma=0.3)
+    x, cb0 = case["x"], case["cb_init"]
+    codes = oracle.encode(x, cb0)
+    new, counts = oracle.codebook_update(x, codes, cb0)
+    assert (counts > 0).all()
+    ds = 32
+    for h in range(2):
+        for m in range(4):
+            pts = x[:, h, m * ds:(m + 1) * ds].astype(np.float64)
+            km = skc.KMeans(n_clusters=16, init=cb0[h, m].astype(np.float64), n_init=1, max_iter=1,
+                            algorithm="lloyd", tol=0.0).fit(pts)
+            sk_labels = np.argmin(((pts[:, None, :] - cb0[h, m].astype(np.float64)[None]) ** 2).sum(-1), 1)
+            np.testing.assert_array_equal(codes[:, h, m], sk_labels)
+            ref = km.cluster_centers_.astype(np.float16)
+            step = np.spacing(np.abs(ref)).astype(np.float64)
+            assert (np.abs(new[h, m].astype(np.float64) - ref.astype(np.float64)) <= step).all()
+
+
+def test_kmeans_lowers_the_objective_and_finds_the_generating_codebook():
+    rng = np.random.default_rng(91)
+    case = gen.kmeans_case(rng, 2048, 2, 8, n_codes=256, sigma=0.05, init_sigma=0.25, n_used=64)
+    x, cb = case["x"], case["cb_init"]
+    objs = [_objective(x, cb, oracle.encode(x, cb))]
+    for _ in range(4):
+        cb, codes = oracle.kmeans(x, cb, 1)
+        objs.append(_objective(x, cb, codes))
+    # each step lowers the objective, up to fp16 rounding of the centroids
+    rounding = x.shape[0] * x.shape[1] * 128 * 2e-3 * 2.0 ** -10
+    assert all(b <= a + rounding for a, b in zip(objs, objs[1:]))
+    assert objs[-1] < 0.5 * objs[0]
+    np.testing.assert_array_equal(codes, case["src"])
+    used = cb[:, :, :64].astype(np.float64)
+    assert np.abs(used - case["cb_true"][:, :, :64]).max() < 0.05
+    # codewords nobody chose keep their starting values
+    np.testing.assert_array_equal(cb[:, :, 64:], case["cb_init"][:, :, 64:])
+
+
+def test_kmeans_fixed_point_and_segment_independence():
+    """Vectors that are exactly codewords are a fixed point; swapping two
+    segments of the data and the codebook swaps the results."""
+    rng = np.random.default_rng(92)
+    case = gen.kmeans_case(rng, 300, 1, 4, n_codes=256, sigma=0.0, init_sigma=0.0, n_used=40)
+    cb, codes = oracle.kmeans(case["x"], case["cb_true"], 2)
+    np.testing.assert_array_equal(cb, case["cb_true"])
+    np.testing.assert_array_equal(codes, case["src"])
+    case = gen.kmeans_case(rng, 200, 1, 4, n_codes=256, sigma=0.1, init_sigma=0.3, n_used=30)
+    a_cb, a_codes = oracle.kmeans(case["x"], case["cb_init"], 2)
+    xs = case["x"].reshape(200, 1, 4, 32)[:, :, [1, 0, 2, 3]].reshape(200, 1, 128)
+    b_cb, b_codes = oracle.kmeans(xs, case["cb_init"][:, [1, 0, 2, 3]], 2)
+    np.testing.assert_array_equal(b_cb, a_cb[:, [1, 0, 2, 3]])
+    np.testing.assert_array_equal(b_codes, a_codes[:, :, [1, 0, 2, 3]])
