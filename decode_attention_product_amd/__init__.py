@@ -24,7 +24,7 @@ EXPORTED = ("pq_attn_num_chunks", "pq_attn_workspace_bytes", "pq_attn_decode",
             "pq_attn_partials", "pq_attn_partials_timed", "pq_attn_step_workspace_bytes",
             "pq_attn_decode_step", "pq_attn_decode_step_timed", "pq_attn_decode_paged",
             "pq_attn_decode_step_paged", "pq_attn_decode_step_paged_timed", "pq_attn_reduce",
-            "pq_encode", "pq_encode_many", "pq_status_string")
+            "pq_encode", "pq_encode_many", "pq_codebook_update", "pq_kmeans", "pq_status_string")
 
 
 class PQError(RuntimeError):
@@ -105,6 +105,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pq_encode_many.argtypes = [ctypes.POINTER(PQEncodeDesc), ctypes.c_int32,
                                    ctypes.POINTER(P), ctypes.POINTER(P), P, ctypes.POINTER(P), P]
     lib.pq_encode_many.restype = ctypes.c_int
+    lib.pq_codebook_update.argtypes = [ctypes.POINTER(PQEncodeDesc), P, P, P, P, P]
+    lib.pq_codebook_update.restype = ctypes.c_int
+    lib.pq_kmeans.argtypes = [ctypes.POINTER(PQEncodeDesc), P, P, ctypes.c_int32, P, P]
+    lib.pq_kmeans.restype = ctypes.c_int
     lib.pq_status_string.argtypes = [ctypes.c_int]
     lib.pq_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -434,6 +438,55 @@ def pq_encode_many(xs, codebooks, codes, *, desc, slots=None, stream=None):
         _ptr(slots), arr(*[_ptr(t) for t in codes]), _stream(stream))
     _check(st, "pq_encode_many")
     return codes
+
+
+def _sample_desc(x, codebook, codes):
+    N, H, D = x.shape
+    _, M, K, _ = codebook.shape
+    return PQEncodeDesc(N, H, D, M, K, H * D, D, H * M, M, codes.numel())
+
+
+def pq_codebook_update(x, codes, codebook, counts=None, *, desc=None, stream=None):
+    """Update step of a Lloyd iteration (C entry point pq_codebook_update):
+    every codeword named by some code moves to the mean of its segments.
+    Default layout (desc None): x fp16 [N, H, D], codes uint8 [N, H, M],
+    codebook fp16 [H, M, K, D/M] (updated in place), counts uint32-compatible
+    int32 [H, M, K] or None.  Returns the codebook."""
+    import torch
+    _need(x, "x", torch.float16, None)
+    _need(codebook, "codebook", torch.float16, None)
+    _need(codes, "codes", torch.uint8, None)
+    if counts is not None:
+        _need(counts, "counts", torch.int32, tuple(codebook.shape[:3]))
+    if desc is None:
+        N, H, _ = x.shape
+        _need(codes, "codes", torch.uint8, (N, H, codebook.shape[1]))
+        desc = _sample_desc(x, codebook, codes)
+    st = load_library().pq_codebook_update(ctypes.byref(desc), _ptr(x), _ptr(codes),
+                                           _ptr(codebook), _ptr(counts), _stream(stream))
+    _check(st, "pq_codebook_update")
+    return codebook
+
+
+def pq_kmeans(x, codebook, n_iter, codes=None, *, desc=None, stream=None):
+    """n_iter Lloyd iterations from ``codebook`` (updated in place) on the
+    sample x (C entry point pq_kmeans).  Returns (codebook, codes), codes
+    being x's codes under the learned codebook."""
+    import torch
+    _need(x, "x", torch.float16, None)
+    _need(codebook, "codebook", torch.float16, None)
+    if codes is None:
+        codes = torch.empty((x.shape[0], x.shape[1], codebook.shape[1]), dtype=torch.uint8,
+                            device=x.device)
+    _need(codes, "codes", torch.uint8, None)
+    if desc is None:
+        N, H, _ = x.shape
+        _need(codes, "codes", torch.uint8, (N, H, codebook.shape[1]))
+        desc = _sample_desc(x, codebook, codes)
+    st = load_library().pq_kmeans(ctypes.byref(desc), _ptr(x), _ptr(codebook), int(n_iter),
+                                  _ptr(codes), _stream(stream))
+    _check(st, "pq_kmeans")
+    return codebook, codes
 
 
 def cache_encode_desc(n_vec, batch, n_kv_heads, max_len, head_dim=128, n_sub=4, n_codes=256,

@@ -8,6 +8,7 @@
 
 #include "decode_kernel.hpp"
 #include "encode_kernel.hpp"
+#include "kmeans_kernel.hpp"
 #include "plan.h"
 #include "pqattn.h"
 
@@ -306,6 +307,14 @@ pq_status pq_attn_reduce(int64_t n_rows, int32_t n_chunks, int32_t head_dim, con
 namespace pqattn {
 namespace {
 
+// The codes' identity places (slot n for vector n) must fit the buffer.
+bool identity_places_fit(const pq_encode_desc* d, const EncodePlan& p) {
+  if (p.N == 0) return true;
+  const double last = double(p.N - 1) * double(d->codes_stride_slot) +
+                      double(p.H - 1) * double(d->codes_stride_head) + p.M;
+  return last <= double(d->codes_bytes);
+}
+
 pq_status encode_planes(const pq_encode_desc* desc, int32_t n, const void* const* x,
                         const void* const* codebook, const int64_t* slots, uint8_t* const* codes,
                         hipStream_t stream) {
@@ -320,11 +329,7 @@ pq_status encode_planes(const pq_encode_desc* desc, int32_t n, const void* const
     if ((reinterpret_cast<uintptr_t>(codes[i]) % p.M) != 0) return PQ_ERR_ALIGN;
   }
   if (p.N == 0) return PQ_OK;
-  if (!slots) {   // identity places: the last one must fit
-    const double last = double(p.N - 1) * double(desc->codes_stride_slot) +
-                        double(p.H - 1) * double(desc->codes_stride_head) + p.M;
-    if (last > double(desc->codes_bytes)) return PQ_ERR_SHAPE;
-  }
+  if (!slots && !identity_places_fit(desc, p)) return PQ_ERR_SHAPE;
   EncodeArgs a{};
   for (int i = 0; i < n; ++i) {
     a.x[i] = static_cast<const __half*>(x[i]);
@@ -344,10 +349,65 @@ pq_status encode_planes(const pq_encode_desc* desc, int32_t n, const void* const
                 stream);
 }
 
+// Checks for the update step: the encode's shape rules, identity places
+// that fit the codes buffer, and at most kMaxUpdateVectors vectors.
+pq_status check_update(const pq_encode_desc* desc, const void* x, const void* codes,
+                       const void* codebook, EncodePlan* p) {
+  pq_status st = plan_encode(desc, kEncodeVectors, p);
+  if (st != PQ_OK) return st;
+  if (p->N > kMaxUpdateVectors) return PQ_ERR_UNSUPPORTED;
+  if (!x || !codes || !codebook) return PQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codebook)) return PQ_ERR_ALIGN;
+  if (!identity_places_fit(desc, *p)) return PQ_ERR_SHAPE;
+  return PQ_OK;
+}
+
+pq_status launch_update(const pq_encode_desc* desc, const EncodePlan& p, const void* x,
+                        const uint8_t* codes, void* codebook, uint32_t* counts, hipStream_t stream) {
+  UpdateArgs a{};
+  a.x = static_cast<const __half*>(x);
+  a.codes = codes;
+  a.cb = static_cast<__half*>(codebook);
+  a.counts = counts;
+  a.N = p.N;
+  a.sxv = desc->x_stride_vec;
+  a.sxh = desc->x_stride_head;
+  a.scs = desc->codes_stride_slot;
+  a.sch = desc->codes_stride_head;
+  const void* fn = p.M == 4 ? reinterpret_cast<const void*>(&codebook_update_kernel<4>)
+                            : reinterpret_cast<const void*>(&codebook_update_kernel<8>);
+  return launch(fn, dim3(unsigned(p.M), unsigned(p.H)), dim3(kUpdateThreads), &a, stream);
+}
+
 }  // namespace
 }  // namespace pqattn
 
 extern "C" {
+
+pq_status pq_codebook_update(const pq_encode_desc* desc, const void* x, const uint8_t* codes,
+                             void* codebook, uint32_t* counts, void* stream) {
+  EncodePlan p;
+  pq_status st = check_update(desc, x, codes, codebook, &p);
+  if (st != PQ_OK) return st;
+  return launch_update(desc, p, x, codes, codebook, counts, static_cast<hipStream_t>(stream));
+}
+
+pq_status pq_kmeans(const pq_encode_desc* desc, const void* x, void* codebook, int32_t n_iter,
+                    uint8_t* codes, void* stream) {
+  EncodePlan p;
+  pq_status st = check_update(desc, x, codes, codebook, &p);
+  if (st != PQ_OK) return st;
+  if (n_iter < 0) return PQ_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const void* cb = codebook;
+  for (int32_t i = 0; i <= n_iter; ++i) {
+    st = encode_planes(desc, 1, &x, &cb, nullptr, &codes, s);
+    if (st != PQ_OK || i == n_iter) break;
+    st = launch_update(desc, p, x, codes, codebook, nullptr, s);
+    if (st != PQ_OK) break;
+  }
+  return st;
+}
 
 pq_status pq_encode(const pq_encode_desc* desc, const void* x, const void* codebook,
                     const int64_t* slots, uint8_t* codes, void* stream) {

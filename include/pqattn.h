@@ -276,6 +276,36 @@ pq_status pq_encode_many(const pq_encode_desc* desc, int32_t n, const void* cons
                          const void* const* codebook, const int64_t* slots,
                          uint8_t* const* codes, void* stream);
 
+/* The update step of one Lloyd (K-means) iteration of codebook learning
+ * (AQPIM page, section 3.2 (2): codebooks fitted online to the first vectors
+ * of a sequence; section 5.2 (1): a fast K-means on a small sample;
+ * section 6.1 (3): a few K-means updates every so many tokens).  For every
+ * head h, segment m and codeword k with at least one vector n whose code
+ * (n, h, m) is k, codebook[h][m][k] becomes the mean of segment m of those
+ * x[n][h]: the exact sum, divided by the count in double precision and
+ * rounded to the nearest fp16 (ties to even).  Codewords no vector names keep
+ * their value.  The result does not depend on the order of the vectors.
+ *  desc      shape and strides as for pq_encode; the codes are read at their
+ *            identity places (slot n for vector n), which must fit
+ *            codes_bytes.  At most 4,194,304 vectors (PQ_ERR_UNSUPPORTED).
+ *  x         fp16, as for pq_encode
+ *  codes     uint8, e.g. what pq_encode wrote for the same x and codebook
+ *  codebook  fp16 [H][M][K][D/M], updated in place, 16-byte aligned
+ *  counts    uint32 [H][M][K] vectors per codeword, written; may be NULL */
+pq_status pq_codebook_update(const pq_encode_desc* desc, const void* x, const uint8_t* codes,
+                             void* codebook, uint32_t* counts, void* stream);
+
+/* n_iter Lloyd iterations of codebook learning on the sample x, starting from
+ * the codebook passed in (AQPIM page, sections 3.2 (2), 5.2 (1), 6.1 (3)):
+ * each iteration is pq_encode of x into codes followed by
+ * pq_codebook_update; then x is encoded once more, so on return codebook
+ * holds the learned codewords and codes the sample's codes under them.
+ * n_iter >= 0 (0: encode only).  Arguments as for pq_codebook_update; the
+ * codes buffer is the iterations' working array and the final assignment.
+ * 2 * n_iter + 1 launches on stream, no synchronisation. */
+pq_status pq_kmeans(const pq_encode_desc* desc, const void* x, void* codebook, int32_t n_iter,
+                    uint8_t* codes, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* pq_status_string(pq_status status);
 

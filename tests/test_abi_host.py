@@ -302,3 +302,31 @@ def test_paged_encode_desc_matches_pool_layout():
     d = pq.paged_encode_desc(10, n_kv_heads=3, n_pages=7, page_tokens=16, n_sub=8)
     assert d.codes_stride_slot == 8 and d.codes_stride_head == 7 * 16 * 8
     assert d.codes_bytes == 3 * 7 * 16 * 8
+
+
+def _enc_desc(**kw):
+    d = dict(n_vec=32, n_heads=2, head_dim=128, n_sub=4, n_codes=256, x_stride_vec=256,
+             x_stride_head=128, codes_stride_slot=8, codes_stride_head=4, codes_bytes=32 * 8)
+    d.update(kw)
+    return pq.PQEncodeDesc(**d)
+
+
+def test_codebook_update_and_kmeans_checks(lib):
+    d = _enc_desc()
+    for which in range(3):                       # x, codes, codebook
+        p = [FAKE] * 3
+        p[which] = None
+        assert lib.pq_codebook_update(ctypes.byref(d), *p, None, None) == 1
+        assert lib.pq_kmeans(ctypes.byref(d), p[0], p[2], 3, p[1], None) == 1
+    # identity places past the codes buffer
+    short = _enc_desc(codes_bytes=32 * 8 - 1)
+    assert lib.pq_codebook_update(ctypes.byref(short), FAKE, FAKE, FAKE, None, None) == 2
+    assert lib.pq_kmeans(ctypes.byref(short), FAKE, FAKE, 1, FAKE, None) == 2
+    # more vectors than the exact 64-bit sums allow
+    big = _enc_desc(n_vec=(1 << 22) + 1, codes_bytes=((1 << 22) + 1) * 8)
+    assert lib.pq_codebook_update(ctypes.byref(big), FAKE, FAKE, FAKE, None, None) == 3
+    assert lib.pq_kmeans(ctypes.byref(d), FAKE, FAKE, -1, FAKE, None) == 2
+    assert lib.pq_codebook_update(ctypes.byref(d), FAKE + 2, FAKE, FAKE, None, None) == 6
+    assert lib.pq_codebook_update(ctypes.byref(d), FAKE, FAKE, FAKE + 8, None, None) == 6
+    assert lib.pq_codebook_update(ctypes.byref(_enc_desc(n_sub=2)), FAKE, FAKE, FAKE, None,
+                                  None) == 3
