@@ -148,6 +148,7 @@ def main():
     ap.add_argument("--encode-reps", type=int, default=5)
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache leg")
     ap.add_argument("--paged-steps", type=int, default=500)
+    ap.add_argument("--no-kmeans", action="store_true", help="skip the codebook-learning leg")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run 3 device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -299,6 +300,8 @@ def main():
                                     step_ms_plain * 1e3 if wid == 3 else None)
     if not args.no_encode:
         result["encode"] = encode_leg(pq, torch, dev, args.encode_reps)
+    if not args.no_kmeans:
+        result["kmeans"] = kmeans_leg(pq, torch, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wid)
     print(json.dumps(result), flush=True)
@@ -413,6 +416,46 @@ def paged_leg(pq, torch, dev, steps, warmup, dense_gqa_us):
         if name == "ragged":
             leg["dense_step_us"] = timed(dense)
         res[name] = leg
+    return res
+
+
+def kmeans_leg(pq, torch, dev, n_iter=10, reps=20):
+    """Codebook learning: pq_kmeans (n_iter Lloyd iterations, then the final
+    assignment) of the K and of the V codebooks of 32 heads (M=4, K=256) on
+    a sample of N vectors per head -- the pages' 32-vector sample and a
+    4096-token prefill -- from a perturbed start.  Timed with events around
+    `reps` learns of both codebooks.  HBM bytes per iteration: the sample
+    read by the assignment and by the update, its codes written and read."""
+    from synth import gen
+    stream = torch.cuda.current_stream()
+    res = {"n_iter": n_iter, "heads": 32, "n_sub": 4}
+    for name, N in (("sample32", 32), ("prefill4096", 4096)):
+        rng = np.random.default_rng(7300 + N)
+        cases = [gen.kmeans_case(rng, N, 32, 4, sigma=0.1, init_sigma=0.3, n_used=min(N, 256))
+                 for _ in range(2)]
+        xs = [torch.from_numpy(c["x"]).to(dev) for c in cases]
+        starts = [torch.from_numpy(c["cb_init"]).to(dev) for c in cases]
+        cbs = [t.clone() for t in starts]
+        codes = [torch.empty((N, 32, 4), dtype=torch.uint8, device=dev) for _ in cases]
+
+        def learn():
+            for x, cb, cd, st in zip(xs, cbs, codes, starts):
+                cb.copy_(st)
+                pq.pq_kmeans(x, cb, n_iter, cd, stream=stream)
+
+        learn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            learn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        per_iter = 2 * (2 * N * 32 * 128 * 2 + 2 * N * 32 * 4)     # K and V
+        res[name] = {"vectors_per_head": N, "us_per_learn_k_and_v": us,
+                     "vector_iterations_per_s": 2 * N * 32 * n_iter / (us * 1e-6),
+                     "hbm_gbs": per_iter * n_iter / (us * 1e-6) / 1e9}
     return res
 
 
