@@ -420,11 +420,12 @@ def paged_leg(pq, torch, dev, steps, warmup, dense_gqa_us):
 
 
 def kmeans_leg(pq, torch, dev, n_iter=10, reps=20):
-    """Codebook learning: pq_kmeans (n_iter Lloyd iterations, then the final
-    assignment) of the K and of the V codebooks of 32 heads (M=4, K=256) on
-    a sample of N vectors per head -- the pages' 32-vector sample and a
-    4096-token prefill -- from a perturbed start.  Timed with events around
-    `reps` learns of both codebooks.  HBM bytes per iteration: the sample
+    """Codebook learning: pq_kmeans_many (n_iter Lloyd iterations, then the
+    final assignment) of the K and the V codebooks of 32 heads (M=4, K=256)
+    together on a sample of N vectors per head -- the pages' 32-vector sample
+    and a 4096-token prefill -- from a perturbed start (one launch each; the
+    timed region also restores the two start codebooks, two small copies).
+    Timed with events around `reps` learns.  HBM bytes per iteration: the sample
     read by the assignment and by the update, its codes written and read."""
     from synth import gen
     stream = torch.cuda.current_stream()
@@ -439,9 +440,9 @@ def kmeans_leg(pq, torch, dev, n_iter=10, reps=20):
         codes = [torch.empty((N, 32, 4), dtype=torch.uint8, device=dev) for _ in cases]
 
         def learn():
-            for x, cb, cd, st in zip(xs, cbs, codes, starts):
+            for cb, st in zip(cbs, starts):
                 cb.copy_(st)
-                pq.pq_kmeans(x, cb, n_iter, cd, stream=stream)
+            pq.pq_kmeans_many(xs, cbs, n_iter, codes, stream=stream)
 
         learn()
         torch.cuda.synchronize()

@@ -24,7 +24,8 @@ EXPORTED = ("pq_attn_num_chunks", "pq_attn_workspace_bytes", "pq_attn_decode",
             "pq_attn_partials", "pq_attn_partials_timed", "pq_attn_step_workspace_bytes",
             "pq_attn_decode_step", "pq_attn_decode_step_timed", "pq_attn_decode_paged",
             "pq_attn_decode_step_paged", "pq_attn_decode_step_paged_timed", "pq_attn_reduce",
-            "pq_encode", "pq_encode_many", "pq_codebook_update", "pq_kmeans", "pq_status_string")
+            "pq_encode", "pq_encode_many", "pq_codebook_update", "pq_kmeans",
+            "pq_kmeans_many", "pq_status_string")
 
 
 class PQError(RuntimeError):
@@ -109,6 +110,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pq_codebook_update.restype = ctypes.c_int
     lib.pq_kmeans.argtypes = [ctypes.POINTER(PQEncodeDesc), P, P, ctypes.c_int32, P, P]
     lib.pq_kmeans.restype = ctypes.c_int
+    lib.pq_kmeans_many.argtypes = [ctypes.POINTER(PQEncodeDesc), ctypes.c_int32, ctypes.POINTER(P),
+                                   ctypes.POINTER(P), ctypes.c_int32, ctypes.POINTER(P), P]
+    lib.pq_kmeans_many.restype = ctypes.c_int
     lib.pq_status_string.argtypes = [ctypes.c_int]
     lib.pq_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -487,6 +491,33 @@ def pq_kmeans(x, codebook, n_iter, codes=None, *, desc=None, stream=None):
                                   _ptr(codes), _stream(stream))
     _check(st, "pq_kmeans")
     return codebook, codes
+
+
+def pq_kmeans_many(xs, codebooks, n_iter, codes=None, *, desc=None, stream=None):
+    """pq_kmeans for 1 or 2 samples of one shape in one call (C entry point
+    pq_kmeans_many), e.g. a layer's K and V samples.  Returns (codebooks,
+    codes) lists."""
+    import torch
+    n = len(xs)
+    if len(codebooks) != n:
+        raise ValueError("xs and codebooks must have the same length")
+    for t in xs:
+        _need(t, "x", torch.float16, None)
+    for t in codebooks:
+        _need(t, "codebook", torch.float16, None)
+    if codes is None:
+        codes = [torch.empty((x.shape[0], x.shape[1], cb.shape[1]), dtype=torch.uint8,
+                             device=x.device) for x, cb in zip(xs, codebooks)]
+    for t in codes:
+        _need(t, "codes", torch.uint8, None)
+    if desc is None:
+        desc = _sample_desc(xs[0], codebooks[0], codes[0])
+    arr = ctypes.c_void_p * max(n, 1)
+    st = load_library().pq_kmeans_many(
+        ctypes.byref(desc), n, arr(*[_ptr(t) for t in xs]), arr(*[_ptr(t) for t in codebooks]),
+        int(n_iter), arr(*[_ptr(t) for t in codes]), _stream(stream))
+    _check(st, "pq_kmeans_many")
+    return codebooks, codes
 
 
 def cache_encode_desc(n_vec, batch, n_kv_heads, max_len, head_dim=128, n_sub=4, n_codes=256,

@@ -379,6 +379,54 @@ pq_status launch_update(const pq_encode_desc* desc, const EncodePlan& p, const v
   return launch(fn, dim3(unsigned(p.M), unsigned(p.H)), dim3(kUpdateThreads), &a, stream);
 }
 
+// Lloyd runs for n (1..kMaxKmeansPlanes) samples of one shape: one launch
+// when the sample fits the fused kernel, else encode and update launches per
+// iteration and plane.
+pq_status kmeans_planes(const pq_encode_desc* desc, int32_t n, const void* const* x,
+                        void* const* codebook, int32_t n_iter, uint8_t* const* codes,
+                        hipStream_t stream) {
+  if (n < 1 || n > kMaxKmeansPlanes) return PQ_ERR_SHAPE;
+  if (!x || !codebook || !codes) return PQ_ERR_NULL;
+  EncodePlan p;
+  for (int i = 0; i < n; ++i) {
+    pq_status st = check_update(desc, x[i], codes[i], codebook[i], &p);
+    if (st != PQ_OK) return st;
+    if ((reinterpret_cast<uintptr_t>(codes[i]) % p.M) != 0) return PQ_ERR_ALIGN;
+  }
+  if (n_iter < 0) return PQ_ERR_SHAPE;
+  if (p.N == 0) return PQ_OK;
+  if (p.N <= kMaxFusedVectors) {
+    KmeansArgs a{};
+    for (int i = 0; i < n; ++i) {
+      a.x[i] = static_cast<const __half*>(x[i]);
+      a.cb[i] = static_cast<__half*>(codebook[i]);
+      a.codes[i] = codes[i];
+    }
+    a.N = p.N;
+    a.sxv = desc->x_stride_vec;
+    a.sxh = desc->x_stride_head;
+    a.scs = desc->codes_stride_slot;
+    a.sch = desc->codes_stride_head;
+    a.codes_bytes = desc->codes_bytes;
+    a.n_iter = n_iter;
+    const void* fn = p.M == 4 ? reinterpret_cast<const void*>(&kmeans_kernel<4>)
+                              : reinterpret_cast<const void*>(&kmeans_kernel<8>);
+    return launch(fn, dim3(unsigned(p.M), unsigned(p.H), unsigned(n)), dim3(kKmeansThreads), &a,
+                  stream);
+  }
+  for (int i = 0; i < n; ++i) {
+    const void* cb = codebook[i];
+    for (int32_t it = 0; it <= n_iter; ++it) {
+      pq_status st = encode_planes(desc, 1, &x[i], &cb, nullptr, &codes[i], stream);
+      if (st != PQ_OK) return st;
+      if (it == n_iter) break;
+      st = launch_update(desc, p, x[i], codes[i], codebook[i], nullptr, stream);
+      if (st != PQ_OK) return st;
+    }
+  }
+  return PQ_OK;
+}
+
 }  // namespace
 }  // namespace pqattn
 
@@ -394,19 +442,13 @@ pq_status pq_codebook_update(const pq_encode_desc* desc, const void* x, const ui
 
 pq_status pq_kmeans(const pq_encode_desc* desc, const void* x, void* codebook, int32_t n_iter,
                     uint8_t* codes, void* stream) {
-  EncodePlan p;
-  pq_status st = check_update(desc, x, codes, codebook, &p);
-  if (st != PQ_OK) return st;
-  if (n_iter < 0) return PQ_ERR_SHAPE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const void* cb = codebook;
-  for (int32_t i = 0; i <= n_iter; ++i) {
-    st = encode_planes(desc, 1, &x, &cb, nullptr, &codes, s);
-    if (st != PQ_OK || i == n_iter) break;
-    st = launch_update(desc, p, x, codes, codebook, nullptr, s);
-    if (st != PQ_OK) break;
-  }
-  return st;
+  return kmeans_planes(desc, 1, &x, &codebook, n_iter, &codes, static_cast<hipStream_t>(stream));
+}
+
+pq_status pq_kmeans_many(const pq_encode_desc* desc, int32_t n, const void* const* x,
+                         void* const* codebook, int32_t n_iter, uint8_t* const* codes,
+                         void* stream) {
+  return kmeans_planes(desc, n, x, codebook, n_iter, codes, static_cast<hipStream_t>(stream));
 }
 
 pq_status pq_encode(const pq_encode_desc* desc, const void* x, const void* codebook,

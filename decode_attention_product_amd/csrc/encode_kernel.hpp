@@ -12,13 +12,17 @@
 // Workgroup = one head and a tile of NV vectors (grid: heads fastest, then
 // tiles, then planes), 2M waves: wave w handles segment m = w % M against
 // codeword half w / M (codewords 128*(w/M) .. +127), holding those 128
-// codewords in registers as MFMA B operands for the whole tile -- half the
-// registers of a whole codebook, so four waves fit on a SIMD.  Lane
-// (l16, q4) of an instruction's result holds vectors 4*q4 .. 4*q4+3
-// against codeword nt*16 + l16; each lane keeps a running best over its
-// half's 8 codeword tiles, the 16 lanes of a row reduce (score, index) with
-// DPP -- larger score, or equal score and lower index, wins -- and the two
-// halves meet in LDS as order-preserving 64-bit keys.
+// codewords in registers for the whole tile -- half the registers of a
+// whole codebook, so four waves fit on a SIMD.  The codewords are the A
+// operand of each product and 16 vectors the B operand, so lane (j, q4) of
+// a result holds vector j against codewords 4*q4 .. 4*q4+3 of the tile; each
+// lane keeps a running best over its half's 8 tiles (larger score, or equal
+// score and lower index, wins), two lane swaps combine the four rows, and
+// the two halves meet in LDS as order-preserving 64-bit keys.
+//
+// score_inits, tile_scores and tiles_best_key are the whole arithmetic of a
+// decision; codebook learning (kmeans_kernel) calls the same functions, so
+// its assignments are this kernel's, decision for decision.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,6 +46,77 @@ struct EncodeArgs {
   int64_t codes_bytes;       // writes outside [0, codes_bytes) are skipped
   int64_t sxv, sxh, scs, sch;
 };
+
+// -|c|^2/2 of the codewords of NCT tiles, given as A operands (lane (l16,
+// q4) holds dims 4*q4 .. of codeword nt*16 + l16 for every k-step), laid out
+// as the accumulator inputs of the products: lane (j, q4) gets those of
+// codewords nt*16 + 4*q4 + r, r = 0..3.
+template <int KS, int NCT>
+__device__ __forceinline__ void score_inits(const f16x4 (&c)[NCT][KS], f32x4 (&cinit)[NCT], int q4) {
+  float cn[NCT];
+  neg_half_norm2_n<KS, NCT>(c, cn);
+#pragma unroll
+  for (int nt = 0; nt < NCT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cinit[nt][r] = __shfl(cn[nt], 4 * q4 + r, 64);
+}
+
+// -|c|^2/2 of one codeword from its DS fp16 values: the value score_inits
+// gives it, by the same operations in the same order -- per group q of four
+// dimensions (dims s*16 + 4q .. +3 of every k-step s) the fdot2 chain of one
+// lane, then (p0 + p1) + (p2 + p3) as the two lane swaps add them.
+template <int KS>
+__device__ __forceinline__ float neg_half_norm2_row(const _Float16* c) {
+  float p[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    p[q] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const f16x2 lo = {c[s * 16 + 4 * q], c[s * 16 + 4 * q + 1]};
+      const f16x2 hi = {c[s * 16 + 4 * q + 2], c[s * 16 + 4 * q + 3]};
+      p[q] = __builtin_amdgcn_fdot2(lo, lo, p[q], false);
+      p[q] = __builtin_amdgcn_fdot2(hi, hi, p[q], false);
+    }
+  }
+  return -0.5f * ((p[0] + p[1]) + (p[2] + p[3]));
+}
+
+// x.c - |c|^2/2 of 16 vectors (B operand, one f16x4 per k-step) against the
+// 16 codewords of one tile (A operand): fp16 products, fp32 sums starting
+// from the tile's score_inits.  Lane (j, q4) gets vector j against
+// codewords 4*q4 + r.
+template <int KS>
+__device__ __forceinline__ f32x4 tile_scores(const f16x4 (&c)[KS], const f16x4 (&x)[KS],
+                                             const f32x4& init) {
+  f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x16f16(c[0], x[0], init, 0, 0, 0);
+#pragma unroll
+  for (int s = 1; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x16f16(c[s], x[s], acc, 0, 0, 0);
+  return acc;
+}
+
+// The best (score, index) over NCT tiles of scores (codeword kbase + nt*16 +
+// 4*q4 + r for acc[nt][r]) as an argmax key, the same in the four lanes of
+// column j: each lane walks its codewords in ascending order (ties keep the
+// lower), then rows q4 ^ 1 and q4 ^ 2 are combined by lane swaps.
+template <int NCT>
+__device__ __forceinline__ unsigned long long tiles_best_key(const f32x4 (&acc)[NCT], int kbase,
+                                                             int q4) {
+  float best = acc[0][0];
+  int bk = kbase + 4 * q4;
+#pragma unroll
+  for (int nt = 0; nt < NCT; ++nt) {
+#pragma unroll
+    for (int r = (nt == 0 ? 1 : 0); r < 4; ++r) {
+      const bool take = acc[nt][r] > best;
+      best = take ? acc[nt][r] : best;
+      bk = take ? kbase + nt * 16 + 4 * q4 + r : bk;
+    }
+  }
+  argmax_pair16(best, bk);   // rows q4 and q4 ^ 1
+  argmax_pair32(best, bk);   // rows q4 and q4 ^ 2
+  return argmax_key(best, bk);
+}
 
 template <int M, int NV>
 __global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
@@ -68,7 +143,7 @@ __global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
   const int64_t n0 = int64_t(blockIdx.y) * NV;
   const int nv = int(min<int64_t>(NV, a.N - n0));
 
-  // ---- this half of the codebook of (h, m) as MFMA B operands ----------------
+  // ---- this half of the codebook of (h, m) as MFMA A operands ----------------
   const __half* cb = a.cb[plane] + (int64_t(h) * M + m) * K * DS + int64_t(half) * (K / 2) * DS;
   f16x4 bop[NCT][KS];
 #pragma unroll
@@ -77,7 +152,7 @@ __global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
     for (int s = 0; s < KS; ++s)
       bop[nt][s] = *reinterpret_cast<const f16x4*>(cb + (nt * 16 + l16) * DS + s * 16 + 4 * q4);
 
-  // A operands (16 vectors x this segment) of one tile; the next tile's are
+  // B operands (16 vectors x this segment) of one tile; the next tile's are
   // requested while the current one is scored
   auto load_a = [&](int t, f16x4 (&dst)[KS]) {
     const int v = t * 16 + l16;
@@ -94,16 +169,8 @@ __global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
   f16x4 acur[KS], anext[KS];
   load_a(0, acur);
 
-  // -|c|^2 / 2 of codeword nt*16 + l16 of this half (the B-operand layout),
-  // then, as the accumulator inputs of the transposed products below, lane
-  // (j, q4) needs those of codewords nt*16 + 4*q4 + r, r = 0..3
-  float cn[NCT];
-  neg_half_norm2_n<KS, NCT>(bop, cn);
   f32x4 cinit[NCT];
-#pragma unroll
-  for (int nt = 0; nt < NCT; ++nt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) cinit[nt][r] = __shfl(cn[nt], 4 * q4 + r, 64);
+  score_inits<KS, NCT>(bop, cinit, q4);
 
   // ---- scores, running argmax, cross-row reduction ---------------------------
   // Transposed products C[i = codeword][j = vector] (the codeword operands
@@ -117,28 +184,11 @@ __global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
     if (t + 1 < NTILE) load_a(t + 1, anext);
     f32x4 acc[NCT];
 #pragma unroll
-    for (int nt = 0; nt < NCT; ++nt) {
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(bop[nt][0], acur[0], cinit[nt], 0, 0, 0);
-#pragma unroll
-      for (int s = 1; s < KS; ++s)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(bop[nt][s], acur[s], acc[nt], 0, 0, 0);
-    }
-    float best = acc[0][0];
-    int bk = kbase + 4 * q4;
-#pragma unroll
-    for (int nt = 0; nt < NCT; ++nt) {
-#pragma unroll
-      for (int r = (nt == 0 ? 1 : 0); r < 4; ++r) {
-        const bool take = acc[nt][r] > best;   // ascending codewords: ties keep the lower
-        best = take ? acc[nt][r] : best;
-        bk = take ? kbase + nt * 16 + 4 * q4 + r : bk;
-      }
-    }
-    argmax_pair16(best, bk);   // rows q4 and q4 ^ 1
-    argmax_pair32(best, bk);   // rows q4 and q4 ^ 2
+    for (int nt = 0; nt < NCT; ++nt) acc[nt] = tile_scores<KS>(bop[nt], acur, cinit[nt]);
+    const unsigned long long key = tiles_best_key<NCT>(acc, kbase, q4);
     if (q4 == 0) {
       const int v = t * 16 + l16;
-      if (v < nv) keys[v][m][half] = argmax_key(best, bk);
+      if (v < nv) keys[v][m][half] = key;
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) acur[s] = anext[s];

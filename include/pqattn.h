@@ -300,11 +300,22 @@ pq_status pq_codebook_update(const pq_encode_desc* desc, const void* x, const ui
  * each iteration is pq_encode of x into codes followed by
  * pq_codebook_update; then x is encoded once more, so on return codebook
  * holds the learned codewords and codes the sample's codes under them.
- * n_iter >= 0 (0: encode only).  Arguments as for pq_codebook_update; the
- * codes buffer is the iterations' working array and the final assignment.
- * 2 * n_iter + 1 launches on stream, no synchronisation. */
+ * n_iter >= 0 (0: encode only).  Arguments as for pq_codebook_update, plus
+ * codes aligned to M bytes; codes receives the final assignment.  Samples of
+ * up to 8192 vectors run in one launch (the whole run on chip); larger ones
+ * as 2 * n_iter + 1 launches.  Either way the result is the same and the
+ * call does not synchronise. */
 pq_status pq_kmeans(const pq_encode_desc* desc, const void* x, void* codebook, int32_t n_iter,
                     uint8_t* codes, void* stream);
+
+/* pq_kmeans for n (1 or 2) samples of the same shape and strides in one call
+ * -- typically the K and the V vectors of a layer, each with its own
+ * codebook and codes.  x, codebook and codes are host arrays of n device
+ * pointers; plane i gets exactly what pq_kmeans(desc, x[i], codebook[i],
+ * n_iter, codes[i]) gives.  n outside 1..2 is PQ_ERR_SHAPE. */
+pq_status pq_kmeans_many(const pq_encode_desc* desc, int32_t n, const void* const* x,
+                         void* const* codebook, int32_t n_iter, uint8_t* const* codes,
+                         void* stream);
 
 /* A static, human-readable name for a status code. */
 const char* pq_status_string(pq_status status);

@@ -330,3 +330,14 @@ def test_codebook_update_and_kmeans_checks(lib):
     assert lib.pq_codebook_update(ctypes.byref(d), FAKE, FAKE, FAKE + 8, None, None) == 6
     assert lib.pq_codebook_update(ctypes.byref(_enc_desc(n_sub=2)), FAKE, FAKE, FAKE, None,
                                   None) == 3
+
+
+def test_kmeans_many_checks(lib):
+    d = _enc_desc()
+    arr = ctypes.c_void_p * 3
+    ok = arr(FAKE, FAKE, FAKE)
+    for n in (0, 3):
+        assert lib.pq_kmeans_many(ctypes.byref(d), n, ok, ok, 2, ok, None) == 2
+    assert lib.pq_kmeans_many(ctypes.byref(d), 2, None, ok, 2, ok, None) == 1
+    assert lib.pq_kmeans_many(ctypes.byref(d), 2, ok, ok, 2, arr(FAKE, None, FAKE), None) == 1
+    assert lib.pq_kmeans_many(ctypes.byref(d), 2, ok, ok, 2, arr(FAKE, FAKE + 2, FAKE), None) == 6

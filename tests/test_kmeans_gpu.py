@@ -189,3 +189,78 @@ def test_learned_codebooks_then_encode_and_decode():
     err = np.abs(got - ref).max()
     say(f"learned-codebook decode: max|d| = {err:.3e}, max|ref| = {np.abs(ref).max():.3e}")
     assert err <= 1e-3 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("N,M,n_iter", [(8192, 8, 3), (8200, 4, 2)])
+def test_kmeans_at_and_past_the_one_launch_size(N, M, n_iter):
+    """8192 vectors: the last size learned in one launch; 8200: the per-
+    iteration launches.  Both as the oracle, bit for bit."""
+    say(f"kmeans N={N} M={M} iters={n_iter}")
+    case = gen.kmeans_case(np.random.default_rng(1300 + N), N, 2, M, sigma=0.05, init_sigma=0.25,
+                           n_used=100)
+    ref_cb, ref_codes = oracle.kmeans(case["x"], case["cb_init"], n_iter)
+    cb = dev(case["cb_init"])
+    _, codes = pq.pq_kmeans(dev(case["x"]), cb, n_iter)
+    torch.cuda.synchronize()
+    same_bits(cb.cpu().numpy(), ref_cb)
+    np.testing.assert_array_equal(codes.cpu().numpy(), ref_codes)
+
+
+def test_kmeans_many_equals_single_calls():
+    """K and V samples learned in one call give what two pq_kmeans calls give,
+    and the oracle's."""
+    say("kmeans_many: K and V of 8 heads, 64 vectors, 4 iterations")
+    rng = np.random.default_rng(1400)
+    cases = [gen.kmeans_case(rng, 64, 8, 4, sigma=0.1, init_sigma=0.3) for _ in range(2)]
+    xs = [dev(c["x"]) for c in cases]
+    many = [dev(c["cb_init"]) for c in cases]
+    _, codes = pq.pq_kmeans_many(xs, many, 4)
+    single = [dev(c["cb_init"]) for c in cases]
+    single_codes = [pq.pq_kmeans(x, cb, 4)[1] for x, cb in zip(xs, single)]
+    torch.cuda.synchronize()
+    for i, c in enumerate(cases):
+        ref_cb, ref_codes = oracle.kmeans(c["x"], c["cb_init"], 4)
+        same_bits(many[i].cpu().numpy(), ref_cb)
+        same_bits(single[i].cpu().numpy(), ref_cb)
+        np.testing.assert_array_equal(codes[i].cpu().numpy(), ref_codes)
+        np.testing.assert_array_equal(single_codes[i].cpu().numpy(), ref_codes)
+
+
+def test_kmeans_one_launch_rounding_cases():
+    """A Lloyd iteration inside the one-launch kernel on clusters whose means
+    fall exactly between two fp16 values (normal, subnormal, large, negative)
+    or at the top of the range: segment 0 of every vector is a constant
+    vector near one chosen codeword; the other segments are codewords exactly,
+    so every assignment is unambiguous."""
+    clusters = [  # (centre, member values)
+        (0.0, [2**-24, 2 * 2**-24]),            # subnormal tie -> 2^-23
+        (1.0, [1.0, 1.0 + 2**-10]),             # tie -> 1.0
+        (2.0, [2.0 + 2**-9, 2.0 + 2 * 2**-9]),  # tie -> 2 + 2^-8 (even)
+        (100.0, [100.0, 100.0 + 2**-4]),        # tie -> 100
+        (-3.0, [-3.0, -3.0 - 2**-9]),           # tie -> -3
+        (65504.0, [65504.0, 65504.0]),
+        (-500.0, [-500.0, -499.75, -499.5]),
+    ]
+    rng = np.random.default_rng(1500)
+    H, M, D = 1, 4, 128
+    cb0 = rng.standard_normal((H, M, 256, 32)).astype(np.float16)
+    cb0[0, 0] = np.float16(20000.0) + np.arange(256, dtype=np.float16)[:, None]   # far away
+    rows = []
+    for i, (centre, members) in enumerate(clusters):
+        cb0[0, 0, 10 + 20 * i] = centre
+        rows += members
+    N = len(rows)
+    x = np.empty((N, H, D), np.float16)
+    x[:, 0, :32] = np.array(rows, np.float16)[:, None]
+    for m in range(1, M):   # exact codewords
+        x[:, 0, 32 * m:32 * (m + 1)] = cb0[0, m, rng.integers(0, 256, N)]
+    ref_cb, ref_codes = oracle.kmeans(x, cb0, 1)
+    cb = dev(cb0)
+    _, codes = pq.pq_kmeans(dev(x), cb, 1)
+    torch.cuda.synchronize()
+    got = cb.cpu().numpy()
+    same_bits(got, ref_cb)
+    np.testing.assert_array_equal(codes.cpu().numpy(), ref_codes)
+    assert got[0, 0, 10, 0] == 2**-23 and got[0, 0, 30, 0] == 1.0
+    assert got[0, 0, 50, 0] == 2.0 + 2**-8 and got[0, 0, 70, 0] == 100.0
+    assert got[0, 0, 90, 0] == -3.0 and got[0, 0, 110, 0] == 65504.0
