@@ -415,6 +415,27 @@ def paged_leg(pq, torch, dev, steps, warmup, dense_gqa_us):
             leg["dense_step_us"] = dense_gqa_us
         if name == "ragged":
             leg["dense_step_us"] = timed(dense)
+            # the plain decode over the same caches (no new token): with one
+            # query head per KV head and 2048 pairs it runs the
+            # request-batched score kernel
+            ws_plain = torch.empty(max(pq.pq_attn_workspace_bytes(desc), 16), dtype=torch.uint8,
+                                   device=dev)
+
+            def paged_plain(t):
+                pq.pq_attn_decode_paged(t["q"], t["k_pool"], t["v_pool"], t["k_cb"], t["v_cb"],
+                                        t["table"], t["lens"], out, page_tokens=P,
+                                        workspace=ws_plain, stream=stream)
+
+            def dense_plain(t):
+                pq.pq_attn_decode(t["q"], t["k_codes"], t["v_codes"], t["k_cb"], t["v_cb"], t["lens"],
+                                  out, desc=desc, workspace=ws_plain, stream=stream)
+
+            for i in range(warmup):
+                paged_plain(reps[i % R])
+                dense_plain(reps[i % R])
+            leg["decode_us"] = timed(paged_plain)
+            leg["dense_decode_us"] = timed(dense_plain)
+            leg["decode_value"] = tokens / (leg["decode_us"] * 1e-6)
         res[name] = leg
     return res
 

@@ -7,6 +7,7 @@
 #include <cmath>
 
 #include "decode_kernel.hpp"
+#include "decode_mha_kernel.hpp"
 #include "encode_kernel.hpp"
 #include "kmeans_kernel.hpp"
 #include "plan.h"
@@ -58,6 +59,26 @@ DecodeFn pick_decode(int G, int M, int T, bool step, bool paged) {
   return step ? pick_gm<true, false>(G, M, T) : pick_gm<false, false>(G, M, T);
 }
 
+// The request-batched kernel (one query head per KV head) whose NT token
+// slots per thread cover a chunk of T tokens.
+template <int M, bool PAGED>
+DecodeFn pick_mha_nt(int T) {
+  constexpr int TPR = kDecodeThreads / kMhaRequests;
+  if (T <= TPR) return &decode_mha_kernel<M, kMhaRequests, 1, PAGED>;
+  if (T <= 2 * TPR) return &decode_mha_kernel<M, kMhaRequests, 2, PAGED>;
+  if (T <= 4 * TPR) return &decode_mha_kernel<M, kMhaRequests, 4, PAGED>;
+  if (T <= 8 * TPR) return &decode_mha_kernel<M, kMhaRequests, 8, PAGED>;
+  if constexpr (M == 4) {
+    if (T <= 16 * TPR) return &decode_mha_kernel<M, kMhaRequests, 16, PAGED>;
+  }
+  return nullptr;
+}
+
+DecodeFn pick_mha(int M, int T, bool paged) {
+  if (M == 4) return paged ? pick_mha_nt<4, true>(T) : pick_mha_nt<4, false>(T);
+  return paged ? pick_mha_nt<8, true>(T) : pick_mha_nt<8, false>(T);
+}
+
 // Launch; with events, the runtime stamps them at the kernel's own start and
 // end (hipExtLaunchKernel), which is what a kernel timer should see.
 pq_status launch(const void* fn, dim3 grid, dim3 block, void* arg, hipStream_t stream,
@@ -102,6 +123,7 @@ pq_status launch_partials(const AttnPlan& p, const void* q, const uint8_t* kc, c
   a.k_new = static_cast<const __half*>(k_new);
   a.v_new = static_cast<const __half*>(v_new);
   a.counters = counters;
+  a.B = p.B;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.Lmax = p.Lmax;
@@ -115,6 +137,13 @@ pq_status launch_partials(const AttnPlan& p, const void* q, const uint8_t* kc, c
     a.max_pages = pages->max_pages;
     a.n_pages = uint32_t(pages->n_pages);
   }
+  if (p.R > 1 && !step) {   // request-batched: grid (Hkv, C, request groups)
+    DecodeFn fn = pick_mha(p.M, p.T, pages != nullptr);
+    if (!fn) return PQ_ERR_UNSUPPORTED;
+    return launch(reinterpret_cast<const void*>(fn),
+                  dim3(unsigned(p.Hkv), unsigned(p.C), unsigned((p.B + p.R - 1) / p.R)),
+                  dim3(kDecodeThreads), &a, stream, start, stop);
+  }
   DecodeFn fn = pick_decode(p.G, p.M, p.T, step, pages != nullptr);
   if (!fn) return PQ_ERR_UNSUPPORTED;
   return launch(reinterpret_cast<const void*>(fn), dim3(unsigned(p.Hkv), unsigned(p.C), unsigned(p.B)),
@@ -122,12 +151,49 @@ pq_status launch_partials(const AttnPlan& p, const void* q, const uint8_t* kc, c
                 &a, stream, start, stop);
 }
 
+// The new token's K and V codes of a decode step, written by the encode
+// kernel at the slot of token lens[b] - 1 (dense or paged cache).
+pq_status launch_step_encode(const AttnPlan& p, const PagePlan* pages, const void* k_new,
+                             const void* v_new, uint8_t* kc, uint8_t* vc, const void* kcb,
+                             const void* vcb, const int32_t* lens, hipStream_t stream,
+                             hipEvent_t start) {
+  EncodeArgs e{};
+  e.x[0] = static_cast<const __half*>(k_new);
+  e.x[1] = static_cast<const __half*>(v_new);
+  e.cb[0] = static_cast<const __half*>(kcb);
+  e.cb[1] = static_cast<const __half*>(vcb);
+  e.codes[0] = kc;
+  e.codes[1] = vc;
+  e.N = p.B;
+  e.sxv = int64_t(p.Hkv) * p.D;
+  e.sxh = p.D;
+  e.scs = p.M;
+  e.lens = lens;
+  e.Lmax = p.Lmax;
+  e.Hkv = p.Hkv;
+  if (pages != nullptr) {
+    e.sch = pages->pool_head_bytes;
+    e.codes_bytes = int64_t(p.Hkv) * pages->pool_head_bytes;
+    e.table = pages->block_table;
+    e.max_pages = pages->max_pages;
+    e.page_shift = pages->shift;
+    e.n_pages = uint32_t(pages->n_pages);
+  } else {
+    e.sch = int64_t(p.Lmax) * p.M;
+    e.codes_bytes = int64_t(p.B) * p.Hkv * p.Lmax * p.M;
+  }
+  const unsigned tiles = unsigned((p.B + kEncodeVectors - 1) / kEncodeVectors);
+  const void* fn = p.M == 4 ? reinterpret_cast<const void*>(&encode_kernel<4, kEncodeVectors>)
+                            : reinterpret_cast<const void*>(&encode_kernel<8, kEncodeVectors>);
+  return launch(fn, dim3(unsigned(p.Hkv), tiles, 2u), dim3(128 * p.M), &e, stream, start, nullptr);
+}
+
 pq_status launch_reduce(int64_t rows, int32_t C, const float* pm, const float* pl, const float* po,
-                        float* out, hipStream_t stream) {
+                        float* out, hipStream_t stream, hipEvent_t stop = nullptr) {
   if (rows == 0) return PQ_OK;
   ReduceArgs a{pm, pl, po, out, C};
   return launch(reinterpret_cast<const void*>(&reduce_kernel), dim3(unsigned(rows)),
-                dim3(kReduceThreads), &a, stream);
+                dim3(kReduceThreads), &a, stream, nullptr, stop);
 }
 
 }  // namespace
@@ -245,6 +311,26 @@ static pq_status decode_step(const pq_attn_desc* desc, const void* q, const void
   if (!aligned16(k_new) || !aligned16(v_new)) return PQ_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
+  if (p.R > 1) {
+    // one query head per KV head and many pairs: the encode kernel writes the
+    // new codes, then the request-batched score kernel (and the merge) reads
+    // the cache that holds them
+    if (p.C > 1 && (!workspace || workspace_bytes < p.ws_step_bytes || !aligned16(workspace)))
+      return PQ_ERR_WORKSPACE;
+    st = launch_step_encode(p, pgp, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, s, e0);
+    if (st != PQ_OK) return st;
+    if (p.C == 1)
+      return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, nullptr, nullptr, nullptr, out,
+                             s, nullptr, e1, nullptr, nullptr, nullptr, pgp);
+    char* ws = static_cast<char*>(workspace);
+    float* pm = reinterpret_cast<float*>(ws + p.ws_m_off);
+    float* pl = reinterpret_cast<float*>(ws + p.ws_l_off);
+    float* po = reinterpret_cast<float*>(ws + p.ws_o_off);
+    st = launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, pm, pl, po, nullptr, s, nullptr,
+                         nullptr, nullptr, nullptr, nullptr, pgp);
+    if (st != PQ_OK) return st;
+    return launch_reduce(p.rows, p.C, pm, pl, po, out, s, e1);
+  }
   if (p.C == 1)
     return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, nullptr, nullptr, nullptr, out,
                            s, e0, e1, k_new, v_new, nullptr, pgp);

@@ -63,7 +63,7 @@ struct DecodeArgs {
   const __half* v_new;
   uint32_t* counters;        // [B*Hkv] chunk arrivals (step kernel with C > 1):
                              // zero on entry, zero again on exit
-  int32_t Hq, Hkv, Lmax, T, C;
+  int32_t B, Hq, Hkv, Lmax, T, C;
   float qscale;              // scale * log2(e)
   // Paged cache only: k_codes and v_codes are pools [Hkv][n_pages][P][M] and
   // token t of request b lives at slot block_table[b][t >> page_shift] * P +

@@ -45,6 +45,14 @@ struct EncodeArgs {
   int64_t N;
   int64_t codes_bytes;       // writes outside [0, codes_bytes) are skipped
   int64_t sxv, sxh, scs, sch;
+  // Decode step (lens non-null): vector n is request n's new token, written
+  // at the slot of token lens[n] - 1 (lens clamped to [0, Lmax]; 0: not
+  // written) of its cache -- slot n*Hkv*Lmax + t of a dense one, or through
+  // the block table of a paged one (table non-null).
+  const int32_t* lens;
+  const int32_t* table;      // [N][max_pages]
+  int32_t Lmax, Hkv, max_pages, page_shift;
+  uint32_t n_pages;
 };
 
 // -|c|^2/2 of the codewords of NCT tiles, given as A operands (lane (l16,
@@ -197,7 +205,19 @@ __global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
 
   for (int v = threadIdx.x; v < nv; v += 128 * M) {
     const int64_t n = n0 + v;
-    const int64_t s = a.slots ? a.slots[n] : n;
+    int64_t s = a.slots ? a.slots[n] : n;
+    if (a.lens != nullptr) {
+      int l = a.lens[n];
+      l = l < 0 ? 0 : (l > a.Lmax ? a.Lmax : l);
+      if (l == 0) continue;
+      const int t = l - 1;
+      if (a.table != nullptr) {
+        const uint32_t pg = min(uint32_t(a.table[n * a.max_pages + (t >> a.page_shift)]), a.n_pages - 1u);
+        s = (int64_t(pg) << a.page_shift) | int64_t(t & ((1 << a.page_shift) - 1));
+      } else {
+        s = n * a.Hkv * a.Lmax + t;
+      }
+    }
     if (s < 0 || (a.scs > 0 && s > a.codes_bytes / a.scs)) continue;
     const int64_t off = s * a.scs + int64_t(h) * a.sch;
     if (off < 0 || off + M > a.codes_bytes) continue;

@@ -57,13 +57,24 @@ pq_status plan_attn(const pq_attn_desc* d, AttnPlan* p) {
   p->Lmax = d->max_len;
   p->T = d->chunk > 0 ? (d->chunk < d->max_len ? d->chunk : d->max_len)
                       : pick_chunk(d->batch, d->n_kv_heads, d->max_len, kTargetBlocks, kChunkGranule);
+  // one query head per KV head and many (request, KV head) pairs: the
+  // request-batched score kernel, with chunks as long as it takes
+  p->R = 1;
+  if (G == 1 && int64_t(p->B) * p->Hkv >= kMhaMinPairs) {
+    const int tmax = p->M == 4 ? kMhaMaxChunkM4 : kMhaMaxChunkM8;
+    const int32_t tb = d->chunk > 0 ? p->T : (p->Lmax < tmax ? p->Lmax : tmax);
+    if (tb <= tmax) {
+      p->R = kMhaRequests;
+      p->T = tb;
+    }
+  }
   if (p->T > kMaxChunk) return PQ_ERR_UNSUPPORTED;
   p->C = int32_t((int64_t(p->Lmax) + p->T - 1) / p->T);
   p->scale = d->scale;
   p->rows = int64_t(p->B) * p->Hq;
   p->blocks = int64_t(p->B) * p->Hkv * p->C;
   if (p->blocks > kMaxBlocks || p->rows > kMaxBlocks) return PQ_ERR_UNSUPPORTED;
-  // score-kernel grid (Hkv, C, B): the y and z extents are 16-bit
+  // score-kernel grids (Hkv, C, B) and (Hkv, C, B / R): the y and z extents are 16-bit
   if (p->C > kMaxGridYZ || p->B > kMaxGridYZ) return PQ_ERR_UNSUPPORTED;
 
   // workspace: m and l [rows][C], o [rows][C][D], each 256-byte aligned

@@ -14,10 +14,19 @@ constexpr int kHeadDim = 128;   // D supported by the kernels
 constexpr int kCodes = 256;     // K codewords per segment codebook
 constexpr int kLenAlign = 16;   // cache capacity granularity, tokens
 constexpr int kMaxChunk = 4096; // longest chunk one score workgroup takes
+// Request batching for one query head per KV head: kMhaRequests requests of
+// a KV head per score workgroup once there are at least kMhaMinPairs
+// (request, KV head) pairs; chunks of up to kMhaMaxChunkM4 / M8 tokens.
+constexpr int kMhaRequests = 4;
+constexpr int64_t kMhaMinPairs = 1024;
+constexpr int kMhaMaxChunkM4 = 4096;
+constexpr int kMhaMaxChunkM8 = 2048;
 
 // A checked decode-attention shape with the chunking resolved.
 struct AttnPlan {
   int32_t B, Hq, Hkv, G, D, M, DS, K, Lmax, T, C;
+  int32_t R;            // requests per score workgroup of the plain decode (1, or
+                        // kMhaRequests for the request-batched kernel)
   float scale;
   int64_t rows;         // B * Hq
   int64_t blocks;       // score-kernel workgroups, B * Hkv * C

@@ -125,7 +125,8 @@ pq_status pq_attn_partials_timed(const pq_attn_desc* desc, const void* q,
  * descriptor as well. */
 size_t pq_attn_step_workspace_bytes(const pq_attn_desc* desc);
 
-/* One decode step with the new token appended, in one kernel launch.  For
+/* One decode step with the new token appended, normally in one kernel
+ * launch (see the exception below).  For
  * every request b with lens[b] >= 1 and every KV head g, the new token's K
  * and V (k_new[b][g], v_new[b][g]) are encoded by nearest codeword -- the
  * same decisions pq_encode takes (AQPIM page, sections 3.1 and 5.2 (2)) --
@@ -149,7 +150,11 @@ size_t pq_attn_step_workspace_bytes(const pq_attn_desc* desc);
  *                    run at the same time need their own workspaces.
  * Other arguments as for pq_attn_decode.  The workgroup whose chunk holds
  * the new token encodes it; with C > 1 the last workgroup of each (b, KV
- * head) to finish merges the chunk records into out. */
+ * head) to finish merges the chunk records into out.  Exception: with one
+ * query head per KV head and at least 1024 (request, KV head) pairs, the
+ * encode kernel writes the new codes first and the request-batched score
+ * kernel (then, with C > 1, the merge kernel) follows -- 2 or 3 launches,
+ * same results, the counters untouched. */
 pq_status pq_attn_decode_step(const pq_attn_desc* desc, const void* q, const void* k_new,
                               const void* v_new, uint8_t* k_codes, uint8_t* v_codes,
                               const void* k_cb, const void* v_cb, const int32_t* lens, float* out,

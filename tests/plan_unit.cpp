@@ -89,6 +89,26 @@ int main() {
   e.n_codes = 256; e.n_vec = int64_t(65535) * 256; EXPECT(plan_encode(&e, 256, &ep) == PQ_OK && ep.blocks_x == 65535);
   e.n_vec += 1;       EXPECT(plan_encode(&e, 256, &ep) == PQ_ERR_UNSUPPORTED);
 
+  // request batching: one query head per KV head and many pairs
+  {
+    pq_attn_desc md = base();
+    md.batch = 64; md.n_q_heads = 32; md.n_kv_heads = 32; md.n_sub = 4; md.max_len = 4096;
+    AttnPlan mp;
+    EXPECT(plan_attn(&md, &mp) == PQ_OK && mp.R == kMhaRequests && mp.T == 4096 && mp.C == 1);
+    md.n_sub = 8;
+    EXPECT(plan_attn(&md, &mp) == PQ_OK && mp.R == kMhaRequests && mp.T == 2048 && mp.C == 2);
+    md.n_sub = 4; md.max_len = 512;
+    EXPECT(plan_attn(&md, &mp) == PQ_OK && mp.R == kMhaRequests && mp.T == 512 && mp.C == 1);
+    md.chunk = 300;
+    EXPECT(plan_attn(&md, &mp) == PQ_OK && mp.R == kMhaRequests && mp.T == 300 && mp.C == 2);
+    md.chunk = 0; md.batch = 4;                     // 128 pairs: one request per workgroup
+    EXPECT(plan_attn(&md, &mp) == PQ_OK && mp.R == 1);
+    md.batch = 64; md.n_q_heads = 64;               // two query heads per KV head
+    EXPECT(plan_attn(&md, &mp) == PQ_OK && mp.R == 1);
+    md.n_q_heads = 32; md.max_len = 8192; md.chunk = 8192;   // longer than either kernel's chunk
+    EXPECT(plan_attn(&md, &mp) == PQ_ERR_UNSUPPORTED);
+  }
+
   // paged cache
   {
     pq_attn_desc pd = base();              // max_len 8192
