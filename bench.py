@@ -335,9 +335,10 @@ def paged_leg(pq, torch, dev, steps, warmup, dense_gqa_us):
     shuffled order), timed like the headline step: kernel-stamped events for
     the kernel, plain back-to-back steps for the step time.
       gqa     the headline workload on pages (paging overhead vs. dense)
-      ragged  64 requests of 512 or 4096 tokens, Lmax 4096: the paged and the
-              dense (padded) step on the same cache, and the capacity each
-              layout needs."""
+      ragged  64 requests of 512 or 4096 tokens, Lmax 4096, one query head
+              per KV head: the paged and the dense (padded) step on the same
+              cache (encode kernel + request-batched score kernel), the plain
+              decode of both, and the capacity each layout needs."""
     from synth import gen
     P = 256
     stream = torch.cuda.current_stream()
