@@ -174,3 +174,59 @@ def test_paged_step_with_many_single_head_pairs():
     ref = oracle.decode_attention_paged(inp["q"], exp_k, exp_v, inp["k_cb"], inp["v_cb"], table,
                                         inp["lens"], P)
     assert_attn_close(out.cpu().numpy(), ref, "paged step, many G=1 pairs")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_step_with_many_single_head_pairs_two_chunks(paged):
+    """M = 8 and 4096-token caches: the batched chunk is 2048 tokens, so the
+    step is the encode kernel, the batched partials and the merge; a
+    workspace reused for a second step."""
+    B, H, L, M, P = 64, 16, 4096, 8, 256
+    say(f"step, many G=1 pairs, two chunks, paged={paged}")
+    rng = np.random.default_rng(2500)
+    _, inp = gen.random_case(2500, batch=B, n_q_heads=H, n_kv_heads=H, max_len=L, n_sub=M,
+                             lens=ragged(rng, B, L))
+    lens = inp["lens"]
+    lens[6:10] = [2048, 2049, 4096, 2047]            # new tokens at the chunk edge and the end
+    q, kcb, vcb, lens_d = dev(inp["q"]), dev(inp["k_cb"]), dev(inp["v_cb"]), dev(lens)
+    if paged:
+        kp, vp, table, _ = gen.paged_cache(np.random.default_rng(2501), inp["k_codes"],
+                                           inp["v_codes"], lens, P)
+        kc_d, vc_d, table_d = dev(kp), dev(vp), dev(table)
+        desc, _ = pq.paged_desc(q, kc_d, kcb, table_d, P)
+    else:
+        kc_d, vc_d = dev(inp["k_codes"]), dev(inp["v_codes"])
+        desc = pq.attn_desc(q, kc_d, kcb)
+    assert pq.pq_attn_num_chunks(desc) == 2
+    ws = pq.step_workspace(desc, q.device)
+    exp_k = (kp if paged else inp["k_codes"]).copy()
+    exp_v = (vp if paged else inp["v_codes"]).copy()
+    for step in range(2):
+        xk, _, xv, _ = gen.step_tokens(np.random.default_rng(2502 + step), inp["k_cb"], inp["v_cb"], B)
+        if paged:
+            out = pq.pq_attn_decode_step_paged(q, dev(xk), dev(xv), kc_d, vc_d, kcb, vcb, table_d,
+                                               lens_d, page_tokens=P, workspace=ws)
+        else:
+            out = pq.pq_attn_decode_step(q, dev(xk), dev(xv), kc_d, vc_d, kcb, vcb, lens_d,
+                                         desc=desc, workspace=ws)
+        torch.cuda.synchronize()
+        ck, cv = oracle.encode(xk, inp["k_cb"]), oracle.encode(xv, inp["v_cb"])
+        for b, l in enumerate(lens):
+            if l >= 1:
+                if paged:
+                    slot = int(table[b, (l - 1) // P]) * P + (l - 1) % P
+                    exp_k[:, slot] = ck[b]
+                    exp_v[:, slot] = cv[b]
+                else:
+                    exp_k[b, :, l - 1] = ck[b]
+                    exp_v[b, :, l - 1] = cv[b]
+        np.testing.assert_array_equal(kc_d.cpu().numpy(), exp_k)
+        np.testing.assert_array_equal(vc_d.cpu().numpy(), exp_v)
+        if paged:
+            ref = oracle.decode_attention_paged(inp["q"], exp_k, exp_v, inp["k_cb"], inp["v_cb"],
+                                                table, lens, P)
+        else:
+            ref = oracle.decode_attention(inp["q"], exp_k, exp_v, inp["k_cb"], inp["v_cb"], lens)
+        assert_attn_close(out.cpu().numpy(), ref, f"two-chunk step {step}, paged={paged}")
+    rec = pq.pq_attn_workspace_bytes(desc)
+    assert (ws[rec:rec + B * H * 4] == 0).all()
