@@ -17,12 +17,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpqattn.so")
 
 PQ_OK = 0
+PQ_ERR_SHAPE_CODE = 2
 STATUS_NAMES = {0: "PQ_OK", 1: "PQ_ERR_NULL", 2: "PQ_ERR_SHAPE", 3: "PQ_ERR_UNSUPPORTED",
                 4: "PQ_ERR_WORKSPACE", 5: "PQ_ERR_HIP", 6: "PQ_ERR_ALIGN"}
 
 EXPORTED = ("pq_attn_num_chunks", "pq_attn_workspace_bytes", "pq_attn_decode",
             "pq_attn_partials", "pq_attn_partials_timed", "pq_attn_step_workspace_bytes",
             "pq_attn_decode_step", "pq_attn_decode_step_timed", "pq_attn_decode_paged",
+            "pq_attn_partials_paged",
             "pq_attn_decode_step_paged", "pq_attn_decode_step_paged_timed", "pq_attn_reduce",
             "pq_encode", "pq_encode_many", "pq_codebook_update", "pq_kmeans",
             "pq_kmeans_many", "pq_status_string")
@@ -93,6 +95,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pq_attn_decode_paged.argtypes = [ctypes.POINTER(PQAttnDesc), PT, P, P, P, P, P, P, P, P,
                                          ctypes.c_size_t, P]
     lib.pq_attn_decode_paged.restype = ctypes.c_int
+    lib.pq_attn_partials_paged.argtypes = [ctypes.POINTER(PQAttnDesc), PT, P, P, P, P, P, P, P, P,
+                                           P, P]
+    lib.pq_attn_partials_paged.restype = ctypes.c_int
     lib.pq_attn_decode_step_paged.argtypes = [ctypes.POINTER(PQAttnDesc), PT, P, P, P, P, P, P,
                                               P, P, P, P, ctypes.c_size_t, P]
     lib.pq_attn_decode_step_paged.restype = ctypes.c_int
@@ -341,6 +346,27 @@ def pq_attn_decode_paged(q, k_pool, v_pool, k_cb, v_cb, block_table, lens, out=N
         _ptr(v_cb), _ptr(lens), _ptr(out), _ptr(workspace), nbytes, _stream(stream))
     _check(st, "pq_attn_decode_paged")
     return out
+
+
+def pq_attn_partials_paged(q, k_pool, v_pool, k_cb, v_cb, block_table, lens, *, page_tokens,
+                           chunk=0, scale=None, stream=None):
+    """Chunk records over a paged cache (C entry point pq_attn_partials_paged).
+    Returns (part_m [B,Hq,C], part_l [B,Hq,C], part_o [B,Hq,C,D]), fp32."""
+    import torch
+    desc, table = paged_desc(q, k_pool, k_cb, block_table, page_tokens, chunk=chunk, scale=scale)
+    _check_paged_inputs(desc, table, q, k_pool, v_pool, k_cb, v_cb, block_table, lens)
+    C = pq_attn_num_chunks(desc)
+    if C < 1:
+        _check(PQ_ERR_SHAPE_CODE, "pq_attn_partials_paged")
+    B, Hq, D = desc.batch, desc.n_q_heads, desc.head_dim
+    part_m = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
+    part_l = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
+    part_o = torch.empty((B, Hq, C, D), dtype=torch.float32, device=q.device)
+    st = load_library().pq_attn_partials_paged(
+        ctypes.byref(desc), ctypes.byref(table), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_cb),
+        _ptr(v_cb), _ptr(lens), _ptr(part_m), _ptr(part_l), _ptr(part_o), _stream(stream))
+    _check(st, "pq_attn_partials_paged")
+    return part_m, part_l, part_o
 
 
 def pq_attn_decode_step_paged(q, k_new, v_new, k_pool, v_pool, k_cb, v_cb, block_table, lens,

@@ -272,6 +272,23 @@ pq_status pq_attn_partials(const pq_attn_desc* desc, const void* q, const uint8_
                          static_cast<hipStream_t>(stream));
 }
 
+pq_status pq_attn_partials_paged(const pq_attn_desc* desc, const pq_page_table* pages,
+                                 const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                                 const void* k_cb, const void* v_cb, const int32_t* lens,
+                                 float* part_m, float* part_l, float* part_o, void* stream) {
+  AttnPlan p;
+  pq_status st = plan_attn(desc, &p);
+  if (st != PQ_OK) return st;
+  PagePlan pg;
+  if ((st = plan_pages(p, pages, &pg)) != PQ_OK) return st;
+  st = check_attn_pointers(q, k_pool, v_pool, k_cb, v_cb, lens);
+  if (st != PQ_OK) return st;
+  if (!part_m || !part_l || !part_o) return PQ_ERR_NULL;
+  return launch_partials(p, q, k_pool, v_pool, k_cb, v_cb, lens, part_m, part_l, part_o, nullptr,
+                         static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, nullptr,
+                         nullptr, &pg);
+}
+
 pq_status pq_attn_partials_timed(const pq_attn_desc* desc, const void* q, const uint8_t* k_codes,
                                  const uint8_t* v_codes, const void* k_cb, const void* v_cb,
                                  const int32_t* lens, float* part_m, float* part_l, float* part_o,

@@ -206,6 +206,16 @@ pq_status pq_attn_decode_paged(const pq_attn_desc* desc, const pq_page_table* pa
                                const void* k_cb, const void* v_cb, const int32_t* lens, float* out,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* pq_attn_partials over a paged cache: the chunk records of pq_attn_partials
+ * for the cache the table describes (arguments as for pq_attn_decode_paged
+ * and pq_attn_partials).  With a table that names only some of a request's
+ * pages and lens counting past them, records of different calls merge with
+ * pq_attn_reduce like token shards (PAM page, section 2.2.3 (2)). */
+pq_status pq_attn_partials_paged(const pq_attn_desc* desc, const pq_page_table* pages,
+                                 const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                                 const void* k_cb, const void* v_cb, const int32_t* lens,
+                                 float* part_m, float* part_l, float* part_o, void* stream);
+
 /* pq_attn_decode_step over a paged cache: the new token's K and V codes go to
  * the slot of token lens[b] - 1 (its page must already be in the table), and
  * out is pq_attn_decode_paged's over the cache that now holds the token.

@@ -341,3 +341,15 @@ def test_kmeans_many_checks(lib):
     assert lib.pq_kmeans_many(ctypes.byref(d), 2, None, ok, 2, ok, None) == 1
     assert lib.pq_kmeans_many(ctypes.byref(d), 2, ok, ok, 2, arr(FAKE, None, FAKE), None) == 1
     assert lib.pq_kmeans_many(ctypes.byref(d), 2, ok, ok, 2, arr(FAKE, FAKE + 2, FAKE), None) == 6
+
+
+def test_paged_partials_checks(lib):
+    d = _desc()
+    ptrs = [FAKE] * 9        # q, k_pool, v_pool, k_cb, v_cb, lens, part_m, part_l, part_o
+    assert lib.pq_attn_partials_paged(ctypes.byref(d), None, *ptrs, None) == 1
+    assert lib.pq_attn_partials_paged(ctypes.byref(d), ctypes.byref(_pages(page_tokens=24)), *ptrs,
+                                      None) == 2
+    for which in range(9):
+        p = list(ptrs)
+        p[which] = None
+        assert lib.pq_attn_partials_paged(ctypes.byref(d), ctypes.byref(_pages()), *p, None) == 1

@@ -215,3 +215,37 @@ def test_paged_step_gqa_workload():
     dense = pq.pq_attn_decode_step(q, dev(xk), dev(xv), kc, vc, kcb, vcb, dev(lens))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out, dense.cpu().numpy())
+
+
+def test_paged_page_range_shards_merge_like_one_call():
+    """A page-range split: two calls over tables that each name half of every
+    request's pages (the other half's entries point at a spare page whose
+    tokens are cut off by lens), records merged with pq_attn_reduce, equal the
+    oracle's attention over the whole cache."""
+    B, H, L, M, P = 4, 8, 1024, 4, 128
+    say("paged page-range shards")
+    _, inp = gen.random_case(3000, batch=B, n_q_heads=2 * H, n_kv_heads=H, max_len=L, n_sub=M,
+                             lens=[1024, 700, 513, 129])
+    kp, vp, table, _ = gen.paged_cache(np.random.default_rng(3001), inp["k_codes"], inp["v_codes"],
+                                       inp["lens"], P)
+    lens = inp["lens"]
+    half = L // 2                                   # shard 0: tokens [0, 512); shard 1: [512, 1024)
+    q, kcb, vcb = (dev(inp[k]) for k in ("q", "k_cb", "v_cb"))
+    kp_d, vp_d = dev(kp), dev(vp)
+    # shard 0: the first half of every table row, lens cut at 512
+    t0 = np.ascontiguousarray(table[:, : half // P])
+    l0 = np.minimum(lens, half).astype(np.int32)
+    # shard 1: the second half, tokens renumbered from 0
+    t1 = np.ascontiguousarray(table[:, half // P:])
+    l1 = np.maximum(lens - half, 0).astype(np.int32)
+    recs = []
+    for t, l in ((t0, l0), (t1, l1)):
+        recs.append(pq.pq_attn_partials_paged(q, kp_d, vp_d, kcb, vcb, dev(t), dev(l),
+                                              page_tokens=P, chunk=256))
+    pm = torch.cat([r[0] for r in recs], dim=2).contiguous()
+    pl = torch.cat([r[1] for r in recs], dim=2).contiguous()
+    po = torch.cat([r[2] for r in recs], dim=2).contiguous()
+    out = pq.pq_attn_reduce(pm, pl, po)
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention_paged(inp["q"], kp, vp, inp["k_cb"], inp["v_cb"], table, lens, P)
+    assert_attn_close(out.cpu().numpy(), ref, "paged page-range shards")
