@@ -98,31 +98,68 @@ pq_status check_attn_pointers(const void* q, const void* kc, const void* vc, con
   return PQ_OK;
 }
 
-// One score-kernel launch.  pm/pl/po null: the normalised output goes to
-// out (C == 1).  step: the decode-step variant with the new token's K and V
-// (and, with C > 1, the arrival counters of the fused merge).
-pq_status launch_partials(const AttnPlan& p, const void* q, const uint8_t* kc, const uint8_t* vc,
-                          const void* kcb, const void* vcb, const int32_t* lens, float* pm,
-                          float* pl, float* po, float* out, hipStream_t stream,
-                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr,
-                          const void* k_new = nullptr, const void* v_new = nullptr,
-                          uint32_t* counters = nullptr, const PagePlan* pages = nullptr) {
-  const bool step = k_new != nullptr;
+// What one score-kernel launch reads and writes: the chunk records (pm, pl,
+// po) or, with C == 1, the normalised output (out); for the decode step the
+// new token's K and V and, for the fused merge (C > 1), the arrival
+// counters; for a paged cache its checked plan.
+struct ScoreIO {
+  const void* q = nullptr;
+  const uint8_t* kc = nullptr;
+  const uint8_t* vc = nullptr;
+  const void* kcb = nullptr;
+  const void* vcb = nullptr;
+  const int32_t* lens = nullptr;
+  const PagePlan* pages = nullptr;
+  float* pm = nullptr;
+  float* pl = nullptr;
+  float* po = nullptr;
+  float* out = nullptr;
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  uint32_t* counters = nullptr;
+};
+
+ScoreIO score_inputs(const void* q, const uint8_t* kc, const uint8_t* vc, const void* kcb,
+                     const void* vcb, const int32_t* lens, const PagePlan* pages) {
+  ScoreIO io;
+  io.q = q;
+  io.kc = kc;
+  io.vc = vc;
+  io.kcb = kcb;
+  io.vcb = vcb;
+  io.lens = lens;
+  io.pages = pages;
+  return io;
+}
+
+// The records of a C > 1 call inside the caller's workspace.
+void carve_records(const AttnPlan& p, void* workspace, ScoreIO& io) {
+  char* ws = static_cast<char*>(workspace);
+  io.pm = reinterpret_cast<float*>(ws + p.ws_m_off);
+  io.pl = reinterpret_cast<float*>(ws + p.ws_l_off);
+  io.po = reinterpret_cast<float*>(ws + p.ws_o_off);
+}
+
+// One score-kernel launch (the step variant when io.k_new is set).
+pq_status launch_score(const AttnPlan& p, const ScoreIO& io, hipStream_t stream,
+                       hipEvent_t start = nullptr, hipEvent_t stop = nullptr) {
+  const bool step = io.k_new != nullptr;
+  const PagePlan* pages = io.pages;
   DecodeArgs a{};
-  a.q = static_cast<const __half*>(q);
-  // the plain kernel never writes the code arrays
-  a.k_codes = const_cast<uint8_t*>(kc);
-  a.v_codes = const_cast<uint8_t*>(vc);
-  a.k_cb = static_cast<const __half*>(kcb);
-  a.v_cb = static_cast<const __half*>(vcb);
-  a.lens = lens;
-  a.part_m = pm;
-  a.part_l = pl;
-  a.part_o = po;
-  a.out = out;
-  a.k_new = static_cast<const __half*>(k_new);
-  a.v_new = static_cast<const __half*>(v_new);
-  a.counters = counters;
+  a.q = static_cast<const __half*>(io.q);
+  // only the step kernel writes the code arrays (the new token's slot)
+  a.k_codes = const_cast<uint8_t*>(io.kc);
+  a.v_codes = const_cast<uint8_t*>(io.vc);
+  a.k_cb = static_cast<const __half*>(io.kcb);
+  a.v_cb = static_cast<const __half*>(io.vcb);
+  a.lens = io.lens;
+  a.part_m = io.pm;
+  a.part_l = io.pl;
+  a.part_o = io.po;
+  a.out = io.out;
+  a.k_new = static_cast<const __half*>(io.k_new);
+  a.v_new = static_cast<const __half*>(io.v_new);
+  a.counters = io.counters;
   a.B = p.B;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
@@ -228,18 +265,16 @@ static pq_status attn_decode(const pq_attn_desc* desc, const pq_page_table* page
   if (st != PQ_OK) return st;
   if (!out) return PQ_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p.C == 1)
-    return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, nullptr, nullptr, nullptr,
-                           out, s, nullptr, nullptr, nullptr, nullptr, nullptr, pgp);
+  ScoreIO io = score_inputs(q, k_codes, v_codes, k_cb, v_cb, lens, pgp);
+  if (p.C == 1) {
+    io.out = out;
+    return launch_score(p, io, s);
+  }
   if (!workspace || workspace_bytes < p.ws_bytes || !aligned16(workspace)) return PQ_ERR_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  float* pm = reinterpret_cast<float*>(ws + p.ws_m_off);
-  float* pl = reinterpret_cast<float*>(ws + p.ws_l_off);
-  float* po = reinterpret_cast<float*>(ws + p.ws_o_off);
-  st = launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, pm, pl, po, nullptr, s, nullptr,
-                       nullptr, nullptr, nullptr, nullptr, pgp);
+  carve_records(p, workspace, io);
+  st = launch_score(p, io, s);
   if (st != PQ_OK) return st;
-  return launch_reduce(p.rows, p.C, pm, pl, po, out, s);
+  return launch_reduce(p.rows, p.C, io.pm, io.pl, io.po, out, s);
 }
 
 pq_status pq_attn_decode(const pq_attn_desc* desc, const void* q, const uint8_t* k_codes,
@@ -268,8 +303,11 @@ pq_status pq_attn_partials(const pq_attn_desc* desc, const void* q, const uint8_
   st = check_attn_pointers(q, k_codes, v_codes, k_cb, v_cb, lens);
   if (st != PQ_OK) return st;
   if (!part_m || !part_l || !part_o) return PQ_ERR_NULL;
-  return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, part_m, part_l, part_o, nullptr,
-                         static_cast<hipStream_t>(stream));
+  ScoreIO io = score_inputs(q, k_codes, v_codes, k_cb, v_cb, lens, nullptr);
+  io.pm = part_m;
+  io.pl = part_l;
+  io.po = part_o;
+  return launch_score(p, io, static_cast<hipStream_t>(stream));
 }
 
 pq_status pq_attn_partials_paged(const pq_attn_desc* desc, const pq_page_table* pages,
@@ -284,9 +322,11 @@ pq_status pq_attn_partials_paged(const pq_attn_desc* desc, const pq_page_table* 
   st = check_attn_pointers(q, k_pool, v_pool, k_cb, v_cb, lens);
   if (st != PQ_OK) return st;
   if (!part_m || !part_l || !part_o) return PQ_ERR_NULL;
-  return launch_partials(p, q, k_pool, v_pool, k_cb, v_cb, lens, part_m, part_l, part_o, nullptr,
-                         static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, nullptr,
-                         nullptr, &pg);
+  ScoreIO io = score_inputs(q, k_pool, v_pool, k_cb, v_cb, lens, &pg);
+  io.pm = part_m;
+  io.pl = part_l;
+  io.po = part_o;
+  return launch_score(p, io, static_cast<hipStream_t>(stream));
 }
 
 pq_status pq_attn_partials_timed(const pq_attn_desc* desc, const void* q, const uint8_t* k_codes,
@@ -299,9 +339,12 @@ pq_status pq_attn_partials_timed(const pq_attn_desc* desc, const void* q, const 
   st = check_attn_pointers(q, k_codes, v_codes, k_cb, v_cb, lens);
   if (st != PQ_OK) return st;
   if (!part_m || !part_l || !part_o) return PQ_ERR_NULL;
-  return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, part_m, part_l, part_o, nullptr,
-                         static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
-                         static_cast<hipEvent_t>(stop_event));
+  ScoreIO io = score_inputs(q, k_codes, v_codes, k_cb, v_cb, lens, nullptr);
+  io.pm = part_m;
+  io.pl = part_l;
+  io.po = part_o;
+  return launch_score(p, io, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
+                      static_cast<hipEvent_t>(stop_event));
 }
 
 size_t pq_attn_step_workspace_bytes(const pq_attn_desc* desc) {
@@ -328,36 +371,30 @@ static pq_status decode_step(const pq_attn_desc* desc, const void* q, const void
   if (!aligned16(k_new) || !aligned16(v_new)) return PQ_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
+  if (p.C > 1 && (!workspace || workspace_bytes < p.ws_step_bytes || !aligned16(workspace)))
+    return PQ_ERR_WORKSPACE;
+  ScoreIO io = score_inputs(q, k_codes, v_codes, k_cb, v_cb, lens, pgp);
+  if (p.C > 1) carve_records(p, workspace, io);
   if (p.R > 1) {
     // one query head per KV head and many pairs: the encode kernel writes the
     // new codes, then the request-batched score kernel (and the merge) reads
     // the cache that holds them
-    if (p.C > 1 && (!workspace || workspace_bytes < p.ws_step_bytes || !aligned16(workspace)))
-      return PQ_ERR_WORKSPACE;
     st = launch_step_encode(p, pgp, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, s, e0);
     if (st != PQ_OK) return st;
-    if (p.C == 1)
-      return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, nullptr, nullptr, nullptr, out,
-                             s, nullptr, e1, nullptr, nullptr, nullptr, pgp);
-    char* ws = static_cast<char*>(workspace);
-    float* pm = reinterpret_cast<float*>(ws + p.ws_m_off);
-    float* pl = reinterpret_cast<float*>(ws + p.ws_l_off);
-    float* po = reinterpret_cast<float*>(ws + p.ws_o_off);
-    st = launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, pm, pl, po, nullptr, s, nullptr,
-                         nullptr, nullptr, nullptr, nullptr, pgp);
+    if (p.C == 1) {
+      io.out = out;
+      return launch_score(p, io, s, nullptr, e1);
+    }
+    st = launch_score(p, io, s);
     if (st != PQ_OK) return st;
-    return launch_reduce(p.rows, p.C, pm, pl, po, out, s, e1);
+    return launch_reduce(p.rows, p.C, io.pm, io.pl, io.po, out, s, e1);
   }
-  if (p.C == 1)
-    return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens, nullptr, nullptr, nullptr, out,
-                           s, e0, e1, k_new, v_new, nullptr, pgp);
-  if (!workspace || workspace_bytes < p.ws_step_bytes || !aligned16(workspace))
-    return PQ_ERR_WORKSPACE;
-  char* ws = static_cast<char*>(workspace);
-  return launch_partials(p, q, k_codes, v_codes, k_cb, v_cb, lens,
-                         reinterpret_cast<float*>(ws + p.ws_m_off), reinterpret_cast<float*>(ws + p.ws_l_off),
-                         reinterpret_cast<float*>(ws + p.ws_o_off), out, s, e0, e1, k_new, v_new,
-                         reinterpret_cast<uint32_t*>(ws + p.ws_cnt_off), pgp);
+  // one launch: encode, attend and (C > 1) the fused merge
+  io.out = out;
+  io.k_new = k_new;
+  io.v_new = v_new;
+  if (p.C > 1) io.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + p.ws_cnt_off);
+  return launch_score(p, io, s, e0, e1);
 }
 
 pq_status pq_attn_decode_step(const pq_attn_desc* desc, const void* q, const void* k_new,

@@ -404,27 +404,12 @@ __device__ __forceinline__ f16x4 quad_transpose(uint32_t w0, uint32_t w1, int u)
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// -|c|^2 / 2 of the codeword whose MFMA B-operand pieces this lane holds
-// (4 dims per k-step), summed over the four lanes l16, l16+16, l16+32,
-// l16+48 that hold the rest of it.
-template <int KS>
-__device__ __forceinline__ float neg_half_norm2(const f16x4 (&b)[KS]) {
-  float p = 0.0f;
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const f16x2 lo = {b[s][0], b[s][1]};
-    const f16x2 hi = {b[s][2], b[s][3]};
-    p = __builtin_amdgcn_fdot2(lo, lo, p, false);
-    p = __builtin_amdgcn_fdot2(hi, hi, p, false);
-  }
-  p = pair_sum16(p);
-  p = pair_sum32(p);
-  return -0.5f * p;
-}
-
-// neg_half_norm2 of N codewords at once: every lane's partial sums first,
-// then each round of cross-lane swaps for all N, so the swaps' latencies
-// overlap instead of chaining.  Same operations per codeword, same result.
+// -|c|^2 / 2 of N codewords whose operand pieces this lane holds (codeword
+// n: 4 dims per k-step s in b[n][s]; the four lanes l16, l16+16, l16+32,
+// l16+48 hold the rest of it).  Every lane's partial sums (an fdot2 chain
+// over its dims) come first, then each round of cross-lane swaps for all N,
+// so the swaps' latencies overlap instead of chaining; each codeword gets
+// (p0 + p1) + (p2 + p3) of the four lanes' partial sums.
 template <int KS, int N>
 __device__ __forceinline__ void neg_half_norm2_n(const f16x4 (*b)[KS], float (&out)[N]) {
   float p[N];
@@ -477,12 +462,6 @@ __device__ __forceinline__ void merge_rows(const DecodeArgs& a, int64_t row0, in
   }
   if (threadIdx.x == 0)   // ready for the next call
     __hip_atomic_store(a.counters + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Two fp16 halves of an fp32 value: v ~= hi + lo to about 22 bits.
-__device__ __forceinline__ void split_f16(float v, _Float16& hi, _Float16& lo) {
-  hi = (_Float16)v;
-  lo = (_Float16)(v - (float)hi);
 }
 
 // G query heads per KV head, M segments, NT token slots per thread.  STEP:
