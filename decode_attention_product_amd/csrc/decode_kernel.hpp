@@ -20,11 +20,14 @@
 //   2. Scores: per token and head, the sum over m of LUT[m][code_m][h]; the
 //      K vectors are never rebuilt.
 //   3. Chunk max m_c and p_t = 2^(s_t - m_c) <= 1 (PAM page, section
-//      2.2.3 (1)); l_c = sum_t p_t.
+//      2.2.3 (1)).
 //   4. V histogram Hist[m][k][h] = sum of p_t over the chunk's tokens whose
 //      segment-m V code is k.  LDS float atomics are slow on gfx950, so p is
-//      added as a 32-bit fixed-point integer (p * 2^31 / Tmax, which cannot
-//      overflow a bin), two heads per 64-bit ds_add_u64.
+//      added as a 32-bit fixed-point integer (p * 2^31 / Tmax, rounded,
+//      which cannot overflow a bin), two heads per 64-bit ds_add_u64.  Every
+//      token lands in exactly one bin of segment 0, so l_c = sum_t p_t is
+//      the integer sum of those bins: exact, and the same quantised p that
+//      the contraction weights.
 //   5. Contraction o[h][m*DS + j] = sum_k Hist[m][k][h] * Cv_g[m][k][j] on
 //      the matrix cores.  This equals sum_t p_t V_t because every V_t is
 //      made of codewords.  The histogram enters as fp16 hi + lo parts, so
@@ -77,10 +80,17 @@ struct DecodeArgs {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// DPP lane moves inside a row of 16 lanes (no LDS traffic).
+// IEEE-754 maximum (v_maximum_f32 / v_maximum3_f32).  fmaxf lowers to maxnum,
+// which first quiets both operands with two extra v_max instructions; the
+// values here are never NaN, and maximum is exact on them and on +-inf.
+__device__ __forceinline__ float max_f(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// DPP lane moves inside a row of 16 lanes (no LDS traffic).  Every source
+// lane of the patterns used is valid, so bound_ctrl changes no value; it
+// lets the compiler fold the move into the VALU instruction that uses it.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
 }
 constexpr int kDppXor1 = 0xB1;   // quad_perm(1,0,3,2)
 constexpr int kDppXor2 = 0x4E;   // quad_perm(2,3,0,1)
@@ -110,15 +120,15 @@ __device__ __forceinline__ void wave_max_n(float (&v)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     float x = v[i];
-    x = fmaxf(x, dpp_f<kDppXor1>(x));
-    x = fmaxf(x, dpp_f<kDppXor2>(x));
-    x = fmaxf(x, dpp_f<kDppRor4>(x));
-    x = fmaxf(x, dpp_f<kDppRor8>(x));
+    x = max_f(x, dpp_f<kDppXor1>(x));
+    x = max_f(x, dpp_f<kDppXor2>(x));
+    x = max_f(x, dpp_f<kDppRor4>(x));
+    x = max_f(x, dpp_f<kDppRor8>(x));
     const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
     const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
     const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
     const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
-    v[i] = fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    v[i] = max_f(max_f(r0, r1), max_f(r2, r3));
   }
 }
 
@@ -151,7 +161,7 @@ __device__ __forceinline__ float key_float(int k) {
 
 template <int CTRL>
 __device__ __forceinline__ int dpp_int(int v) {
-  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, true);
 }
 
 // (score, index) -> the better of the pair and its DPP partner: the larger
@@ -227,7 +237,7 @@ __device__ __forceinline__ float merge_chunks(const float* pm, const float* pl, 
       o[c] = c < C ? rec_load<COH>(po + int64_t(c) * stride_o) : 0.0f;
     }
 #pragma unroll
-    for (int c = 0; c < kFew; ++c) m_star = fmaxf(m_star, m[c]);
+    for (int c = 0; c < kFew; ++c) m_star = max_f(m_star, m[c]);
     if (m_star != -INFINITY) {
 #pragma unroll
       for (int c = 0; c < kFew; ++c) {
@@ -238,7 +248,7 @@ __device__ __forceinline__ float merge_chunks(const float* pm, const float* pl, 
       }
     }
   } else {
-    for (int c = 0; c < C; ++c) m_star = fmaxf(m_star, rec_load<COH>(pm + c));
+    for (int c = 0; c < C; ++c) m_star = max_f(m_star, rec_load<COH>(pm + c));
     if (m_star != -INFINITY) {
       for (int c = 0; c < C; ++c) {
         const float mc = rec_load<COH>(pm + c);
@@ -376,7 +386,7 @@ __device__ __forceinline__ uint32_t quad_rotate(uint32_t v) {
   // quad_perm: lane i reads lane (i + D_ROT) & 3
   constexpr int ctrl = ((0 + D_ROT) & 3) | (((1 + D_ROT) & 3) << 2) | (((2 + D_ROT) & 3) << 4) |
                        (((3 + D_ROT) & 3) << 6);
-  return uint32_t(__builtin_amdgcn_mov_dpp(int(v), ctrl, 0xf, 0xf, false));
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(v), ctrl, 0xf, 0xf, true));
 }
 
 __device__ __forceinline__ f16x4 quad_transpose(uint32_t w0, uint32_t w1, int u) {
@@ -485,8 +495,11 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   constexpr int KSPLIT = NW / NTILE;          // waves sharing a tile, each a slice of the bins
   constexpr int KSL = K / KSPLIT;             // bins per slice
   static_assert(NTILE == 8 && KSPLIT == 2, "two contraction waves per output tile");
-  // fixed point: a bin collects at most NT*NTHR tokens of value <= 1
-  constexpr float kFix = float(1u << 31) / float(NT * NTHR);
+  // fixed point: a bin collects at most NT*NTHR tokens of value <= 1, each
+  // p * 2^kFixBits with kFixBits = 31 - log2(NT * NTHR)
+  static_assert((NT & (NT - 1)) == 0 && NTHR == 1024, "power-of-two token capacity");
+  constexpr float kFixBits = float(31 - 10 - (NT >= 2) - (NT >= 4) - (NT >= 8));
+  static_assert(NT <= 8, "token slots per thread");
   constexpr float kUnfix = float(NT * NTHR) / float(1u << 31);
 
   // Table and histogram live in separate LDS regions, so the histogram can be
@@ -504,7 +517,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   __shared__ __align__(16) uint32_t hist[HIST_WORDS];
   uint32_t* hist32 = hist;                                                 // [m][k] (G = 1)
   char* hist_bytes = reinterpret_cast<char*>(hist);                        // [k][R] u64 (G >= 2)
-  __shared__ float lsum[NW * G];              // per-wave partial sums of p
+  __shared__ uint32_t lsum[2 * G];            // l_c per head and bin slice, fixed point
   __shared__ __align__(16) int mkey[G];       // chunk max per head, as float_key
   __shared__ unsigned long long new_key[2][NW];  // step: per-wave argmax keys of the new K, V
   __shared__ uint32_t arrive_flag;
@@ -758,7 +771,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   for (int h = 0; h < G; ++h) {
     float mx = s[0][h];
 #pragma unroll
-    for (int i = 1; i < NT; ++i) mx = fmaxf(mx, s[i][h]);
+    for (int i = 1; i < NT; ++i) mx = max_f(mx, s[i][h]);
     m_c[h] = mx;
   }
   wave_max_n<G>(m_c);
@@ -786,24 +799,21 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   // hold registers through the gathers).
   // Wave w owns segment m_v and 16 output columns jt*16..+15.  With
   // 32-codeword steps lane (l16, q4) needs rows 8*q4 .. 8*q4+7 of column l16
-  // of each block; lane (4a + u, q4) loads rows 8*q4 + u and 8*q4 + 4 + u,
-  // columns 4a..4a+3 (8 contiguous bytes each), and two quad transposes
-  // deliver the column.
-  const __half* cvg = a.v_cb + int64_t(g) * M * K * DS;
+  // of each block: eight 16-bit loads straight into the halves of the
+  // operand registers (the 16 lanes of a row group read 32 contiguous
+  // bytes), so no VALU work puts them in MFMA order.
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  const _Float16* cvg = reinterpret_cast<const _Float16*>(a.v_cb) + int64_t(g) * M * K * DS;
   const int tile = wave % NTILE;
   const int ksl = wave / NTILE;               // bins [ksl * KSL, (ksl + 1) * KSL)
   const int m_v = tile % M;
   const int jt = tile / M;
-  const int qu = l16 & 3;
-  uint2 cvr[KSL / 32][2];
+  f16x8 cvb[KSL / 32];
 #pragma unroll
-  for (int s = 0; s < KSL / 32; ++s) {
+  for (int st = 0; st < KSL / 32; ++st) {
+    const _Float16* src = cvg + (int64_t(m_v) * K + ksl * KSL + st * 32 + 8 * q4) * DS + jt * 16 + l16;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const __half* src = cvg + (int64_t(m_v) * K + ksl * KSL + s * 32 + 8 * q4 + 4 * half + qu) * DS +
-                          jt * 16 + 4 * (l16 >> 2);
-      cvr[s][half] = *reinterpret_cast<const uint2*>(src);
-    }
+    for (int j = 0; j < 8; ++j) cvb[st][j] = src[j * DS];
   }
 
   // ---- 4. V histogram (fixed point, integer LDS atomics) -----------------------
@@ -816,27 +826,34 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   // immediate per pair.
   const int om = lane & (M - 1);
   const bool swap_pairs = GP >= 2 && ((lane / M) & 1) != 0;
-  // byte offset of rotated segment jm in the row of pair 0 (or pair 1 when
-  // swapping); pair 2q + b lives at (this ^ b*8M) + q*16M
+  // LDS byte address of rotated segment jm in the row of pair 0 (or pair 1
+  // when swapping) of codeword 0; pair 2q + b lives at (this ^ b*8M) +
+  // q*16M.  The empty asm hides the histogram's (constant) LDS address from
+  // the optimiser, which would otherwise merge it with the pair offsets into
+  // constants too large for the instruction's 16-bit offset field and spend
+  // two more VALU instructions per segment on them.
+  typedef __attribute__((address_space(3))) char lds_char;
+  const uint32_t hist_lds = uint32_t(reinterpret_cast<uintptr_t>((lds_char*)hist_bytes));
   uint32_t row_m[M];
 #pragma unroll
-  for (int jm = 0; jm < M; ++jm)
-    row_m[jm] = uint32_t(((jm + om) & (M - 1)) * 8) + (swap_pairs ? M * 8 : 0);
+  for (int jm = 0; jm < M; ++jm) {
+    row_m[jm] = hist_lds + uint32_t(((jm + om) & (M - 1)) * 8) + (swap_pairs ? M * 8 : 0);
+    asm("" : "+v"(row_m[jm]));
+  }
 
-  float l_thr[G];
+  // exponent offset: 2^(s - m_c + kFixBits) = p * 2^kFixBits is the bin
+  // value before rounding
+  float m_fix[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) l_thr[h] = 0.0f;
+  for (int h = 0; h < G; ++h) m_fix[h] = m_c[h] - kFixBits;
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     const int t = t_begin + i * NTHR + tid;
     if (t < t_end) {
       uint32_t u[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = fast_exp2(s[i][h] - m_c[h]);
-        l_thr[h] += p;
-        u[h] = uint32_t(fmaf(p, kFix, 0.5f));   // p * kFix <= 2^31 / Tmax, rounded
-      }
+      for (int h = 0; h < G; ++h)
+        u[h] = uint32_t(fast_exp2(s[i][h] - m_fix[h]) + 0.5f);   // <= 2^31 / Tmax, rounded
       if constexpr (G >= 2) {
         uint64_t pv[GP];
 #pragma unroll
@@ -853,16 +870,19 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
         const TokenCodes<M> rc = vcode[i].rotated(om);
 #pragma unroll
         for (int jm = 0; jm < M; ++jm) {
+          typedef __attribute__((address_space(3))) unsigned long long lds_u64;
           const uint32_t b0 = uint32_t(rc.get(jm)) * (R * 8) + row_m[jm];
-          char* p0 = hist_bytes + b0;
+          lds_u64* p0 = reinterpret_cast<lds_u64*>(uintptr_t(b0));
           if constexpr (GP == 1) {
-            atomicAdd(reinterpret_cast<unsigned long long*>(p0), (unsigned long long)pv[0]);
+            __hip_atomic_fetch_add(p0, (unsigned long long)pv[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           } else {
-            char* p1 = hist_bytes + (b0 ^ uint32_t(M * 8));
+            lds_u64* p1 = reinterpret_cast<lds_u64*>(uintptr_t(b0 ^ uint32_t(M * 8)));
 #pragma unroll
             for (int q = 0; q < GP / 2; ++q) {
-              atomicAdd(reinterpret_cast<unsigned long long*>(p0 + q * 16 * M), (unsigned long long)pv[2 * q]);
-              atomicAdd(reinterpret_cast<unsigned long long*>(p1 + q * 16 * M), (unsigned long long)pv[2 * q + 1]);
+              __hip_atomic_fetch_add(p0 + q * 2 * M, (unsigned long long)pv[2 * q],
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+              __hip_atomic_fetch_add(p1 + q * 2 * M, (unsigned long long)pv[2 * q + 1],
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
           }
         }
@@ -872,25 +892,8 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       }
     }
   }
-  // B operands of the contraction (the prefetched V codebook rows, put
-  // in MFMA order while the LDS drains the atomics)
-  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-  f16x8 cvb[KSL / 32];
-#pragma unroll
-  for (int st = 0; st < KSL / 32; ++st) {
-    const f16x4 b0 = quad_transpose(cvr[st][0].x, cvr[st][0].y, qu);
-    const f16x4 b1 = quad_transpose(cvr[st][1].x, cvr[st][1].y, qu);
-    cvb[st] = f16x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-  }
 
-  wave_sum_n<G>(l_thr);
-  if (lane < G) {
-    float mine = l_thr[0];
-#pragma unroll
-    for (int h = 1; h < G; ++h) mine = (lane == h) ? l_thr[h] : mine;
-    lsum[wave * G + lane] = mine;
-  }
-  __syncthreads();   // histogram and partial sums complete
+  __syncthreads();   // histogram complete
 
   // ---- 5. contraction with the V codebook on the matrix cores ----------------
   // A[i][k]: rows i < 8 carry the fp16 high part of Hist[m_v][k][i], rows
@@ -920,6 +923,26 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       }
     }
   }
+  // l_c: the waves of segment 0, first column tile (one per bin slice), add
+  // their bins in integers; lanes (h, q4) and (h + 8, q4) hold complementary
+  // bins of head h, so a row_ror:8 and two lane swaps complete the slice.
+  if (tile == 0) {
+    uint32_t lpart = 0;
+#pragma unroll
+    for (int st = 0; st < KSL / 32; ++st)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) lpart += raw[st][v];
+    lpart += uint32_t(__builtin_amdgcn_mov_dpp(int(lpart), kDppRor8, 0xf, 0xf, true));
+    {
+      const auto r = __builtin_amdgcn_permlane16_swap(lpart, lpart, false, false);
+      lpart = uint32_t(r[0]) + uint32_t(r[1]);
+    }
+    {
+      const auto r = __builtin_amdgcn_permlane32_swap(lpart, lpart, false, false);
+      lpart = uint32_t(r[0]) + uint32_t(r[1]);
+    }
+    if (lane < G) lsum[ksl * G + lane] = lpart;
+  }
   f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int st = 0; st < KSL / 32; ++st) {
@@ -935,8 +958,8 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     }
     // the hi lane sends its low parts, the lo lane its high parts; row_ror:8
     // delivers lane i+8's word to lane i and lane i's to lane i+8
-    const uint32_t r0 = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_row ? hw[0] : lw[0]), kDppRor8, 0xf, 0xf, false));
-    const uint32_t r1 = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_row ? hw[1] : lw[1]), kDppRor8, 0xf, 0xf, false));
+    const uint32_t r0 = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_row ? hw[0] : lw[0]), kDppRor8, 0xf, 0xf, true));
+    const uint32_t r1 = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_row ? hw[1] : lw[1]), kDppRor8, 0xf, 0xf, true));
     uint4 aw;
     aw.x = lo_row ? r0 : hw[0];
     aw.y = lo_row ? r1 : hw[1];
@@ -958,17 +981,6 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   // first slice's waves add it and write.
   float4* part_tile = reinterpret_cast<float4*>(lut);                      // [NTILE][64]
   if (ksl == 1) part_tile[tile * 64 + lane] = make_float4(o[0], o[1], o[2], o[3]);
-  __shared__ float fin[2 * G];
-  if (tid < G) {   // head tid: chunk max and the sum of the waves' partial sums
-    float mh = m_c[0];
-#pragma unroll
-    for (int x = 1; x < G; ++x) mh = (tid == x) ? m_c[x] : mh;
-    float lh = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) lh += lsum[w * G + tid];
-    fin[tid] = mh;
-    fin[G + tid] = lh;
-  }
   __syncthreads();
   if (ksl == 0) {
     const float4 other = part_tile[tile * 64 + lane];
@@ -978,7 +990,8 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * q4 + r;
       if (h < G) {
-        const float mh = fin[h], lh = fin[G + h];
+        const float mh = key_float(mkey[h]);
+        const float lh = float(lsum[h] + lsum[G + h]) * kUnfix;
         if (a.part_o == nullptr) {
           a.out[(row0 + h) * D + d] = lh > 0.0f ? o[r] * __builtin_amdgcn_rcpf(lh) : 0.0f;
         } else {

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
   {
     float mx[1] = {s[0]};
 #pragma unroll
-    for (int j = 1; j < NT; ++j) mx[0] = fmaxf(mx[0], s[j]);
+    for (int j = 1; j < NT; ++j) mx[0] = max_f(mx[0], s[j]);
     wave_max_n<1>(mx);
     if (lane == 0) atomicMax(&mkey[r], float_key(mx[0]));
   }
@@ -238,8 +238,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
       hw[v] = uint32_t(__builtin_bit_cast(uint16_t, h0)) | (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
       lw[v] = uint32_t(__builtin_bit_cast(uint16_t, e0)) | (uint32_t(__builtin_bit_cast(uint16_t, e1)) << 16);
     }
-    const uint32_t r0 = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_row ? hw[0] : lw[0]), kDppRor8, 0xf, 0xf, false));
-    const uint32_t r1 = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_row ? hw[1] : lw[1]), kDppRor8, 0xf, 0xf, false));
+    const uint32_t r0 = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_row ? hw[0] : lw[0]), kDppRor8, 0xf, 0xf, true));
+    const uint32_t r1 = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_row ? hw[1] : lw[1]), kDppRor8, 0xf, 0xf, true));
     uint4 aw;
     aw.x = lo_row ? r0 : hw[0];
     aw.y = lo_row ? r1 : hw[1];
