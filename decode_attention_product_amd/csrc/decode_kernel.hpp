@@ -80,6 +80,9 @@ struct DecodeArgs {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// log2 of a power of two (compile time)
+constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
+
 // IEEE-754 maximum (v_maximum_f32 / v_maximum3_f32).  fmaxf lowers to maxnum,
 // which first quiets both operands with two extra v_max instructions; the
 // values here are never NaN, and maximum is exact on them and on +-inf.
@@ -112,11 +115,10 @@ __device__ __forceinline__ float pair_sum32(float v) {
   return __builtin_bit_cast(float, int(r[0])) + __builtin_bit_cast(float, int(r[1]));
 }
 
-// Wave-wide max / sum of N values at once: all-reduce inside each row with
-// DPP, then combine the four rows' results read from lanes 0, 16, 32, 48.
-// Every lane receives the results.
+// Max of N values over each row of 16 lanes (every lane of the row receives
+// its row's results): DPP only, no cross-row steps.
 template <int N>
-__device__ __forceinline__ void wave_max_n(float (&v)[N]) {
+__device__ __forceinline__ void row_max_n(float (&v)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     float x = v[i];
@@ -124,28 +126,7 @@ __device__ __forceinline__ void wave_max_n(float (&v)[N]) {
     x = max_f(x, dpp_f<kDppXor2>(x));
     x = max_f(x, dpp_f<kDppRor4>(x));
     x = max_f(x, dpp_f<kDppRor8>(x));
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
-    v[i] = max_f(max_f(r0, r1), max_f(r2, r3));
-  }
-}
-
-template <int N>
-__device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    float x = v[i];
-    x += dpp_f<kDppXor1>(x);
-    x += dpp_f<kDppXor2>(x);
-    x += dpp_f<kDppRor4>(x);
-    x += dpp_f<kDppRor8>(x);
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
-    v[i] = (r0 + r1) + (r2 + r3);
+    v[i] = x;
   }
 }
 
@@ -377,41 +358,6 @@ __device__ __forceinline__ void token_scores(const float* lut, const Codes& code
   }
 }
 
-// 4x4 transpose of 16-bit values across the lanes of a quad: lane u holds
-// row u as (w0 = x[u][0] | x[u][1] << 16, w1 = x[u][2] | x[u][3] << 16) and
-// gets column u back as the four halves x[0][u], x[1][u], x[2][u], x[3][u].
-// Rotation d sends, from lane r, the word that lane (r - d) & 3 needs.
-template <int D_ROT>
-__device__ __forceinline__ uint32_t quad_rotate(uint32_t v) {
-  // quad_perm: lane i reads lane (i + D_ROT) & 3
-  constexpr int ctrl = ((0 + D_ROT) & 3) | (((1 + D_ROT) & 3) << 2) | (((2 + D_ROT) & 3) << 4) |
-                       (((3 + D_ROT) & 3) << 6);
-  return uint32_t(__builtin_amdgcn_mov_dpp(int(v), ctrl, 0xf, 0xf, true));
-}
-
-__device__ __forceinline__ f16x4 quad_transpose(uint32_t w0, uint32_t w1, int u) {
-  uint16_t e[4];
-  // d = 0: own row u, element u
-  {
-    const uint32_t w = (u >> 1) ? w1 : w0;
-    e[u & 3] = uint16_t((u & 1) ? (w >> 16) : (w & 0xffff));
-  }
-  uint32_t got[4];
-  // the sender r = (u + d) & 3 picks word ((r - d) & 3) >> 1 = (u >> 1) of the receiver
-#define PQ_ROT(DR)                                                           {                                                                            const int recv = (u - DR) & 3; /* receiver of this lane's word */          const uint32_t send = (recv >> 1) ? w1 : w0;                               got[DR] = quad_rotate<DR>(send);                                         }
-  PQ_ROT(1) PQ_ROT(2) PQ_ROT(3)
-#undef PQ_ROT
-#pragma unroll
-  for (int d = 1; d < 4; ++d) {
-    const int r = (u + d) & 3;   // row the word came from
-    e[r] = uint16_t((u & 1) ? (got[d] >> 16) : (got[d] & 0xffff));
-  }
-  f16x4 out;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) out[r] = __builtin_bit_cast(_Float16, e[r]);
-  return out;
-}
-
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // -|c|^2 / 2 of N codewords whose operand pieces this lane holds (codeword
@@ -497,9 +443,8 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   static_assert(NTILE == 8 && KSPLIT == 2, "two contraction waves per output tile");
   // fixed point: a bin collects at most NT*NTHR tokens of value <= 1, each
   // p * 2^kFixBits with kFixBits = 31 - log2(NT * NTHR)
-  static_assert((NT & (NT - 1)) == 0 && NTHR == 1024, "power-of-two token capacity");
-  constexpr float kFixBits = float(31 - 10 - (NT >= 2) - (NT >= 4) - (NT >= 8));
-  static_assert(NT <= 8, "token slots per thread");
+  static_assert((NT & (NT - 1)) == 0, "power-of-two token capacity");
+  constexpr float kFixBits = float(31 - ilog2(NT * NTHR));
   constexpr float kUnfix = float(NT * NTHR) / float(1u << 31);
 
   // Table and histogram live in separate LDS regions, so the histogram can be
@@ -774,12 +719,12 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     for (int i = 1; i < NT; ++i) mx = max_f(mx, s[i][h]);
     m_c[h] = mx;
   }
-  wave_max_n<G>(m_c);
-  if (lane < G) {   // one integer LDS max per (wave, head)
+  row_max_n<G>(m_c);
+  if (l16 < G) {   // lane h of each row of 16: one integer LDS max for head h
     float mine = m_c[0];
 #pragma unroll
-    for (int h = 1; h < G; ++h) mine = (lane == h) ? m_c[h] : mine;
-    atomicMax(&mkey[lane], float_key(mine));
+    for (int h = 1; h < G; ++h) mine = (l16 == h) ? m_c[h] : mine;
+    atomicMax(&mkey[l16], float_key(mine));
   }
   __syncthreads();
 #pragma unroll

@@ -15,7 +15,8 @@
 //
 // Thread t serves request t / TPR (TPR = 1024 / R threads, whole waves) and
 // its tokens chunk_start + t % TPR + j*TPR, j < NT.  LDS: the table
-// [m][r][k] (fp32), the histogram [r][m][k] (32-bit fixed point).
+// [m][r][k] (fp32), the histogram [r][m][k] (32-bit fixed point); a
+// request's l_c is the integer sum of its segment-0 bins.
 #pragma once
 
 #include "decode_kernel.hpp"
@@ -30,7 +31,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
   constexpr int DS = D / M;
   constexpr int NW = NTHR / 64;
   constexpr int TPR = NTHR / R;                 // threads per request
-  constexpr int WPR = TPR / 64;                 // waves per request
   constexpr int KSTEP_Q = DS / 16;              // MFMA k-steps of the table build
   constexpr int LUT_JOBS = (M * 16) / NW;       // (m, 16-codeword tile) jobs per wave
   constexpr int NTILE = M * DS / 16;            // 16-column output tiles of the contraction
@@ -38,15 +38,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
   constexpr int KSL = K / KSPLIT;
   static_assert(R == 4 || R == 8, "requests per workgroup");
   static_assert(NTILE == 8 && KSPLIT == 2, "two contraction waves per output tile");
-  // fixed point: a bin collects at most NT*TPR tokens of value <= 1
-  constexpr float kFix = float(1u << 31) / float(NT * TPR);
+  // fixed point: a bin collects at most NT*TPR tokens of value <= 1, each
+  // p * 2^kFixBits
+  static_assert((NT & (NT - 1)) == 0, "power-of-two token capacity");
+  constexpr float kFixBits = float(31 - ilog2(NT * TPR));
   constexpr float kUnfix = float(NT * TPR) / float(1u << 31);
 
   __shared__ __align__(16) float lut[M * R * K];         // [m][r][k]
   __shared__ __align__(16) uint32_t hist[R * M * K];     // [r][m][k]
-  __shared__ float lsum[NW];
+  __shared__ uint32_t lsum[2 * R];                       // l_c per request and bin slice
   __shared__ int mkey[R];
-  __shared__ float fin[2 * R];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -157,55 +158,41 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
     float mx[1] = {s[0]};
 #pragma unroll
     for (int j = 1; j < NT; ++j) mx[0] = max_f(mx[0], s[j]);
-    wave_max_n<1>(mx);
-    if (lane == 0) atomicMax(&mkey[r], float_key(mx[0]));
+    row_max_n<1>(mx);
+    if (l16 == 0) atomicMax(&mkey[r], float_key(mx[0]));
   }
   __syncthreads();
   const float m_r = key_float(mkey[r]);
 
-  // V codebook operands of the contraction (as in the per-request kernel)
-  const __half* cvg = a.v_cb + int64_t(g) * M * K * DS;
+  // V codebook operands of the contraction, in MFMA order by 16-bit loads
+  // (as in the per-request kernel)
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  const _Float16* cvg = reinterpret_cast<const _Float16*>(a.v_cb) + int64_t(g) * M * K * DS;
   const int tile = wave % NTILE;
   const int ksl = wave / NTILE;
   const int m_v = tile % M;
   const int jt = tile / M;
-  const int qu = l16 & 3;
-  uint2 cvr[KSL / 32][2];
+  f16x8 cvb[KSL / 32];
 #pragma unroll
   for (int st = 0; st < KSL / 32; ++st) {
+    const _Float16* src = cvg + (int64_t(m_v) * K + ksl * KSL + st * 32 + 8 * q4) * DS + jt * 16 + l16;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const __half* src = cvg + (int64_t(m_v) * K + ksl * KSL + st * 32 + 8 * q4 + 4 * half + qu) * DS +
-                          jt * 16 + 4 * (l16 >> 2);
-      cvr[st][half] = *reinterpret_cast<const uint2*>(src);
-    }
+    for (int j = 0; j < 8; ++j) cvb[st][j] = src[j * DS];
   }
 
   // ---- 4. probabilities and the request's V histogram ----------------------------------
-  float l_thr[1] = {0.0f};
+  const float m_fix = m_r - kFixBits;   // 2^(s - m_fix) = p * 2^kFixBits
   uint32_t* hr = hist + r * M * K;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int t = t_begin + li + j * TPR;
     if (t < t_end) {
-      const float p = fast_exp2(s[j] - m_r);
-      l_thr[0] += p;
-      const uint32_t u = uint32_t(fmaf(p, kFix, 0.5f));
+      const uint32_t u = uint32_t(fast_exp2(s[j] - m_fix) + 0.5f);
 #pragma unroll
       for (int m = 0; m < M; ++m) atomicAdd(hr + m * K + vcode[j].get(m), u);
     }
   }
-  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-  f16x8 cvb[KSL / 32];
-#pragma unroll
-  for (int st = 0; st < KSL / 32; ++st) {
-    const f16x4 v0 = quad_transpose(cvr[st][0].x, cvr[st][0].y, qu);
-    const f16x4 v1 = quad_transpose(cvr[st][1].x, cvr[st][1].y, qu);
-    cvb[st] = f16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-  }
-  wave_sum_n<1>(l_thr);
-  if (lane == 0) lsum[wave] = l_thr[0];
-  __syncthreads();   // histograms and partial sums complete
+  __syncthreads();   // histograms complete
 
   // ---- 5. contraction with the V codebook on the matrix cores ----------------------
   // A rows i < 8: fp16 high part of request i's bins, rows i >= 8 the low
@@ -224,6 +211,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
       const uint4 w = *reinterpret_cast<const uint4*>(hist + (hh * M + m_v) * K + k0);
       raw[st][0] = w.x; raw[st][1] = w.y; raw[st][2] = w.z; raw[st][3] = w.w;
     }
+  }
+  // l_c of request hh: the segment-0 waves of the first column tile add
+  // their bins in integers (lanes hh and hh + 8 hold complementary bins)
+  if (tile == 0) {
+    uint32_t lpart = 0;
+#pragma unroll
+    for (int st = 0; st < KSL / 32; ++st)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) lpart += raw[st][v];
+    lpart += uint32_t(__builtin_amdgcn_mov_dpp(int(lpart), kDppRor8, 0xf, 0xf, true));
+    {
+      const auto x = __builtin_amdgcn_permlane16_swap(lpart, lpart, false, false);
+      lpart = uint32_t(x[0]) + uint32_t(x[1]);
+    }
+    {
+      const auto x = __builtin_amdgcn_permlane32_swap(lpart, lpart, false, false);
+      lpart = uint32_t(x[0]) + uint32_t(x[1]);
+    }
+    if (lane < R) lsum[ksl * R + lane] = lpart;
   }
   f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -256,13 +262,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
   // ---- 6. write (m, l, o) or the normalised output, per request ----------------------
   float4* part_tile = reinterpret_cast<float4*>(lut);   // [NTILE][64]; the table is dead
   if (ksl == 1) part_tile[tile * 64 + lane] = make_float4(o[0], o[1], o[2], o[3]);
-  if (tid < R) {
-    fin[tid] = key_float(mkey[tid]);
-    float lh = 0.0f;
-#pragma unroll
-    for (int w = 0; w < WPR; ++w) lh += lsum[tid * WPR + w];
-    fin[R + tid] = lh;
-  }
   __syncthreads();
   if (ksl == 0) {
     const float4 other = part_tile[tile * 64 + lane];
@@ -273,7 +272,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
       const int rr = 4 * q4 + e;
       if (rr < R && b0 + rr < a.B) {
         const int64_t row = int64_t(b0 + rr) * a.Hq + g;
-        const float mh = fin[rr], lh = fin[R + rr];
+        const float mh = key_float(mkey[rr]);
+        const float lh = float(lsum[rr] + lsum[R + rr]) * kUnfix;
         if (a.part_o == nullptr) {
           a.out[row * D + d] = lh > 0.0f ? o[e] * __builtin_amdgcn_rcpf(lh) : 0.0f;
         } else {
