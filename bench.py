@@ -14,6 +14,10 @@ K=256).  Inputs live in HBM before timing starts; N seeded replicas of every
 input are rotated so that the working set (>= 512 MiB) is twice the 256 MB
 Infinity Cache and each step reads its codes from HBM.
 
+Further legs in the same line: "long_context" (the same one-launch step on
+the long-context split-K workload, B=1, Hq=64, Hkv=8, L=131072, M=4, 64
+chunks of 2048 tokens per KV head), "paged", "encode" and "kmeans".
+
 Prints one JSON line.  `value` = KV tokens scanned per second over the timed
 steps (sum of lens per step / step time).  `roofline` is the step kernel's
 algorithmic bytes per launch over its average duration, timed with HIP
@@ -149,6 +153,7 @@ def main():
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache leg")
     ap.add_argument("--paged-steps", type=int, default=500)
     ap.add_argument("--no-kmeans", action="store_true", help="skip the codebook-learning leg")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context step leg")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run 3 device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -295,6 +300,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         result["copy_probe_bytes"] = n
+    if not args.no_long and wid != 4:
+        result["long_context"] = long_context_leg(pq, torch, dev, args.paged_steps, args.warmup)
     if not args.no_paged:
         result["paged"] = paged_leg(pq, torch, dev, args.paged_steps, args.warmup,
                                     step_ms_plain * 1e3 if wid == 3 else None)
@@ -439,6 +446,66 @@ def paged_leg(pq, torch, dev, steps, warmup, dense_gqa_us):
             leg["decode_value"] = tokens / (leg["decode_us"] * 1e-6)
         res[name] = leg
     return res
+
+
+def long_context_leg(pq, torch, dev, steps, warmup):
+    """The decode step on the long-context split-K workload (B=1, Hq=64,
+    Hkv=8, L=131072, M=4, chunks of 2048 tokens: 64 chunk records per KV
+    head merged in the same launch), timed like the headline step."""
+    from synth import gen
+    wid = 4
+    w = gen.WORKLOADS[wid]
+    B, Hq, Hkv, L, M, D = w.batch, w.n_q_heads, w.n_kv_heads, w.max_len, w.n_sub, w.head_dim
+    stream = torch.cuda.current_stream()
+    base = gen.workload_inputs(wid, with_encode=False)
+    lens_np = base["lens"]
+    alg = algorithmic_bytes(w, lens_np)
+    R = max(2, math.ceil((512 << 20) / alg))
+    reps = []
+    for r in range(R):
+        inp = base if r == 0 else gen.workload_inputs(wid, replica=r, with_encode=False)
+        rng = np.random.default_rng([7200 + wid, r])
+        xk, _, xv, _ = gen.step_tokens(rng, inp["k_cb"], inp["v_cb"], B)
+        t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev)
+             for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")}
+        t["xk"], t["xv"] = torch.from_numpy(xk).to(dev), torch.from_numpy(xv).to(dev)
+        reps.append(t)
+    desc = pq.attn_desc(reps[0]["q"], reps[0]["k_codes"], reps[0]["k_cb"], chunk=2048)
+    ws = pq.step_workspace(desc, dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+
+    def step(t, ev=None):
+        pq.pq_attn_decode_step(t["q"], t["xk"], t["xv"], t["k_codes"], t["v_codes"], t["k_cb"],
+                               t["v_cb"], t["lens"], out, desc=desc, workspace=ws, stream=stream,
+                               events=ev)
+
+    for i in range(warmup):
+        step(reps[i % R])
+    hip = HipEvents()
+    raw = hip.create(2 * steps)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(reps[i % R], (raw[2 * i], raw[2 * i + 1]))
+    torch.cuda.synchronize()
+    kern_us = float(np.mean([hip.elapsed_ms(raw[2 * i], raw[2 * i + 1]) for i in range(steps)])) * 1e3
+    hip.destroy(raw)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(steps):
+        step(reps[i % R])
+    b.record(stream)
+    torch.cuda.synchronize()
+    step_us = a.elapsed_time(b) * 1e3 / steps
+    tokens = int(lens_np.sum())
+    achieved = alg / (kern_us * 1e-6) / 1e9
+    return {"workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} L={L} M={M}, chunk 2048, "
+                        f"{pq.pq_attn_num_chunks(desc)} chunks per KV head",
+            "value": tokens / (step_us * 1e-6), "unit": "KV tokens/s", "step_us": step_us,
+            "kernel_us": kern_us, "replicas": R,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": alg,
+                         "kernel": "decode_partials_kernel (decode-step variant)"}}
 
 
 def kmeans_leg(pq, torch, dev, n_iter=10, reps=20):

@@ -229,15 +229,32 @@ __device__ __forceinline__ float merge_chunks(const float* pm, const float* pl, 
       }
     }
   } else {
-    for (int c = 0; c < C; ++c) m_star = max_f(m_star, rec_load<COH>(pm + c));
-    if (m_star != -INFINITY) {
-      for (int c = 0; c < C; ++c) {
-        const float mc = rec_load<COH>(pm + c);
-        if (mc == -INFINITY) continue;
-        const float w = fast_exp2((mc - m_star) * kLog2e);
-        num = fmaf(w, rec_load<COH>(po + int64_t(c) * stride_o), num);
-        den = fmaf(w, rec_load<COH>(pl + c), den);
+    // one pass in batches of kFew records, all of a batch's loads issued
+    // together; the running sums are rescaled when the running max grows
+    for (int c0 = 0; c0 < C; c0 += kFew) {
+      float m[kFew], l[kFew], o[kFew];
+#pragma unroll
+      for (int j = 0; j < kFew; ++j) {
+        const int c = c0 + j;
+        m[j] = c < C ? rec_load<COH>(pm + c) : -INFINITY;
+        l[j] = c < C ? rec_load<COH>(pl + c) : 0.0f;
+        o[j] = c < C ? rec_load<COH>(po + int64_t(c) * stride_o) : 0.0f;
       }
+      float mb = m_star;
+#pragma unroll
+      for (int j = 0; j < kFew; ++j) mb = max_f(mb, m[j]);
+      if (mb == -INFINITY) continue;
+      const float r = fast_exp2((m_star - mb) * kLog2e);   // 0 while m_star = -inf
+      num *= r;
+      den *= r;
+#pragma unroll
+      for (int j = 0; j < kFew; ++j) {
+        if (m[j] == -INFINITY) continue;
+        const float w = fast_exp2((m[j] - mb) * kLog2e);
+        num = fmaf(w, o[j], num);
+        den = fmaf(w, l[j], den);
+      }
+      m_star = mb;
     }
   }
   return den > 0.0f ? num / den : 0.0f;
@@ -406,15 +423,81 @@ __device__ __forceinline__ TokenCodes<M> combine_new_codes(const unsigned long l
 }
 
 // The last workgroup of (request, KV head) bg: the normalised output of its
-// G query rows from the C chunk records.
+// G query rows from the C chunk records.  Up to 8 chunks, one thread per
+// output element with every record load in flight at once.  Beyond that
+// the record loads are the critical path (each a round trip to the
+// device-coherent level), so they are spread: the chunk maxima first go
+// through an LDS integer max per head (one load per (head, chunk)); then
+// thread (h, d4, cq) takes four output columns 4*d4.. of head h and the
+// chunks c = cq (mod 4), eight chunks' loads in flight per batch, and the
+// four cq lanes of a quad add their sums with two DPP steps.
 template <int G>
 __device__ __forceinline__ void merge_rows(const DecodeArgs& a, int64_t row0, int64_t bg) {
   constexpr int D = 128;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int64_t row = row0 + i / D;
-    const int d = i % D;
-    a.out[row * D + d] = merge_chunks<true>(a.part_m + row * a.C, a.part_l + row * a.C,
-                                            a.part_o + row * a.C * D + d, a.C, D);
+  const int C = a.C;
+  if (C <= 8) {
+    for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+      const int64_t row = row0 + i / D;
+      const int d = i % D;
+      a.out[row * D + d] = merge_chunks<true>(a.part_m + row * C, a.part_l + row * C,
+                                              a.part_o + row * C * D + d, C, D);
+    }
+  } else {
+    static_assert(G * D <= kDecodeThreads, "one thread per (head, column quad, chunk class)");
+    __shared__ int mstar[G];
+    if (threadIdx.x < G) mstar[threadIdx.x] = float_key(-INFINITY);
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * C; i += blockDim.x) {
+      const int h = i / C;
+      atomicMax(&mstar[h], float_key(rec_load<true>(a.part_m + (row0 + h) * C + (i - h * C))));
+    }
+    __syncthreads();
+    const int tid = threadIdx.x;
+    const int cq = tid & 3, d4 = (tid >> 2) & 31, h = tid >> 7;
+    if (h < G) {   // whole waves
+      const int64_t row = row0 + h;
+      const float ms = key_float(mstar[h]);
+      float num[4] = {0.0f, 0.0f, 0.0f, 0.0f}, den = 0.0f;
+      if (ms != -INFINITY) {
+        constexpr int kB = 8;
+        for (int c0 = cq; c0 < C; c0 += 4 * kB) {
+          float m[kB], l[kB], o[kB][4];
+#pragma unroll
+          for (int j = 0; j < kB; ++j) {
+            const int c = c0 + 4 * j;
+            const bool in = c < C;
+            m[j] = in ? rec_load<true>(a.part_m + row * C + c) : -INFINITY;
+            l[j] = in ? rec_load<true>(a.part_l + row * C + c) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              o[j][e] = in ? rec_load<true>(a.part_o + (row * C + c) * D + 4 * d4 + e) : 0.0f;
+          }
+#pragma unroll
+          for (int j = 0; j < kB; ++j) {
+            if (m[j] == -INFINITY) continue;
+            const float w = fast_exp2((m[j] - ms) * kLog2e);
+            den = fmaf(w, l[j], den);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) num[e] = fmaf(w, o[j][e], num[e]);
+          }
+        }
+      }
+      den += dpp_f<kDppXor1>(den);
+      den += dpp_f<kDppXor2>(den);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        num[e] += dpp_f<kDppXor1>(num[e]);
+        num[e] += dpp_f<kDppXor2>(num[e]);
+      }
+      if (cq == 0) {
+        float4 r;
+        r.x = den > 0.0f ? num[0] / den : 0.0f;
+        r.y = den > 0.0f ? num[1] / den : 0.0f;
+        r.z = den > 0.0f ? num[2] / den : 0.0f;
+        r.w = den > 0.0f ? num[3] / den : 0.0f;
+        *reinterpret_cast<float4*>(a.out + row * D + 4 * d4) = r;
+      }
+    }
   }
   if (threadIdx.x == 0)   // ready for the next call
     __hip_atomic_store(a.counters + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

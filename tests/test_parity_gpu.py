@@ -419,6 +419,22 @@ def test_step_gqa_workload():
     check_counters_zero(desc, ws)
 
 
+def test_step_long_context_workload():
+    say("step on the long-context workload (B=1 Hq=64 Hkv=8 L=131072 M=4, 64 chunks merged in the launch)")
+    w = gen.WORKLOADS[4]
+    inp = gen.workload_inputs(4, with_encode=False)
+    xk, sk, xv, sv = gen.step_tokens(np.random.default_rng(3002), inp["k_cb"], inp["v_cb"], 1)
+    lens = inp["lens"]
+    desc, ws, kc, vc, out = run_step(inp, xk, xv, lens, chunk=w.chunk)
+    assert pq.pq_attn_num_chunks(desc) == 64
+    exp_k, exp_v, ref = step_expected(inp, xk, xv, lens)
+    np.testing.assert_array_equal(kc[0, :, lens[0] - 1], exp_k[0, :, lens[0] - 1])
+    np.testing.assert_array_equal(vc[0, :, lens[0] - 1], exp_v[0, :, lens[0] - 1])
+    np.testing.assert_array_equal(kc[0, :, lens[0] - 1], sk[0])
+    assert_attn_close(out, ref, "long-context step")
+    check_counters_zero(desc, ws)
+
+
 def test_step_matches_encode_then_decode():
     """The fused step gives the codes of pq_encode_many and the output of
     pq_attn_decode over the same cache."""
@@ -453,6 +469,11 @@ STEP_EDGE = [
     (2, 4, 1024, 256, [256, 1, 1024, 300]),
     (1, 8, 512, 0, [512, 1, 0, 255]),
     (1, 4, 4096, 2048, [4096, 2048, 2049, 0]),
+    # more than 8 chunks: the merging workgroup's spread record loads
+    (8, 4, 4096, 128, [1, 4096, 2049, 0]),
+    (4, 8, 2048, 64, [100, 2048, 1, 1500]),
+    (2, 8, 1536, 128, [1536, 129, 0, 700]),
+    (1, 4, 2048, 128, [2048, 1, 1000, 0]),
 ]
 
 
