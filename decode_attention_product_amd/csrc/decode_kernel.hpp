@@ -422,17 +422,40 @@ __device__ __forceinline__ TokenCodes<M> combine_new_codes(const unsigned long l
   return t;
 }
 
+// Running merge state of chunk records: max m (natural-log units), and the
+// sums num[0..3] = sum_c w_c o_c, den = sum_c w_c l_c with w_c = exp(m_c - m).
+struct MergeState {
+  float m, num[4], den;
+};
+// (x, y) -> one state over both record sets; either may be empty (m = -inf)
+__device__ __forceinline__ MergeState merge_states(const MergeState& x, const MergeState& y) {
+  MergeState r;
+  r.m = max_f(x.m, y.m);
+  if (r.m == -INFINITY) return x;
+  const float sx = fast_exp2((x.m - r.m) * kLog2e), sy = fast_exp2((y.m - r.m) * kLog2e);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r.num[e] = x.num[e] * sx + y.num[e] * sy;
+  r.den = x.den * sx + y.den * sy;
+  return r;
+}
+
 // The last workgroup of (request, KV head) bg: the normalised output of its
 // G query rows from the C chunk records.  Up to 8 chunks, one thread per
 // output element with every record load in flight at once.  Beyond that
-// the record loads are the critical path (each a round trip to the
-// device-coherent level), so they are spread: the chunk maxima first go
-// through an LDS integer max per head (one load per (head, chunk)); then
-// thread (h, d4, cq) takes four output columns 4*d4.. of head h and the
-// chunks c = cq (mod 4), eight chunks' loads in flight per batch, and the
-// four cq lanes of a quad add their sums with two DPP steps.
+// the record loads are the critical path, so they are spread and widened:
+// thread (h, cq, d4) takes four output columns 4*d4.. of head h and the
+// chunks c = cq (mod 4), eight chunks per batch with all their loads in
+// flight, and keeps a running merge state (rescaled when its max grows).
+// Its column quad is one 16-byte load per chunk; the 32 lanes of a chunk
+// class read a record's 512 contiguous bytes.  The four classes then merge:
+// lanes l and l ^ 32 of a wave by one lane swap, the head's two waves
+// through LDS (scratch: G * 32 * 6 floats).
+// The 16-byte record loads are buffer loads with the sc1 cache policy, the
+// policy of the device-scope relaxed atomic loads that read m and l (and of
+// all of them for C <= 8): served from the device-coherent level, so they
+// see the records the other workgroups completed before their arrival.
 template <int G>
-__device__ __forceinline__ void merge_rows(const DecodeArgs& a, int64_t row0, int64_t bg) {
+__device__ __forceinline__ void merge_rows(const DecodeArgs& a, int64_t row0, int64_t bg, float* scratch) {
   constexpr int D = 128;
   const int C = a.C;
   if (C <= 8) {
@@ -443,60 +466,87 @@ __device__ __forceinline__ void merge_rows(const DecodeArgs& a, int64_t row0, in
                                               a.part_o + row * C * D + d, C, D);
     }
   } else {
-    static_assert(G * D <= kDecodeThreads, "one thread per (head, column quad, chunk class)");
-    __shared__ int mstar[G];
-    if (threadIdx.x < G) mstar[threadIdx.x] = float_key(-INFINITY);
-    __syncthreads();
-    for (int i = threadIdx.x; i < G * C; i += blockDim.x) {
-      const int h = i / C;
-      atomicMax(&mstar[h], float_key(rec_load<true>(a.part_m + (row0 + h) * C + (i - h * C))));
-    }
-    __syncthreads();
+    static_assert(G * D <= kDecodeThreads, "one thread per (head, chunk class, column quad)");
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    constexpr int kSc1 = 16;              // buffer cache policy bit SC1
+    constexpr int kRsrcWord3 = 0x00020000;  // gfx9 buffer descriptor: raw dword access
     const int tid = threadIdx.x;
-    const int cq = tid & 3, d4 = (tid >> 2) & 31, h = tid >> 7;
+    const int d4 = tid & 31, cq = (tid >> 5) & 3, h = tid >> 7;
+    const bool second = (tid >> 6) & 1;   // the head's wave with classes 2, 3
+    MergeState st = {-INFINITY, {0.0f, 0.0f, 0.0f, 0.0f}, 0.0f};
+    const int64_t row = row0 + h;
     if (h < G) {   // whole waves
-      const int64_t row = row0 + h;
-      const float ms = key_float(mstar[h]);
-      float num[4] = {0.0f, 0.0f, 0.0f, 0.0f}, den = 0.0f;
-      if (ms != -INFINITY) {
-        constexpr int kB = 8;
-        for (int c0 = cq; c0 < C; c0 += 4 * kB) {
-          float m[kB], l[kB], o[kB][4];
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          a.part_o + row * C * D, (short)0, C * D * 4, kRsrcWord3);
+      constexpr int kB = 8;
+      for (int c0 = cq; c0 < C; c0 += 4 * kB) {
+        float m[kB], l[kB];
+        f32x4v o[kB];
 #pragma unroll
-          for (int j = 0; j < kB; ++j) {
-            const int c = c0 + 4 * j;
-            const bool in = c < C;
-            m[j] = in ? rec_load<true>(a.part_m + row * C + c) : -INFINITY;
-            l[j] = in ? rec_load<true>(a.part_l + row * C + c) : 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              o[j][e] = in ? rec_load<true>(a.part_o + (row * C + c) * D + 4 * d4 + e) : 0.0f;
-          }
-#pragma unroll
-          for (int j = 0; j < kB; ++j) {
-            if (m[j] == -INFINITY) continue;
-            const float w = fast_exp2((m[j] - ms) * kLog2e);
-            den = fmaf(w, l[j], den);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) num[e] = fmaf(w, o[j][e], num[e]);
-          }
+        for (int j = 0; j < kB; ++j) {
+          const int c = c0 + 4 * j;
+          const bool in = c < C;
+          m[j] = in ? rec_load<true>(a.part_m + row * C + c) : -INFINITY;
+          l[j] = in ? rec_load<true>(a.part_l + row * C + c) : 0.0f;
+          o[j] = in ? __builtin_amdgcn_raw_buffer_load_b128(rs, (c * D + 4 * d4) * 4, 0, kSc1)
+                    : f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
         }
+        float mb = st.m;
+#pragma unroll
+        for (int j = 0; j < kB; ++j) mb = max_f(mb, m[j]);
+        if (mb == -INFINITY) continue;
+        const float r = fast_exp2((st.m - mb) * kLog2e);   // 0 while st.m = -inf
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.num[e] *= r;
+        st.den *= r;
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+          if (m[j] == -INFINITY) continue;
+          const float w = fast_exp2((m[j] - mb) * kLog2e);
+          st.den = fmaf(w, l[j], st.den);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st.num[e] = fmaf(w, o[j][e], st.num[e]);
+        }
+        st.m = mb;
       }
-      den += dpp_f<kDppXor1>(den);
-      den += dpp_f<kDppXor2>(den);
+      // classes cq and cq ^ 1 (lanes l and l ^ 32): both lanes end with the
+      // merge of the pair, taken in the same order
+      MergeState x, y;
+      {
+        const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, st.m), __builtin_bit_cast(int, st.m), false, false);
+        x.m = __builtin_bit_cast(float, int(p[0])); y.m = __builtin_bit_cast(float, int(p[1]));
+      }
+      {
+        const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, st.den), __builtin_bit_cast(int, st.den), false, false);
+        x.den = __builtin_bit_cast(float, int(p[0])); y.den = __builtin_bit_cast(float, int(p[1]));
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        num[e] += dpp_f<kDppXor1>(num[e]);
-        num[e] += dpp_f<kDppXor2>(num[e]);
+        const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, st.num[e]), __builtin_bit_cast(int, st.num[e]), false, false);
+        x.num[e] = __builtin_bit_cast(float, int(p[0])); y.num[e] = __builtin_bit_cast(float, int(p[1]));
       }
-      if (cq == 0) {
-        float4 r;
-        r.x = den > 0.0f ? num[0] / den : 0.0f;
-        r.y = den > 0.0f ? num[1] / den : 0.0f;
-        r.z = den > 0.0f ? num[2] / den : 0.0f;
-        r.w = den > 0.0f ? num[3] / den : 0.0f;
-        *reinterpret_cast<float4*>(a.out + row * D + 4 * d4) = r;
+      st = merge_states(x, y);
+      if (second && d4 == (tid & 63)) {   // lanes 0..31 of the second wave
+        float* dst = scratch + (h * 32 + d4) * 6;
+        dst[0] = st.m; dst[1] = st.den;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[2 + e] = st.num[e];
       }
+    }
+    __syncthreads();
+    if (h < G && !second && d4 == (tid & 63)) {
+      const float* src = scratch + (h * 32 + d4) * 6;
+      MergeState o2;
+      o2.m = src[0]; o2.den = src[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o2.num[e] = src[2 + e];
+      st = merge_states(st, o2);
+      float4 r;
+      r.x = st.den > 0.0f ? st.num[0] / st.den : 0.0f;
+      r.y = st.den > 0.0f ? st.num[1] / st.den : 0.0f;
+      r.z = st.den > 0.0f ? st.num[2] / st.den : 0.0f;
+      r.w = st.den > 0.0f ? st.num[3] / st.den : 0.0f;
+      *reinterpret_cast<float4*>(a.out + row * D + 4 * d4) = r;
     }
   }
   if (threadIdx.x == 0)   // ready for the next call
@@ -626,7 +676,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       }
     }
     if constexpr (STEP) {
-      if (a.part_o != nullptr && arrive_last(a.counters + bg, a.C, &arrive_flag)) merge_rows<G>(a, row0, bg);
+      if (a.part_o != nullptr && arrive_last(a.counters + bg, a.C, &arrive_flag)) merge_rows<G>(a, row0, bg, lut);
     }
     return;
   }
@@ -1033,7 +1083,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     }
   }
   if constexpr (STEP) {
-    if (a.part_o != nullptr && arrive_last(a.counters + bg, a.C, &arrive_flag)) merge_rows<G>(a, row0, bg);
+    if (a.part_o != nullptr && arrive_last(a.counters + bg, a.C, &arrive_flag)) merge_rows<G>(a, row0, bg, lut);
   }
 }
 
