@@ -450,8 +450,10 @@ def paged_leg(pq, torch, dev, steps, warmup, dense_gqa_us):
 
 def long_context_leg(pq, torch, dev, steps, warmup):
     """The decode step on the long-context split-K workload (B=1, Hq=64,
-    Hkv=8, L=131072, M=4, chunks of 2048 tokens: 64 chunk records per KV
-    head merged in the same launch), timed like the headline step."""
+    Hkv=8, L=131072, M=4), timed like the headline step: with the workload's
+    chunks of 2048 tokens (64 chunk records per KV head merged in the same
+    launch), and with the chunk length the library picks (4096: one
+    workgroup per CU)."""
     from synth import gen
     wid = 4
     w = gen.WORKLOADS[wid]
@@ -470,42 +472,51 @@ def long_context_leg(pq, torch, dev, steps, warmup):
              for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")}
         t["xk"], t["xv"] = torch.from_numpy(xk).to(dev), torch.from_numpy(xv).to(dev)
         reps.append(t)
-    desc = pq.attn_desc(reps[0]["q"], reps[0]["k_codes"], reps[0]["k_cb"], chunk=2048)
-    ws = pq.step_workspace(desc, dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-
-    def step(t, ev=None):
-        pq.pq_attn_decode_step(t["q"], t["xk"], t["xv"], t["k_codes"], t["v_codes"], t["k_cb"],
-                               t["v_cb"], t["lens"], out, desc=desc, workspace=ws, stream=stream,
-                               events=ev)
-
-    for i in range(warmup):
-        step(reps[i % R])
-    hip = HipEvents()
-    raw = hip.create(2 * steps)
-    torch.cuda.synchronize()
-    for i in range(steps):
-        step(reps[i % R], (raw[2 * i], raw[2 * i + 1]))
-    torch.cuda.synchronize()
-    kern_us = float(np.mean([hip.elapsed_ms(raw[2 * i], raw[2 * i + 1]) for i in range(steps)])) * 1e3
-    hip.destroy(raw)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for i in range(steps):
-        step(reps[i % R])
-    b.record(stream)
-    torch.cuda.synchronize()
-    step_us = a.elapsed_time(b) * 1e3 / steps
     tokens = int(lens_np.sum())
-    achieved = alg / (kern_us * 1e-6) / 1e9
-    return {"workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} L={L} M={M}, chunk 2048, "
-                        f"{pq.pq_attn_num_chunks(desc)} chunks per KV head",
-            "value": tokens / (step_us * 1e-6), "unit": "KV tokens/s", "step_us": step_us,
-            "kernel_us": kern_us, "replicas": R,
-            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": alg,
-                         "kernel": "decode_partials_kernel (decode-step variant)"}}
+
+    def run(chunk):
+        desc = pq.attn_desc(reps[0]["q"], reps[0]["k_codes"], reps[0]["k_cb"], chunk=chunk)
+        ws = pq.step_workspace(desc, dev)
+
+        def step(t, ev=None):
+            pq.pq_attn_decode_step(t["q"], t["xk"], t["xv"], t["k_codes"], t["v_codes"], t["k_cb"],
+                                   t["v_cb"], t["lens"], out, desc=desc, workspace=ws, stream=stream,
+                                   events=ev)
+
+        for i in range(warmup):
+            step(reps[i % R])
+        hip = HipEvents()
+        raw = hip.create(2 * steps)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            step(reps[i % R], (raw[2 * i], raw[2 * i + 1]))
+        torch.cuda.synchronize()
+        kern_us = float(np.mean([hip.elapsed_ms(raw[2 * i], raw[2 * i + 1]) for i in range(steps)])) * 1e3
+        hip.destroy(raw)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(steps):
+            step(reps[i % R])
+        b.record(stream)
+        torch.cuda.synchronize()
+        step_us = a.elapsed_time(b) * 1e3 / steps
+        achieved = alg / (kern_us * 1e-6) / 1e9
+        return {"chunk": chunk,
+                "n_chunks": pq.pq_attn_num_chunks(desc),
+                "value": tokens / (step_us * 1e-6), "unit": "KV tokens/s", "step_us": step_us,
+                "kernel_us": kern_us,
+                "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": alg,
+                             "kernel": "decode_partials_kernel (decode-step variant)"}}
+
+    leg = {"workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} L={L} M={M}", "replicas": R}
+    leg.update(run(w.chunk))
+    lib = run(0)
+    lib["chunk"] = "library"
+    leg["library_chunk"] = lib
+    return leg
 
 
 def kmeans_leg(pq, torch, dev, n_iter=10, reps=20):
