@@ -589,7 +589,9 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   // hit rows that differ mod 16; each lane walks the rows in a lane-rotated
   // order that guarantees it (step 4).  For G = 1 it is [m][k] 32-bit words.
   constexpr int R = M * GP;                                                // rows per codeword
-  constexpr int LUT_WORDS = M * K * G;
+  // the table region is reused for the contraction's partial tiles
+  // (NTILE * 64 float4) once the scores are in registers
+  constexpr int LUT_WORDS = M * K * G > NTILE * 64 * 4 ? M * K * G : NTILE * 64 * 4;
   constexpr int HIST_WORDS = G >= 2 ? K * R * 2 : M * K;
   __shared__ __align__(16) float lut[LUT_WORDS];
   __shared__ __align__(16) uint32_t hist[HIST_WORDS];

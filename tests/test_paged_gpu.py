@@ -169,6 +169,9 @@ STEP_PAGED = [
     (1, 4, 16, 512, 0, [1, 0, 17, 512]),
     (4, 8, 256, 4096, 1024, [257, 1024, 1025, 4096]),
     (2, 4, 4096, 8192, 2048, [4097, 4096, 2048, 1]),
+    # more than 8 chunks per (request, KV head): the spread merge
+    (8, 4, 64, 2048, 128, [1, 2048, 700, 0]),
+    (2, 8, 32, 1536, 64, [1536, 65, 33, 0]),
 ]
 
 

@@ -474,6 +474,7 @@ STEP_EDGE = [
     (4, 8, 2048, 64, [100, 2048, 1, 1500]),
     (2, 8, 1536, 128, [1536, 129, 0, 700]),
     (1, 4, 2048, 128, [2048, 1, 1000, 0]),
+    (1, 4, 4096, 1024, [4096, 1, 3000, 0]),   # partial tiles fill the whole table region
 ]
 
 
