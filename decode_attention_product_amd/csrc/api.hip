@@ -23,14 +23,22 @@ constexpr int kEncodeVectors = 256;   // vectors per encode workgroup (one wave 
 
 using DecodeFn = void (*)(DecodeArgs);
 
-template <int G, int M, int NT, bool STEP, bool PAGED>
+template <int G, int M, int NT, bool STEP, bool PAGED, int CPW = 1>
 DecodeFn kernel_for() {
-  if constexpr (PAGED) return &decode_paged_kernel<G, M, NT, STEP>;
-  else return &decode_partials_kernel<G, M, NT, STEP>;
+  if constexpr (PAGED) return &decode_paged_kernel<G, M, NT, STEP, CPW>;
+  else return &decode_partials_kernel<G, M, NT, STEP, CPW>;
 }
 
 template <int G, int M, bool STEP, bool PAGED>
-DecodeFn pick_nt(int T) {
+DecodeFn pick_nt(int T, int cpw) {
+  if constexpr (M == 4) {   // two chunks of exactly 1024 or 2048 tokens per workgroup
+    if (cpw == 2) {
+      if (T == kDecodeThreads) return kernel_for<G, M, 2, STEP, PAGED, 2>();
+      if (T == 2 * kDecodeThreads) return kernel_for<G, M, 4, STEP, PAGED, 2>();
+      return nullptr;
+    }
+  }
+  if (cpw != 1) return nullptr;
   if (T <= kDecodeThreads) return kernel_for<G, M, 1, STEP, PAGED>();
   if (T <= 2 * kDecodeThreads) return kernel_for<G, M, 2, STEP, PAGED>();
   if (T <= 4 * kDecodeThreads) return kernel_for<G, M, 4, STEP, PAGED>();
@@ -38,25 +46,38 @@ DecodeFn pick_nt(int T) {
 }
 
 template <bool STEP, bool PAGED>
-DecodeFn pick_gm(int G, int M, int T) {
+DecodeFn pick_gm(int G, int M, int T, int cpw) {
   switch (M * 16 + G) {
-    case 4 * 16 + 1: return pick_nt<1, 4, STEP, PAGED>(T);
-    case 4 * 16 + 2: return pick_nt<2, 4, STEP, PAGED>(T);
-    case 4 * 16 + 4: return pick_nt<4, 4, STEP, PAGED>(T);
-    case 4 * 16 + 8: return pick_nt<8, 4, STEP, PAGED>(T);
-    case 8 * 16 + 1: return pick_nt<1, 8, STEP, PAGED>(T);
-    case 8 * 16 + 2: return pick_nt<2, 8, STEP, PAGED>(T);
-    case 8 * 16 + 4: return pick_nt<4, 8, STEP, PAGED>(T);
-    case 8 * 16 + 8: return pick_nt<8, 8, STEP, PAGED>(T);
+    case 4 * 16 + 1: return pick_nt<1, 4, STEP, PAGED>(T, cpw);
+    case 4 * 16 + 2: return pick_nt<2, 4, STEP, PAGED>(T, cpw);
+    case 4 * 16 + 4: return pick_nt<4, 4, STEP, PAGED>(T, cpw);
+    case 4 * 16 + 8: return pick_nt<8, 4, STEP, PAGED>(T, cpw);
+    case 8 * 16 + 1: return pick_nt<1, 8, STEP, PAGED>(T, cpw);
+    case 8 * 16 + 2: return pick_nt<2, 8, STEP, PAGED>(T, cpw);
+    case 8 * 16 + 4: return pick_nt<4, 8, STEP, PAGED>(T, cpw);
+    case 8 * 16 + 8: return pick_nt<8, 8, STEP, PAGED>(T, cpw);
   }
   return nullptr;
 }
 
 // The kernel instance for (G, M), the chunk length T (T <= kMaxChunk), the
-// plain or decode-step variant and the dense or paged cache.
-DecodeFn pick_decode(int G, int M, int T, bool step, bool paged) {
-  if (paged) return step ? pick_gm<true, true>(G, M, T) : pick_gm<false, true>(G, M, T);
-  return step ? pick_gm<true, false>(G, M, T) : pick_gm<false, false>(G, M, T);
+// chunks per workgroup, the plain or decode-step variant and the dense or
+// paged cache.
+DecodeFn pick_decode(int G, int M, int T, int cpw, bool step, bool paged) {
+  if (paged) return step ? pick_gm<true, true>(G, M, T, cpw) : pick_gm<false, true>(G, M, T, cpw);
+  return step ? pick_gm<true, false>(G, M, T, cpw) : pick_gm<false, false>(G, M, T, cpw);
+}
+
+// Chunks per workgroup of the score kernel: two when one chunk per
+// workgroup would need more than one workgroup per CU (a second round of
+// workgroups, each with its own prologue and table build) and two chunks fit
+// (M = 4, chunks of exactly 1024 or 2048 tokens).  The chunk records are the
+// same either way.
+int chunks_per_workgroup(const AttnPlan& p) {
+  constexpr int64_t kCUs = 256;
+  if (p.M != 4 || p.C < 2) return 1;
+  if (p.T != kDecodeThreads && p.T != 2 * kDecodeThreads) return 1;
+  return int64_t(p.B) * p.Hkv * p.C > kCUs ? 2 : 1;
 }
 
 // The request-batched kernel (one query head per KV head) whose NT token
@@ -181,11 +202,12 @@ pq_status launch_score(const AttnPlan& p, const ScoreIO& io, hipStream_t stream,
                   dim3(unsigned(p.Hkv), unsigned(p.C), unsigned((p.B + p.R - 1) / p.R)),
                   dim3(kDecodeThreads), &a, stream, start, stop);
   }
-  DecodeFn fn = pick_decode(p.G, p.M, p.T, step, pages != nullptr);
+  const int cpw = chunks_per_workgroup(p);
+  DecodeFn fn = pick_decode(p.G, p.M, p.T, cpw, step, pages != nullptr);
   if (!fn) return PQ_ERR_UNSUPPORTED;
-  return launch(reinterpret_cast<const void*>(fn), dim3(unsigned(p.Hkv), unsigned(p.C), unsigned(p.B)),
-                dim3(kDecodeThreads),
-                &a, stream, start, stop);
+  return launch(reinterpret_cast<const void*>(fn),
+                dim3(unsigned(p.Hkv), unsigned((p.C + cpw - 1) / cpw), unsigned(p.B)),
+                dim3(kDecodeThreads), &a, stream, start, stop);
 }
 
 // The new token's K and V codes of a decode step, written by the encode

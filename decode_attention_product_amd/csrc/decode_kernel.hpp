@@ -260,8 +260,9 @@ __device__ __forceinline__ float merge_chunks(const float* pm, const float* pl, 
   return den > 0.0f ? num / den : 0.0f;
 }
 
-// Chunk-arrival count for one (request, KV head), called by every thread of
-// a workgroup after its chunk record has been stored with rec_store<true>.
+// Arrival count for one (request, KV head), called by every thread of a
+// workgroup after its chunk records have been stored with rec_store<true>;
+// C is the number of workgroups that arrive (one per CPW chunks).
 // Every wave first waits until its own stores have completed (vmcnt = 0:
 // acknowledged at the device-coherent level), then thread 0 adds 1 to the
 // counter with a device-scope atomic.  So when a workgroup's add returns
@@ -553,14 +554,17 @@ __device__ __forceinline__ void merge_rows(const DecodeArgs& a, int64_t row0, in
     __hip_atomic_store(a.counters + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// G query heads per KV head, M segments, NT token slots per thread.  STEP:
+// G query heads per KV head, M segments, NT token slots per thread, CPW
+// chunks per workgroup (NT / CPW slots each: slot i of a thread is in chunk
+// i / (NT / CPW) of its workgroup, every chunk exactly (NT / CPW) * 1024
+// tokens; CPW = 2 only with M = 4, where two histograms fit in LDS).  STEP:
 // the decode-step variant -- the workgroup whose chunk holds the new token
 // (slot lens[b] - 1) encodes the token's K and V into the cache first, and
 // with C > 1 the last workgroup of each (request, KV head) merges the chunk
 // records into the output.
 // PAGED: the codes are read (and the new token's written) through the block
 // table of a paged cache.
-template <int G, int M, int NT, bool STEP, bool PAGED>
+template <int G, int M, int NT, bool STEP, bool PAGED, int CPW>
 __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   constexpr int NTHR = kDecodeThreads;
   constexpr int D = 128;
@@ -574,11 +578,13 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   constexpr int KSPLIT = NW / NTILE;          // waves sharing a tile, each a slice of the bins
   constexpr int KSL = K / KSPLIT;             // bins per slice
   static_assert(NTILE == 8 && KSPLIT == 2, "two contraction waves per output tile");
-  // fixed point: a bin collects at most NT*NTHR tokens of value <= 1, each
-  // p * 2^kFixBits with kFixBits = 31 - log2(NT * NTHR)
-  static_assert((NT & (NT - 1)) == 0, "power-of-two token capacity");
-  constexpr float kFixBits = float(31 - ilog2(NT * NTHR));
-  constexpr float kUnfix = float(NT * NTHR) / float(1u << 31);
+  static_assert(CPW == 1 || (CPW == 2 && M == 4 && NT % 2 == 0), "two chunks per workgroup need M = 4");
+  constexpr int NTC = NT / CPW;               // token slots per thread in one chunk
+  // fixed point: a bin collects at most NTC*NTHR tokens of value <= 1, each
+  // p * 2^kFixBits with kFixBits = 31 - log2(NTC * NTHR)
+  static_assert((NTC & (NTC - 1)) == 0, "power-of-two token capacity");
+  constexpr float kFixBits = float(31 - ilog2(NTC * NTHR));
+  constexpr float kUnfix = float(NTC * NTHR) / float(1u << 31);
 
   // Table and histogram live in separate LDS regions, so the histogram can be
   // cleared while the workgroup still waits for its operands.
@@ -591,14 +597,16 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   constexpr int R = M * GP;                                                // rows per codeword
   // the table region is reused for the contraction's partial tiles
   // (NTILE * 64 float4) once the scores are in registers
-  constexpr int LUT_WORDS = M * K * G > NTILE * 64 * 4 ? M * K * G : NTILE * 64 * 4;
-  constexpr int HIST_WORDS = G >= 2 ? K * R * 2 : M * K;
+  constexpr int LUT_WORDS = M * K * G > CPW * NTILE * 64 * 4 ? M * K * G : CPW * NTILE * 64 * 4;
+  constexpr int HIST_WORDS = G >= 2 ? K * R * 2 : M * K;   // one chunk's histogram
   __shared__ __align__(16) float lut[LUT_WORDS];
-  __shared__ __align__(16) uint32_t hist[HIST_WORDS];
+  // 256-byte aligned: the pair bit of a row address (step 4) is a bit of the
+  // full LDS address
+  __shared__ __align__(256) uint32_t hist[CPW * HIST_WORDS];
   uint32_t* hist32 = hist;                                                 // [m][k] (G = 1)
   char* hist_bytes = reinterpret_cast<char*>(hist);                        // [k][R] u64 (G >= 2)
-  __shared__ uint32_t lsum[2 * G];            // l_c per head and bin slice, fixed point
-  __shared__ __align__(16) int mkey[G];       // chunk max per head, as float_key
+  __shared__ uint32_t lsum[CPW][2 * G];       // l_c per chunk, head and bin slice, fixed point
+  __shared__ __align__(16) int mkey[CPW][G];  // chunk max per head, as float_key
   __shared__ unsigned long long new_key[2][NW];  // step: per-wave argmax keys of the new K, V
   __shared__ uint32_t arrive_flag;
 
@@ -608,13 +616,14 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
 
-  // Grid (Hkv, C, B), dispatched x fastest: consecutive workgroups go to
+  // Grid (Hkv, C / CPW, B), dispatched x fastest: consecutive workgroups go to
   // different XCDs, so with Hkv a multiple of 8 every chunk of one KV head
   // lands on the same XCD and shares its L2 copy of the codebooks.
   const int g = blockIdx.x;
-  const int c = blockIdx.y;
+  const int c = blockIdx.y * CPW;             // first chunk of this workgroup
   const int b = blockIdx.z;
   const int t_begin = c * a.T;
+  const int n_own = min(CPW, a.C - c);        // chunks this workgroup owns
   const int64_t row0 = int64_t(b) * a.Hq + int64_t(g) * G;   // first query row
 
   // ---- 0. requests --------------------------------------------------------------
@@ -663,22 +672,23 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   }
 
   len = len < 0 ? 0 : (len > a.Lmax ? a.Lmax : len);
-  const int t_end = min(t_begin + a.T, len);
-  if (t_begin >= t_end) {   // empty chunk (uniform over the workgroup)
-    for (int i = tid; i < G * D; i += NTHR) {
-      const int h = i / D, d = i % D;
+  const int t_end = min(t_begin + n_own * a.T, len);
+  if (t_begin >= t_end) {   // empty chunks (uniform over the workgroup)
+    for (int i = tid; i < n_own * G * D; i += NTHR) {
+      const int cc = c + i / (G * D), h = (i / D) % G, d = i % D;
       if (a.part_o == nullptr) {
         a.out[(row0 + h) * D + d] = 0.0f;
       } else {
-        rec_store<STEP>(a.part_o + ((row0 + h) * a.C + c) * D + d, 0.0f);
+        rec_store<STEP>(a.part_o + ((row0 + h) * a.C + cc) * D + d, 0.0f);
         if (d == 0) {
-          rec_store<STEP>(a.part_m + (row0 + h) * a.C + c, -INFINITY);
-          rec_store<STEP>(a.part_l + (row0 + h) * a.C + c, 0.0f);
+          rec_store<STEP>(a.part_m + (row0 + h) * a.C + cc, -INFINITY);
+          rec_store<STEP>(a.part_l + (row0 + h) * a.C + cc, 0.0f);
         }
       }
     }
     if constexpr (STEP) {
-      if (a.part_o != nullptr && arrive_last(a.counters + bg, a.C, &arrive_flag)) merge_rows<G>(a, row0, bg, lut);
+      if (a.part_o != nullptr && arrive_last(a.counters + bg, int(gridDim.y), &arrive_flag))
+        merge_rows<G>(a, row0, bg, lut);
     }
     return;
   }
@@ -715,10 +725,10 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     }
   }
 
-  // the histogram is cleared while the operands are in flight
-  for (int i = tid; i < HIST_WORDS / 4; i += NTHR)
+  // the histograms are cleared while the operands are in flight
+  for (int i = tid; i < CPW * HIST_WORDS / 4; i += NTHR)
     reinterpret_cast<uint4*>(hist)[i] = make_uint4(0, 0, 0, 0);
-  if (tid < G) mkey[tid] = float_key(-INFINITY);
+  if (tid < CPW * G) mkey[tid / G][tid % G] = float_key(-INFINITY);
 
   // ---- 1. lookup table on the matrix cores ----------------------------------
   // Step kernel, chunk with the new token: row 8 of every product starts at
@@ -846,24 +856,29 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   }
 
   // ---- 3. chunk max and probabilities ----------------------------------------
-  float m_c[G];
+  float m_c[CPW][G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mx = s[0][h];
+  for (int p = 0; p < CPW; ++p) {
 #pragma unroll
-    for (int i = 1; i < NT; ++i) mx = max_f(mx, s[i][h]);
-    m_c[h] = mx;
-  }
-  row_max_n<G>(m_c);
-  if (l16 < G) {   // lane h of each row of 16: one integer LDS max for head h
-    float mine = m_c[0];
+    for (int h = 0; h < G; ++h) {
+      float mx = s[p * NTC][h];
 #pragma unroll
-    for (int h = 1; h < G; ++h) mine = (l16 == h) ? m_c[h] : mine;
-    atomicMax(&mkey[l16], float_key(mine));
+      for (int i = 1; i < NTC; ++i) mx = max_f(mx, s[p * NTC + i][h]);
+      m_c[p][h] = mx;
+    }
+    row_max_n<G>(m_c[p]);
+    if (l16 < G) {   // lane h of each row of 16: one integer LDS max for head h
+      float mine = m_c[p][0];
+#pragma unroll
+      for (int h = 1; h < G; ++h) mine = (l16 == h) ? m_c[p][h] : mine;
+      atomicMax(&mkey[p][l16], float_key(mine));
+    }
   }
   __syncthreads();
 #pragma unroll
-  for (int h = 0; h < G; ++h) m_c[h] = key_float(mkey[h]);
+  for (int p = 0; p < CPW; ++p)
+#pragma unroll
+    for (int h = 0; h < G; ++h) m_c[p][h] = key_float(mkey[p][h]);
   if constexpr (STEP) {
     if (has_new) {   // the new token's V codes (per-wave keys written before the barrier above)
       const TokenCodes<M> nv = combine_new_codes<M, NW>(new_key[1]);
@@ -923,17 +938,21 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
 
   // exponent offset: 2^(s - m_c + kFixBits) = p * 2^kFixBits is the bin
   // value before rounding
-  float m_fix[G];
+  float m_fix[CPW][G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) m_fix[h] = m_c[h] - kFixBits;
+  for (int p = 0; p < CPW; ++p)
+#pragma unroll
+    for (int h = 0; h < G; ++h) m_fix[p][h] = m_c[p][h] - kFixBits;
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     const int t = t_begin + i * NTHR + tid;
+    constexpr int kHistBytes = HIST_WORDS * 4;
+    const int pc = i / NTC;                   // chunk of this slot (compile time)
     if (t < t_end) {
       uint32_t u[G];
 #pragma unroll
       for (int h = 0; h < G; ++h)
-        u[h] = uint32_t(fast_exp2(s[i][h] - m_fix[h]) + 0.5f);   // <= 2^31 / Tmax, rounded
+        u[h] = uint32_t(fast_exp2(s[i][h] - m_fix[pc][h]) + 0.5f);   // <= 2^31 / Tmax, rounded
       if constexpr (G >= 2) {
         uint64_t pv[GP];
 #pragma unroll
@@ -951,7 +970,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
 #pragma unroll
         for (int jm = 0; jm < M; ++jm) {
           typedef __attribute__((address_space(3))) unsigned long long lds_u64;
-          const uint32_t b0 = uint32_t(rc.get(jm)) * (R * 8) + row_m[jm];
+          const uint32_t b0 = uint32_t(rc.get(jm)) * (R * 8) + row_m[jm] + uint32_t(pc * kHistBytes);
           lds_u64* p0 = reinterpret_cast<lds_u64*>(uintptr_t(b0));
           if constexpr (GP == 1) {
             __hip_atomic_fetch_add(p0, (unsigned long long)pv[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -968,7 +987,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
         }
       } else {
 #pragma unroll
-        for (int m = 0; m < M; ++m) atomicAdd(hist32 + m * K + vcode[i].get(m), u[0]);
+        for (int m = 0; m < M; ++m) atomicAdd(hist32 + pc * HIST_WORDS + m * K + vcode[i].get(m), u[0]);
       }
     }
   }
@@ -986,120 +1005,133 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   const int hh = l16 & 7;
   const bool lo_row = l16 >= 8;
   const int kh = lo_row ? 4 : 0;
-  uint32_t raw[KSL / 32][4];
+  float4* part_tile = reinterpret_cast<float4*>(lut);   // [CPW][NTILE][64]; the table is dead
+  f32x4 o_own[CPW];
 #pragma unroll
-  for (int st = 0; st < KSL / 32; ++st) {
-    const int k0 = ksl * KSL + st * 32 + 8 * q4 + kh;
+  for (int p = 0; p < CPW; ++p) {
+    const char* hb = hist_bytes + p * HIST_WORDS * 4;
+    const uint32_t* h32 = hist32 + p * HIST_WORDS;
+    uint32_t raw[KSL / 32][4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) raw[st][v] = 0;
-    if (hh < G) {
-      if constexpr (G >= 2) {
-        const char* src = hist_bytes + (k0 * R + (hh >> 1) * M + m_v) * 8 + (hh & 1) * 4;
+    for (int st = 0; st < KSL / 32; ++st) {
+      const int k0 = ksl * KSL + st * 32 + 8 * q4 + kh;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) raw[st][v] = *reinterpret_cast<const uint32_t*>(src + v * R * 8);
-      } else {
-        const uint4 w = *reinterpret_cast<const uint4*>(hist32 + m_v * K + k0);
-        raw[st][0] = w.x; raw[st][1] = w.y; raw[st][2] = w.z; raw[st][3] = w.w;
+      for (int v = 0; v < 4; ++v) raw[st][v] = 0;
+      if (hh < G) {
+        if constexpr (G >= 2) {
+          const char* src = hb + (k0 * R + (hh >> 1) * M + m_v) * 8 + (hh & 1) * 4;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) raw[st][v] = *reinterpret_cast<const uint32_t*>(src + v * R * 8);
+        } else {
+          const uint4 w = *reinterpret_cast<const uint4*>(h32 + m_v * K + k0);
+          raw[st][0] = w.x; raw[st][1] = w.y; raw[st][2] = w.z; raw[st][3] = w.w;
+        }
       }
     }
-  }
-  // l_c: the waves of segment 0, first column tile (one per bin slice), add
-  // their bins in integers; lanes (h, q4) and (h + 8, q4) hold complementary
-  // bins of head h, so a row_ror:8 and two lane swaps complete the slice.
-  if (tile == 0) {
-    uint32_t lpart = 0;
+    // l_c: the waves of segment 0, first column tile (one per bin slice), add
+    // their bins in integers; lanes (h, q4) and (h + 8, q4) hold complementary
+    // bins of head h, so a row_ror:8 and two lane swaps complete the slice.
+    if (tile == 0) {
+      uint32_t lpart = 0;
 #pragma unroll
-    for (int st = 0; st < KSL / 32; ++st)
+      for (int st = 0; st < KSL / 32; ++st)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) lpart += raw[st][v];
-    lpart += uint32_t(__builtin_amdgcn_mov_dpp(int(lpart), kDppRor8, 0xf, 0xf, true));
-    {
-      const auto r = __builtin_amdgcn_permlane16_swap(lpart, lpart, false, false);
-      lpart = uint32_t(r[0]) + uint32_t(r[1]);
+        for (int v = 0; v < 4; ++v) lpart += raw[st][v];
+      lpart += uint32_t(__builtin_amdgcn_mov_dpp(int(lpart), kDppRor8, 0xf, 0xf, true));
+      {
+        const auto r = __builtin_amdgcn_permlane16_swap(lpart, lpart, false, false);
+        lpart = uint32_t(r[0]) + uint32_t(r[1]);
+      }
+      {
+        const auto r = __builtin_amdgcn_permlane32_swap(lpart, lpart, false, false);
+        lpart = uint32_t(r[0]) + uint32_t(r[1]);
+      }
+      if (lane < G) lsum[p][ksl * G + lane] = lpart;
     }
-    {
-      const auto r = __builtin_amdgcn_permlane32_swap(lpart, lpart, false, false);
-      lpart = uint32_t(r[0]) + uint32_t(r[1]);
+    f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < KSL / 32; ++st) {
+      uint32_t hw[2], lw[2];   // packed fp16 pairs: high parts, low parts
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const float f0 = float(raw[st][2 * v]) * kUnfix;
+        const float f1 = float(raw[st][2 * v + 1]) * kUnfix;
+        const _Float16 h0 = (_Float16)f0, h1 = (_Float16)f1;
+        const _Float16 e0 = (_Float16)(f0 - (float)h0), e1 = (_Float16)(f1 - (float)h1);
+        hw[v] = uint32_t(__builtin_bit_cast(uint16_t, h0)) | (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
+        lw[v] = uint32_t(__builtin_bit_cast(uint16_t, e0)) | (uint32_t(__builtin_bit_cast(uint16_t, e1)) << 16);
+      }
+      // the hi lane sends its low parts, the lo lane its high parts; row_ror:8
+      // delivers lane i+8's word to lane i and lane i's to lane i+8
+      const uint32_t r0 = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_row ? hw[0] : lw[0]), kDppRor8, 0xf, 0xf, true));
+      const uint32_t r1 = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_row ? hw[1] : lw[1]), kDppRor8, 0xf, 0xf, true));
+      uint4 aw;
+      aw.x = lo_row ? r0 : hw[0];
+      aw.y = lo_row ? r1 : hw[1];
+      aw.z = lo_row ? lw[0] : r0;
+      aw.w = lo_row ? lw[1] : r1;
+      const f16x8 av = __builtin_bit_cast(f16x8, aw);
+      if (st & 1) ob = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, cvb[st], ob, 0, 0, 0);
+      else        oa = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, cvb[st], oa, 0, 0, 0);
     }
-    if (lane < G) lsum[ksl * G + lane] = lpart;
-  }
-  f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int st = 0; st < KSL / 32; ++st) {
-    uint32_t hw[2], lw[2];   // packed fp16 pairs: high parts, low parts
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const float f0 = float(raw[st][2 * v]) * kUnfix;
-      const float f1 = float(raw[st][2 * v + 1]) * kUnfix;
-      const _Float16 h0 = (_Float16)f0, h1 = (_Float16)f1;
-      const _Float16 e0 = (_Float16)(f0 - (float)h0), e1 = (_Float16)(f1 - (float)h1);
-      hw[v] = uint32_t(__builtin_bit_cast(uint16_t, h0)) | (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
-      lw[v] = uint32_t(__builtin_bit_cast(uint16_t, e0)) | (uint32_t(__builtin_bit_cast(uint16_t, e1)) << 16);
-    }
-    // the hi lane sends its low parts, the lo lane its high parts; row_ror:8
-    // delivers lane i+8's word to lane i and lane i's to lane i+8
-    const uint32_t r0 = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_row ? hw[0] : lw[0]), kDppRor8, 0xf, 0xf, true));
-    const uint32_t r1 = uint32_t(__builtin_amdgcn_mov_dpp(int(lo_row ? hw[1] : lw[1]), kDppRor8, 0xf, 0xf, true));
-    uint4 aw;
-    aw.x = lo_row ? r0 : hw[0];
-    aw.y = lo_row ? r1 : hw[1];
-    aw.z = lo_row ? lw[0] : r0;
-    aw.w = lo_row ? lw[1] : r1;
-    const f16x8 av = __builtin_bit_cast(f16x8, aw);
-    if (st & 1) ob = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, cvb[st], ob, 0, 0, 0);
-    else        oa = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, cvb[st], oa, 0, 0, 0);
-  }
-  f32x4 o;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    o[r] = pair_sum32(oa[r] + ob[r]);   // rows 4*q4 + r and 4*q4 + r + 8 (lane + 32)
-  }
-
-  // ---- 6. write (m, l, o) or the normalised output ----------------------------
-  // lane holds the slice's o[h = 4*q4 + r][d = m_v*DS + jt*16 + l16]; the
-  // second slice's waves leave theirs in the (dead) table region and the
-  // first slice's waves add it and write.
-  float4* part_tile = reinterpret_cast<float4*>(lut);                      // [NTILE][64]
-  if (ksl == 1) part_tile[tile * 64 + lane] = make_float4(o[0], o[1], o[2], o[3]);
-  __syncthreads();
-  if (ksl == 0) {
-    const float4 other = part_tile[tile * 64 + lane];
-    o[0] += other.x; o[1] += other.y; o[2] += other.z; o[3] += other.w;
-    const int d = m_v * DS + jt * 16 + l16;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int h = 4 * q4 + r;
-      if (h < G) {
-        const float mh = key_float(mkey[h]);
-        const float lh = float(lsum[h] + lsum[G + h]) * kUnfix;
-        if (a.part_o == nullptr) {
-          a.out[(row0 + h) * D + d] = lh > 0.0f ? o[r] * __builtin_amdgcn_rcpf(lh) : 0.0f;
-        } else {
-          rec_store<STEP>(a.part_o + ((row0 + h) * a.C + c) * D + d, o[r]);
-          if (d == 0) {
-            rec_store<STEP>(a.part_m + (row0 + h) * a.C + c, mh * kLn2);
-            rec_store<STEP>(a.part_l + (row0 + h) * a.C + c, lh);
+      o_own[p][r] = pair_sum32(oa[r] + ob[r]);   // rows 4*q4 + r and 4*q4 + r + 8 (lane + 32)
+    }
+    // lane holds the slice's o[h = 4*q4 + r][d = m_v*DS + jt*16 + l16]; the
+    // second slice's waves leave theirs in the (dead) table region and the
+    // first slice's waves add it and write.
+    if (ksl == 1)
+      part_tile[(p * NTILE + tile) * 64 + lane] = make_float4(o_own[p][0], o_own[p][1], o_own[p][2], o_own[p][3]);
+  }
+
+  // ---- 6. write (m, l, o) of each chunk, or the normalised output --------------
+  __syncthreads();
+  if (ksl == 0) {
+    const int d = m_v * DS + jt * 16 + l16;
+#pragma unroll
+    for (int p = 0; p < CPW; ++p) {
+      if (p >= n_own) break;   // the grid's last workgroup may own fewer chunks
+      const int cc = c + p;
+      f32x4 o = o_own[p];
+      const float4 other = part_tile[(p * NTILE + tile) * 64 + lane];
+      o[0] += other.x; o[1] += other.y; o[2] += other.z; o[3] += other.w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * q4 + r;
+        if (h < G) {
+          const float mh = key_float(mkey[p][h]);
+          const float lh = float(lsum[p][h] + lsum[p][G + h]) * kUnfix;
+          if (a.part_o == nullptr) {   // one chunk in all (C == 1)
+            a.out[(row0 + h) * D + d] = lh > 0.0f ? o[r] * __builtin_amdgcn_rcpf(lh) : 0.0f;
+          } else {
+            rec_store<STEP>(a.part_o + ((row0 + h) * a.C + cc) * D + d, o[r]);
+            if (d == 0) {
+              rec_store<STEP>(a.part_m + (row0 + h) * a.C + cc, mh * kLn2);
+              rec_store<STEP>(a.part_l + (row0 + h) * a.C + cc, lh);
+            }
           }
         }
       }
     }
   }
   if constexpr (STEP) {
-    if (a.part_o != nullptr && arrive_last(a.counters + bg, a.C, &arrive_flag)) merge_rows<G>(a, row0, bg, lut);
+    if (a.part_o != nullptr && arrive_last(a.counters + bg, int(gridDim.y), &arrive_flag))
+      merge_rows<G>(a, row0, bg, lut);
   }
 }
 
 // G query heads per KV head, M segments, NT token slots per thread, STEP as
 // above; the codes in a dense [B][Hkv][Lmax][M] cache.
-template <int G, int M, int NT, bool STEP>
+template <int G, int M, int NT, bool STEP, int CPW = 1>
 __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeArgs a) {
-  score_chunk<G, M, NT, STEP, false>(a);
+  score_chunk<G, M, NT, STEP, false, CPW>(a);
 }
 
 // The same over a paged cache (block table and per-head page pools).
-template <int G, int M, int NT, bool STEP>
+template <int G, int M, int NT, bool STEP, int CPW = 1>
 __global__ __launch_bounds__(kDecodeThreads) void decode_paged_kernel(DecodeArgs a) {
-  score_chunk<G, M, NT, STEP, true>(a);
+  score_chunk<G, M, NT, STEP, true, CPW>(a);
 }
 
 // Merge of chunk statistics: one workgroup of D threads per row.

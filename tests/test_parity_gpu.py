@@ -498,6 +498,50 @@ def test_step_edges(G, M, Lmax, chunk, lens):
     check_counters_zero(desc, ws)
 
 
+TWO_CHUNK = [
+    # (G, Hkv, B, chunk, C, lens): M = 4 and more chunks than CUs, so each
+    # workgroup owns two chunks; C odd leaves the last workgroup one chunk.
+    # lens: full, one token, mid, empty, a workgroup's first chunk full and
+    # its second empty, one token in a second chunk, one token in the lone
+    # last chunk.
+    (2, 4, 8, 1024, 9, [9216, 1, 5000, 0, 1024, 1025, 2049, 8193]),
+    (8, 8, 2, 2048, 17, [34816, 2049]),
+]
+
+
+@pytest.mark.parametrize("G,Hkv,B,chunk,C,lens", TWO_CHUNK)
+def test_two_chunks_per_workgroup(G, Hkv, B, chunk, C, lens):
+    """Chunk records from workgroups that own two chunks each: the plain
+    decode (records + merge launch), the records themselves, and the decode
+    step (merge in the launch), against the oracle."""
+    say(f"two chunks per workgroup G={G} Hkv={Hkv} B={B} chunk={chunk} C={C} lens={lens}")
+    _, inp = gen.random_case(3600 + G, batch=B, n_q_heads=G * Hkv, n_kv_heads=Hkv,
+                             max_len=chunk * C, n_sub=4, lens=lens)
+    t = gpu_inputs(inp)
+    desc = pq.attn_desc(t[0], t[1], t[3], chunk=chunk)
+    assert pq.pq_attn_num_chunks(desc) == C
+    out = pq.pq_attn_decode(*t, desc=desc)
+    pm, pl, po = pq.pq_attn_partials(*t, desc=desc)
+    torch.cuda.synchronize()
+    assert_attn_close(out.cpu().numpy(), oracle_out(inp), "two-chunk decode")
+    rm, rl, ro = oracle.chunk_partials(inp["q"], inp["k_codes"], inp["v_codes"], inp["k_cb"],
+                                       inp["v_cb"], inp["lens"], chunk=chunk)
+    np.testing.assert_allclose(pm.cpu().numpy(), rm, rtol=0, atol=1e-4)
+    np.testing.assert_allclose(pl.cpu().numpy(), rl, rtol=2e-4, atol=0)
+    assert_attn_close(po.cpu().numpy(), ro, "two-chunk partial o")
+    xk, _, xv, _ = gen.step_tokens(np.random.default_rng(3700 + G), inp["k_cb"], inp["v_cb"], B)
+    lens = np.asarray(lens, np.int32)
+    desc2, ws, kc, vc, out2 = run_step(inp, xk, xv, lens, chunk=chunk)
+    exp_k, exp_v, ref = step_expected(inp, xk, xv, lens)
+    np.testing.assert_array_equal(kc, exp_k)
+    np.testing.assert_array_equal(vc, exp_v)
+    assert_attn_close(out2, ref, "two-chunk step")
+    for b, l in enumerate(lens):
+        if l == 0:
+            assert (out2[b] == 0).all()
+    check_counters_zero(desc2, ws)
+
+
 def test_step_twice_reuses_workspace():
     """Two consecutive steps through one workspace: the second appends after
     the first and sees both new tokens."""
