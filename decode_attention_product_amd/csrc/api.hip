@@ -68,17 +68,6 @@ DecodeFn pick_decode(int G, int M, int T, int cpw, bool step, bool paged) {
   return step ? pick_gm<true, false>(G, M, T, cpw) : pick_gm<false, false>(G, M, T, cpw);
 }
 
-// Chunks per workgroup of the score kernel: two when one chunk per
-// workgroup would need more than one workgroup per CU (a second round of
-// workgroups, each with its own prologue and table build) and two chunks fit
-// (M = 4, chunks of exactly 1024 or 2048 tokens).  The chunk records are the
-// same either way.
-int chunks_per_workgroup(const AttnPlan& p) {
-  constexpr int64_t kCUs = 256;
-  if (p.M != 4 || p.C < 2) return 1;
-  if (p.T != kDecodeThreads && p.T != 2 * kDecodeThreads) return 1;
-  return int64_t(p.B) * p.Hkv * p.C > kCUs ? 2 : 1;
-}
 
 // The request-batched kernel (one query head per KV head) whose NT token
 // slots per thread cover a chunk of T tokens.
@@ -202,7 +191,7 @@ pq_status launch_score(const AttnPlan& p, const ScoreIO& io, hipStream_t stream,
                   dim3(unsigned(p.Hkv), unsigned(p.C), unsigned((p.B + p.R - 1) / p.R)),
                   dim3(kDecodeThreads), &a, stream, start, stop);
   }
-  const int cpw = chunks_per_workgroup(p);
+  const int cpw = p.CPW;   // the chunk records are the same either way
   DecodeFn fn = pick_decode(p.G, p.M, p.T, cpw, step, pages != nullptr);
   if (!fn) return PQ_ERR_UNSUPPORTED;
   return launch(reinterpret_cast<const void*>(fn),

@@ -72,6 +72,8 @@ pq_status plan_attn(const pq_attn_desc* d, AttnPlan* p) {
   p->C = int32_t((int64_t(p->Lmax) + p->T - 1) / p->T);
   p->scale = d->scale;
   p->rows = int64_t(p->B) * p->Hq;
+  p->CPW = (p->R == 1 && p->M == 4 && p->C >= 2 && (p->T == 1024 || p->T == 2048) &&
+            int64_t(p->B) * p->Hkv * p->C > kCpwCUs) ? 2 : 1;
   p->blocks = int64_t(p->B) * p->Hkv * p->C;
   if (p->blocks > kMaxBlocks || p->rows > kMaxBlocks) return PQ_ERR_UNSUPPORTED;
   // score-kernel grids (Hkv, C, B) and (Hkv, C, B / R): the y and z extents are 16-bit

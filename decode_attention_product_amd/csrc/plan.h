@@ -21,12 +21,19 @@ constexpr int kMhaRequests = 4;
 constexpr int64_t kMhaMinPairs = 1024;
 constexpr int kMhaMaxChunkM4 = 4096;
 constexpr int kMhaMaxChunkM8 = 2048;
+// A per-request score workgroup takes two chunks when one chunk each would
+// give more workgroups than the chip has CUs (a second round of workgroups,
+// each with its own prologue and table build) and two histograms fit in LDS:
+// M = 4 and chunks of exactly 1024 or 2048 tokens.
+constexpr int64_t kCpwCUs = 256;
 
 // A checked decode-attention shape with the chunking resolved.
 struct AttnPlan {
   int32_t B, Hq, Hkv, G, D, M, DS, K, Lmax, T, C;
   int32_t R;            // requests per score workgroup of the plain decode (1, or
                         // kMhaRequests for the request-batched kernel)
+  int32_t CPW;          // chunks per workgroup of the per-request score kernel
+                        // (1, or 2: see kCpwCUs)
   float scale;
   int64_t rows;         // B * Hq
   int64_t blocks;       // score-kernel workgroups, B * Hkv * C

@@ -109,6 +109,28 @@ int main() {
     EXPECT(plan_attn(&md, &mp) == PQ_ERR_UNSUPPORTED);
   }
 
+  // two chunks per workgroup: M = 4, chunks of 1024 or 2048 tokens, more
+  // (request, KV head, chunk) triples than CUs
+  {
+    pq_attn_desc ld = base();
+    ld.batch = 1; ld.n_q_heads = 64; ld.n_kv_heads = 8; ld.n_sub = 4; ld.max_len = 131072;
+    AttnPlan lp;
+    ld.chunk = 2048;   // the long-context workload: 8 x 64 = 512 chunks
+    EXPECT(plan_attn(&ld, &lp) == PQ_OK && lp.C == 64 && lp.CPW == 2);
+    ld.chunk = 1024;
+    EXPECT(plan_attn(&ld, &lp) == PQ_OK && lp.C == 128 && lp.CPW == 2);
+    ld.chunk = 0;      // the library's chunk (4096): 256 workgroups already
+    EXPECT(plan_attn(&ld, &lp) == PQ_OK && lp.T == 4096 && lp.CPW == 1);
+    ld.chunk = 1536;   // not a whole number of token slots per thread
+    EXPECT(plan_attn(&ld, &lp) == PQ_OK && lp.CPW == 1);
+    ld.chunk = 2048; ld.n_sub = 8;   // two M = 8 histograms do not fit in LDS
+    EXPECT(plan_attn(&ld, &lp) == PQ_OK && lp.CPW == 1);
+    ld.n_sub = 4; ld.max_len = 65536;   // 8 x 32 = 256 chunks: one per CU already
+    EXPECT(plan_attn(&ld, &lp) == PQ_OK && lp.C == 32 && lp.CPW == 1);
+    ld.max_len = 67584;                 // 8 x 33 = 264 > 256
+    EXPECT(plan_attn(&ld, &lp) == PQ_OK && lp.C == 33 && lp.CPW == 2);
+  }
+
   // paged cache
   {
     pq_attn_desc pd = base();              // max_len 8192
