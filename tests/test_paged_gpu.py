@@ -68,6 +68,7 @@ PAGED_EDGE = [
     (8, 8, 256, 2048, 1024, [1023, 1024, 1025, 1]),
     (8, 4, 1024, 4096, 0, [4096, 3000, 1, 2]),
     (1, 8, 4096, 8192, 2048, [8192, 4097, 4096, 0]),  # a page longer than a chunk
+    (2, 4, 512, 17408, 1024, [17408, 1, 1024, 1025, 0, 16385, 2048, 9000]),  # two chunks per workgroup
     (4, 4, 32, 4096, 4096, [4096, 4095, 2049, 33]),   # several token slots per thread
 ]
 
@@ -172,6 +173,9 @@ STEP_PAGED = [
     # more than 8 chunks per (request, KV head): the spread merge
     (8, 4, 64, 2048, 128, [1, 2048, 700, 0]),
     (2, 8, 32, 1536, 64, [1536, 65, 33, 0]),
+    # 8 requests x 2 KV heads x 17 chunks of 1024 > 256: two chunks per
+    # workgroup, the last workgroup of each (request, KV head) with one
+    (4, 4, 256, 17408, 1024, [17408, 1, 1024, 1025, 0, 16385, 2048, 9000]),
 ]
 
 
