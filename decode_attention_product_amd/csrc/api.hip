@@ -73,7 +73,7 @@ DecodeFn pick_decode(int G, int M, int T, int cpw, bool step, bool paged) {
 // slots per thread cover a chunk of T tokens.
 template <int M, bool PAGED>
 DecodeFn pick_mha_nt(int T) {
-  constexpr int TPR = kDecodeThreads / kMhaRequests;
+  constexpr int TPR = kDecodeThreads / kMhaPassRequests;   // threads per request in a pass
   if (T <= TPR) return &decode_mha_kernel<M, kMhaRequests, 1, PAGED>;
   if (T <= 2 * TPR) return &decode_mha_kernel<M, kMhaRequests, 2, PAGED>;
   if (T <= 4 * TPR) return &decode_mha_kernel<M, kMhaRequests, 4, PAGED>;

@@ -13,30 +13,40 @@
 // kernel's: table gathers in fp32, base-2 exponentials, a fixed-point
 // histogram, an fp16 hi + lo contraction on the matrix cores.
 //
-// Thread t serves request t / TPR (TPR = 1024 / R threads, whole waves) and
-// its tokens chunk_start + t % TPR + j*TPR, j < NT.  LDS: the table
+// The R requests are taken in passes of RP = 4: in pass p thread t serves
+// request p*RP + t / TPR (TPR = 1024 / RP threads, whole waves) and its
+// tokens chunk_start + t % TPR + j*TPR, j < NT.  The table build and the
+// contraction take all R requests at once (R <= 8 rows of the matrix-core
+// tiles), so R = 8 halves the workgroups, and with them the codebook loads,
+// table builds and contractions per request, against R = 4; the next pass's
+// codes are requested as soon as the current pass's K codes are consumed.
+// LDS: the table
 // [m][r][k] (fp32), the histogram [r][m][k] (32-bit fixed point); a
 // request's l_c is the integer sum of its segment-0 bins.
 #pragma once
 
 #include "decode_kernel.hpp"
+#include "plan.h"   // kMhaPassRequests
 
 namespace pqattn {
 
 template <int M, int R, int NT, bool PAGED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a) {
+  constexpr int RP = kMhaPassRequests;          // requests per pass
+  constexpr int NP = R / RP;                    // passes
   constexpr int NTHR = kDecodeThreads;
   constexpr int D = 128;
   constexpr int K = 256;
   constexpr int DS = D / M;
   constexpr int NW = NTHR / 64;
-  constexpr int TPR = NTHR / R;                 // threads per request
+  constexpr int TPR = NTHR / RP;                // threads per request in a pass
   constexpr int KSTEP_Q = DS / 16;              // MFMA k-steps of the table build
   constexpr int LUT_JOBS = (M * 16) / NW;       // (m, 16-codeword tile) jobs per wave
   constexpr int NTILE = M * DS / 16;            // 16-column output tiles of the contraction
   constexpr int KSPLIT = NW / NTILE;            // waves sharing a tile, each a slice of the bins
   constexpr int KSL = K / KSPLIT;
   static_assert(R == 4 || R == 8, "requests per workgroup");
+  static_assert(R % RP == 0, "whole passes");
   static_assert(NTILE == 8 && KSPLIT == 2, "two contraction waves per output tile");
   // fixed point: a bin collects at most NT*TPR tokens of value <= 1, each
   // p * 2^kFixBits
@@ -57,23 +67,44 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
   const int g = blockIdx.x;
   const int c = blockIdx.y;
   const int b0 = blockIdx.z * R;                // first request of the group
-  const int r = tid / TPR;                      // this thread's request, uniform per wave
+  const int rl = tid / TPR;                     // this thread's request within a pass, uniform per wave
   const int li = tid % TPR;
-  const int b = b0 + r;
-  const bool live = b < a.B;
   const int t_begin = c * a.T;
 
   // ---- 0. requests ------------------------------------------------------------
-  int len = live ? a.lens[b] : 0;
-  int32_t page[PAGED ? NT : 1];
-  if constexpr (PAGED) {
-    const int32_t* row = a.block_table + int64_t(live ? b : 0) * a.max_pages;
+  // per pass: the request, whether it exists, its tokens' end in the chunk
+  int t_end[NP];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int t = t_begin + li + j * TPR;
-      page[j] = (live && t < a.Lmax) ? row[t >> a.page_shift] : 0;
-    }
+  for (int p = 0; p < NP; ++p) {
+    const int b = b0 + p * RP + rl;
+    int len = b < a.B ? a.lens[b] : 0;
+    len = len < 0 ? 0 : (len > a.Lmax ? a.Lmax : len);
+    t_end[p] = min(t_begin + a.T, len);         // t_end <= t_begin: no token of b here
   }
+  // the code bytes of token slot j of pass p (the slot must hold a token)
+  auto code_offset = [&](int p, int t, int32_t pg) -> int64_t {
+    if constexpr (PAGED) {
+      const uint32_t pp = min(uint32_t(pg), a.n_pages - 1u);
+      return int64_t(g) * a.pool_head_bytes +
+             ((int64_t(pp) << a.page_shift) | int64_t(t & ((1 << a.page_shift) - 1))) * M;
+    } else {
+      return ((int64_t(b0 + p * RP + rl) * a.Hkv + g) * a.Lmax + t) * M;
+    }
+  };
+  // paged cache: the pages of this thread's slots in a pass
+  auto load_pages = [&](int p, int32_t (&pg)[PAGED ? NT : 1]) {
+    if constexpr (PAGED) {
+      const int b = b0 + p * RP + rl;
+      const int32_t* row = a.block_table + int64_t(b < a.B ? b : 0) * a.max_pages;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int t = t_begin + li + j * TPR;
+        pg[j] = (b < a.B && t < a.Lmax) ? row[t >> a.page_shift] : 0;
+      }
+    }
+  };
+  int32_t page[PAGED ? NT : 1];
+  load_pages(0, page);
   // table build operands: lane l16 < R carries the query of request b0 + l16
   const int m_l = wave % M;
   f16x4 qa[KSTEP_Q];
@@ -94,26 +125,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
     for (int s = 0; s < KSTEP_Q; ++s) ckb[i][s] = *reinterpret_cast<const f16x4*>(row + s * 16);
   }
 
-  len = len < 0 ? 0 : (len > a.Lmax ? a.Lmax : len);
-  const int t_end = min(t_begin + a.T, len);    // t_end <= t_begin: no token of b here
-  const int64_t code_base = PAGED ? int64_t(g) * a.pool_head_bytes
-                                  : (int64_t(live ? b : 0) * a.Hkv + g) * a.Lmax * M;
-  const uint8_t* kc = a.k_codes + code_base;
-  const uint8_t* vc = a.v_codes + code_base;
-  TokenCodes<M> kcode[NT], vcode[NT];
+  TokenCodes<M> kcode[NT], vcode[NP][NT];
+  auto load_codes = [&](int p) {
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int t = t_begin + li + j * TPR;
-    if (t < t_end) {
-      int64_t slot = t;
-      if constexpr (PAGED) {
-        const uint32_t p = min(uint32_t(page[j]), a.n_pages - 1u);
-        slot = (int64_t(p) << a.page_shift) | int64_t(t & ((1 << a.page_shift) - 1));
+    for (int j = 0; j < NT; ++j) {
+      const int t = t_begin + li + j * TPR;
+      if (t < t_end[p]) {
+        const int64_t off = code_offset(p, t, PAGED ? page[j] : 0);
+        kcode[j].load(a.k_codes + off);
+        vcode[p][j].load(a.v_codes + off);
       }
-      kcode[j].load(kc + slot * M);
-      vcode[j].load(vc + slot * M);
     }
-  }
+  };
+  load_codes(0);
   for (int i = tid; i < R * M * K / 4; i += NTHR)
     reinterpret_cast<uint4*>(hist)[i] = make_uint4(0, 0, 0, 0);
   if (tid < R) mkey[tid] = float_key(-INFINITY);
@@ -136,34 +160,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
   }
   __syncthreads();
 
-  // ---- 2. scores ------------------------------------------------------------------
-  float s[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int t = t_begin + li + j * TPR;
-    s[j] = -INFINITY;
-    if (t < t_end) {
-      float v[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) v[m] = lut[(m * R + r) * K + kcode[j].get(m)];
-      float acc = v[0];
-#pragma unroll
-      for (int m = 1; m < M; ++m) acc += v[m];
-      s[j] = acc;
-    }
-  }
-
-  // ---- 3. chunk max per request -----------------------------------------------------
-  {
-    float mx[1] = {s[0]};
-#pragma unroll
-    for (int j = 1; j < NT; ++j) mx[0] = max_f(mx[0], s[j]);
-    row_max_n<1>(mx);
-    if (l16 == 0) atomicMax(&mkey[r], float_key(mx[0]));
-  }
-  __syncthreads();
-  const float m_r = key_float(mkey[r]);
-
   // V codebook operands of the contraction, in MFMA order by 16-bit loads
   // (as in the per-request kernel)
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -173,23 +169,62 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
   const int m_v = tile % M;
   const int jt = tile / M;
   f16x8 cvb[KSL / 32];
-#pragma unroll
-  for (int st = 0; st < KSL / 32; ++st) {
-    const _Float16* src = cvg + (int64_t(m_v) * K + ksl * KSL + st * 32 + 8 * q4) * DS + jt * 16 + l16;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) cvb[st][j] = src[j * DS];
-  }
 
-  // ---- 4. probabilities and the request's V histogram ----------------------------------
-  const float m_fix = m_r - kFixBits;   // 2^(s - m_fix) = p * 2^kFixBits
-  uint32_t* hr = hist + r * M * K;
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int t = t_begin + li + j * TPR;
-    if (t < t_end) {
-      const uint32_t u = uint32_t(fast_exp2(s[j] - m_fix) + 0.5f);
+  for (int p = 0; p < NP; ++p) {
+    const int r = p * RP + rl;                  // this thread's request in the pass
+    // ---- 2. scores ----------------------------------------------------------------
+    float s[NT];
 #pragma unroll
-      for (int m = 0; m < M; ++m) atomicAdd(hr + m * K + vcode[j].get(m), u);
+    for (int j = 0; j < NT; ++j) {
+      const int t = t_begin + li + j * TPR;
+      s[j] = -INFINITY;
+      if (t < t_end[p]) {
+        float v[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) v[m] = lut[(m * R + r) * K + kcode[j].get(m)];
+        float acc = v[0];
+#pragma unroll
+        for (int m = 1; m < M; ++m) acc += v[m];
+        s[j] = acc;
+      }
+    }
+    if (p + 1 < NP) {   // the next pass's pages and codes, while this pass finishes
+      load_pages(p + 1, page);
+      load_codes(p + 1);
+    }
+
+    // ---- 3. chunk max per request ---------------------------------------------------
+    {
+      float mx[1] = {s[0]};
+#pragma unroll
+      for (int j = 1; j < NT; ++j) mx[0] = max_f(mx[0], s[j]);
+      row_max_n<1>(mx);
+      if (l16 == 0) atomicMax(&mkey[r], float_key(mx[0]));
+    }
+    __syncthreads();
+    const float m_r = key_float(mkey[r]);
+
+    if (p == NP - 1) {
+#pragma unroll
+      for (int st = 0; st < KSL / 32; ++st) {
+        const _Float16* src = cvg + (int64_t(m_v) * K + ksl * KSL + st * 32 + 8 * q4) * DS + jt * 16 + l16;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cvb[st][j] = src[j * DS];
+      }
+    }
+
+    // ---- 4. probabilities and the request's V histogram --------------------------------
+    const float m_fix = m_r - kFixBits;   // 2^(s - m_fix) = p * 2^kFixBits
+    uint32_t* hr = hist + r * M * K;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int t = t_begin + li + j * TPR;
+      if (t < t_end[p]) {
+        const uint32_t u = uint32_t(fast_exp2(s[j] - m_fix) + 0.5f);
+#pragma unroll
+        for (int m = 0; m < M; ++m) atomicAdd(hr + m * K + vcode[p][j].get(m), u);
+      }
     }
   }
   __syncthreads();   // histograms complete

@@ -15,9 +15,11 @@ constexpr int kCodes = 256;     // K codewords per segment codebook
 constexpr int kLenAlign = 16;   // cache capacity granularity, tokens
 constexpr int kMaxChunk = 4096; // longest chunk one score workgroup takes
 // Request batching for one query head per KV head: kMhaRequests requests of
-// a KV head per score workgroup once there are at least kMhaMinPairs
-// (request, KV head) pairs; chunks of up to kMhaMaxChunkM4 / M8 tokens.
-constexpr int kMhaRequests = 4;
+// a KV head per score workgroup (in passes of kMhaPassRequests) once there
+// are at least kMhaMinPairs (request, KV head) pairs; chunks of up to
+// kMhaMaxChunkM4 / M8 tokens.
+constexpr int kMhaRequests = 8;
+constexpr int kMhaPassRequests = 4;
 constexpr int64_t kMhaMinPairs = 1024;
 constexpr int kMhaMaxChunkM4 = 4096;
 constexpr int kMhaMaxChunkM8 = 2048;

@@ -52,7 +52,8 @@ def ragged(rng, B, L):
 
 MHA = [
     # (B, H, L, M, chunk): B*H >= 1024
-    (66, 16, 512, 4, 0),      # a last group of two requests; T = 512, one chunk
+    (66, 16, 512, 4, 0),      # a last group of two requests (second pass empty); T = 512, one chunk
+    (69, 16, 1024, 4, 0),     # a last group of five requests (second pass with one)
     (64, 16, 4096, 8, 0),     # T = 2048: two chunks merged
     (64, 32, 1024, 4, 300),   # explicit chunks across thread strides
     (128, 8, 256, 8, 0),      # short caches
