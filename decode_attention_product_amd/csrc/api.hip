@@ -20,6 +20,25 @@ static_assert(kMaxChunk == 4 * kDecodeThreads, "a chunk is at most 4 token slots
 
 constexpr int kReduceThreads = 128;
 constexpr int kEncodeVectors = 256;   // vectors per encode workgroup (one wave per segment)
+constexpr int kEncodeVectorsSmall = 16;   // one tile: for launches with fewer workgroups than CUs
+constexpr int64_t kEncodeCUs = 256;
+
+// Vectors per encode workgroup: 256, or one 16-vector tile when 256-vector
+// tiles would leave CUs idle (e.g. a decode step's new tokens): every
+// workgroup loads its codebook half and computes its norms either way, so
+// more, shorter workgroups finish sooner.
+int encode_vectors(int64_t n_vec, int64_t heads, int64_t planes) {
+  const int64_t big = (n_vec + kEncodeVectors - 1) / kEncodeVectors;
+  return big * heads * planes < kEncodeCUs ? kEncodeVectorsSmall : kEncodeVectors;
+}
+
+const void* encode_fn(int M, int nv) {
+  if (nv == kEncodeVectorsSmall)
+    return M == 4 ? reinterpret_cast<const void*>(&encode_kernel<4, kEncodeVectorsSmall>)
+                  : reinterpret_cast<const void*>(&encode_kernel<8, kEncodeVectorsSmall>);
+  return M == 4 ? reinterpret_cast<const void*>(&encode_kernel<4, kEncodeVectors>)
+                : reinterpret_cast<const void*>(&encode_kernel<8, kEncodeVectors>);
+}
 
 using DecodeFn = void (*)(DecodeArgs);
 
@@ -230,10 +249,10 @@ pq_status launch_step_encode(const AttnPlan& p, const PagePlan* pages, const voi
     e.sch = int64_t(p.Lmax) * p.M;
     e.codes_bytes = int64_t(p.B) * p.Hkv * p.Lmax * p.M;
   }
-  const unsigned tiles = unsigned((p.B + kEncodeVectors - 1) / kEncodeVectors);
-  const void* fn = p.M == 4 ? reinterpret_cast<const void*>(&encode_kernel<4, kEncodeVectors>)
-                            : reinterpret_cast<const void*>(&encode_kernel<8, kEncodeVectors>);
-  return launch(fn, dim3(unsigned(p.Hkv), tiles, 2u), dim3(128 * p.M), &e, stream, start, nullptr);
+  const int nv = encode_vectors(p.B, p.Hkv, 2);
+  const unsigned tiles = unsigned((p.B + nv - 1) / nv);
+  return launch(encode_fn(p.M, nv), dim3(unsigned(p.Hkv), tiles, 2u), dim3(128 * p.M), &e, stream, start,
+                nullptr);
 }
 
 pq_status launch_reduce(int64_t rows, int32_t C, const float* pm, const float* pl, const float* po,
@@ -494,9 +513,9 @@ pq_status encode_planes(const pq_encode_desc* desc, int32_t n, const void* const
   a.sxh = desc->x_stride_head;
   a.scs = desc->codes_stride_slot;
   a.sch = desc->codes_stride_head;
-  const void* fn = p.M == 4 ? reinterpret_cast<const void*>(&encode_kernel<4, kEncodeVectors>)
-                            : reinterpret_cast<const void*>(&encode_kernel<8, kEncodeVectors>);
-  return launch(fn, dim3(unsigned(p.H), unsigned(p.blocks_x), unsigned(n)), dim3(128 * p.M), &a,
+  const int nv = encode_vectors(p.N, p.H, n);
+  const unsigned tiles = unsigned((p.N + nv - 1) / nv);   // one-vector-tile launches have < 4,096 tiles
+  return launch(encode_fn(p.M, nv), dim3(unsigned(p.H), tiles, unsigned(n)), dim3(128 * p.M), &a,
                 stream);
 }
 
