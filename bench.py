@@ -16,7 +16,9 @@ Infinity Cache and each step reads its codes from HBM.
 
 Further legs in the same line: "long_context" (the same one-launch step on
 the long-context split-K workload, B=1, Hq=64, Hkv=8, L=131072, M=4, 64
-chunks of 2048 tokens per KV head), "paged", "encode" and "kmeans".
+chunks of 2048 tokens per KV head), "paged", "encode", "kmeans" and
+"stream_reference" (device copies of the step's size and of 512 MiB: what
+one launch reaches on the same box).
 
 Prints one JSON line.  `value` = KV tokens scanned per second over the timed
 steps (sum of lens per step / step time).  `roofline` is the step kernel's
@@ -154,6 +156,7 @@ def main():
     ap.add_argument("--paged-steps", type=int, default=500)
     ap.add_argument("--no-kmeans", action="store_true", help="skip the codebook-learning leg")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context step leg")
+    ap.add_argument("--no-stream", action="store_true", help="skip the device-copy reference")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run 3 device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -309,6 +312,8 @@ def main():
         result["encode"] = encode_leg(pq, torch, dev, args.encode_reps)
     if not args.no_kmeans:
         result["kmeans"] = kmeans_leg(pq, torch, dev)
+    if not args.no_stream:
+        result["stream_reference"] = stream_leg(torch, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wid)
     print(json.dumps(result), flush=True)
@@ -517,6 +522,35 @@ def long_context_leg(pq, torch, dev, steps, warmup):
     lib["chunk"] = "library"
     leg["library_chunk"] = lib
     return leg
+
+
+def stream_leg(torch, dev, reps=200):
+    """Reference HBM rates on the same box: device-to-device copies (one
+    read and one write per byte) of the step kernel's size (~10 MB, one
+    launch each) and of 512 MiB, rotated over enough buffers that the copies
+    miss the Infinity Cache.  What one launch of this size can reach, next to
+    the step kernel's roofline fraction."""
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, nbytes in (("10MB", 9864192), ("512MiB", 512 << 20)):
+        nbuf = max(2, math.ceil((1 << 30) / nbytes))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1) for _ in range(nbuf)]
+        n = reps if nbytes < (64 << 20) else 20
+        for i in range(10):
+            bufs[(i + 1) % nbuf].copy_(bufs[i % nbuf])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(n):
+            bufs[(2 * i + 1) % nbuf].copy_(bufs[(2 * i) % nbuf])
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / n
+        gbs = 2 * nbytes / (us * 1e-6) / 1e9
+        res[name] = {"bytes": nbytes, "us_per_copy": us, "gbs_read_plus_write": gbs,
+                     "frac": gbs / HBM_PEAK_GBS}
+        del bufs
+    return res
 
 
 def kmeans_leg(pq, torch, dev, n_iter=10, reps=20):
