@@ -4,8 +4,7 @@ TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this module.  The HIP library never
 calls it and shares no code with it.
 
-It computes the plain definitions, slowly and in float64 (the encode
-decision in float32, the precision the GPU kernel decides in):
+It computes the plain definitions, slowly and in float64:
 
 * Product quantization of a cached vector (AQPIM page, section 3.1): the
   D-dimensional vector is cut into M equal contiguous segments; segment m is
@@ -176,26 +175,27 @@ def merge_partials(m, l, o):
     return out
 
 
-def encode(x, cb, block=4096):
+def encode(x, cb, block=1024):
     """Nearest-codeword encode (AQPIM page, sections 3.1 and 5.2 (2)).
 
     x   fp16 [N, H, D]
     cb  fp16 [H, M, K, ds]
     returns uint8 [N, H, M]: per (vector, head, segment) the index k that
-    minimises sum_j (x_j - C[k]_j)^2, computed in float32 from the exact fp16
-    values; the lowest index wins a tie (numpy argmin).
+    minimises the squared Euclidean distance sum_j (x_j - C[k]_j)^2, taken in
+    float64 from the exact fp16 values; the lowest index wins a tie (numpy
+    argmin).
     """
     N, H, D = x.shape
     _, M, K, ds = cb.shape
     codes = np.empty((N, H, M), dtype=np.uint8)
-    cb32 = cb.astype(np.float32)
+    cb64 = cb.astype(np.float64)
     for lo in range(0, N, block):
         hi = min(N, lo + block)
-        xs = x[lo:hi].astype(np.float32).reshape(hi - lo, H, M, ds)
+        xs = x[lo:hi].astype(np.float64).reshape(hi - lo, H, M, ds)
         for h in range(H):
             for m in range(M):
-                diff = xs[:, h, m, None, :] - cb32[h, m][None, :, :]     # [n, K, ds]
-                d2 = np.einsum("nkj,nkj->nk", diff, diff)
+                diff = xs[:, h, m, None, :] - cb64[h, m][None, :, :]     # [n, K, ds]
+                d2 = (diff * diff).sum(axis=-1)
                 codes[lo:hi, h, m] = np.argmin(d2, axis=1).astype(np.uint8)
     return codes
 

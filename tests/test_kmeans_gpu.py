@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
+from margins import assert_clear_margins, assert_lloyd_margins
 from synth import gen
 
 torch = pytest.importorskip("torch")
@@ -53,6 +54,7 @@ def test_update_matches_oracle(N, H, M, n_used):
     case = gen.kmeans_case(np.random.default_rng(900 + N + M), N, H, M, sigma=0.1,
                            init_sigma=0.3, n_used=n_used)
     x, cb0 = case["x"], case["cb_init"]
+    assert_clear_margins(x, cb0, "update assignment")
     codes = oracle.encode(x, cb0)
     ref, ref_counts = oracle.codebook_update(x, codes, cb0)
     cb = dev(cb0)
@@ -117,6 +119,7 @@ def test_kmeans_matches_oracle(N, H, M, n_used, n_iter):
     case = gen.kmeans_case(np.random.default_rng(1000 + N + n_iter), N, H, M, sigma=0.05,
                            init_sigma=0.25, n_used=n_used)
     x, cb0 = case["x"], case["cb_init"]
+    assert_lloyd_margins(x, cb0, n_iter, oracle, "kmeans")
     ref_cb, ref_codes = oracle.kmeans(x, cb0, n_iter)
     cb = dev(cb0)
     _, codes = pq.pq_kmeans(dev(x), cb, n_iter)
@@ -134,6 +137,7 @@ def test_kmeans_strided_sample_from_a_cache_and_order_independence():
                            n_used=24)
     kv = np.ascontiguousarray(case["x"].reshape(B, L, H, D).transpose(0, 2, 1, 3))   # [B, H, L, D]
     sample = np.ascontiguousarray(kv[1, :, :N].transpose(1, 0, 2))                  # [N, H, D]
+    assert_lloyd_margins(sample, case["cb_init"], 4, oracle, "strided sample")
     ref_cb, ref_codes = oracle.kmeans(sample, case["cb_init"], 4)
     kv_d = dev(kv)
     x_view = kv_d[1, :, :N].transpose(0, 1)           # [N, H, D] view, strides (D, L*D, 1)
@@ -163,8 +167,12 @@ def test_learned_codebooks_then_encode_and_decode():
     vc = gen.kmeans_case(rng, B * L, H, M, sigma=0.1, init_sigma=0.3, n_used=48)
     q = (rng.standard_normal((B, H, 128)).astype(np.float16))
     lens = np.array([L, 150], np.int32)
+    assert_lloyd_margins(kc["x"][:N], kc["cb_init"], 3, oracle, "K sample")
+    assert_lloyd_margins(vc["x"][:N], vc["cb_init"], 3, oracle, "V sample")
     ref_kcb, _ = oracle.kmeans(kc["x"][:N], kc["cb_init"], 3)
     ref_vcb, _ = oracle.kmeans(vc["x"][:N], vc["cb_init"], 3)
+    assert_clear_margins(kc["x"], ref_kcb, "prefill K with learned codebook")
+    assert_clear_margins(vc["x"], ref_vcb, "prefill V with learned codebook")
     kcb, vcb = dev(kc["cb_init"]), dev(vc["cb_init"])
     pq.pq_kmeans(dev(kc["x"][:N]), kcb, 3)
     pq.pq_kmeans(dev(vc["x"][:N]), vcb, 3)
@@ -198,6 +206,7 @@ def test_kmeans_at_and_past_the_one_launch_size(N, M, n_iter):
     say(f"kmeans N={N} M={M} iters={n_iter}")
     case = gen.kmeans_case(np.random.default_rng(1300 + N), N, 2, M, sigma=0.05, init_sigma=0.25,
                            n_used=100)
+    assert_lloyd_margins(case["x"], case["cb_init"], n_iter, oracle, "kmeans")
     ref_cb, ref_codes = oracle.kmeans(case["x"], case["cb_init"], n_iter)
     cb = dev(case["cb_init"])
     _, codes = pq.pq_kmeans(dev(case["x"]), cb, n_iter)
@@ -219,6 +228,7 @@ def test_kmeans_many_equals_single_calls():
     single_codes = [pq.pq_kmeans(x, cb, 4)[1] for x, cb in zip(xs, single)]
     torch.cuda.synchronize()
     for i, c in enumerate(cases):
+        assert_lloyd_margins(c["x"], c["cb_init"], 4, oracle, f"plane {i}")
         ref_cb, ref_codes = oracle.kmeans(c["x"], c["cb_init"], 4)
         same_bits(many[i].cpu().numpy(), ref_cb)
         same_bits(single[i].cpu().numpy(), ref_cb)
@@ -254,6 +264,7 @@ def test_kmeans_one_launch_rounding_cases():
     x[:, 0, :32] = np.array(rows, np.float16)[:, None]
     for m in range(1, M):   # exact codewords
         x[:, 0, 32 * m:32 * (m + 1)] = cb0[0, m, rng.integers(0, 256, N)]
+    assert_lloyd_margins(x, cb0, 1, oracle, "rounding clusters")
     ref_cb, ref_codes = oracle.kmeans(x, cb0, 1)
     cb = dev(cb0)
     _, codes = pq.pq_kmeans(dev(x), cb, 1)

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
+from margins import assert_clear_margins
 from synth import gen
 
 torch = pytest.importorskip("torch")
@@ -133,6 +134,8 @@ def test_step_with_many_single_head_pairs():
     again = pq.pq_attn_decode(q, kc, vc, kcb, vcb, lens)
     torch.cuda.synchronize()
     exp_k, exp_v = inp["k_codes"].copy(), inp["v_codes"].copy()
+    assert_clear_margins(xk, inp["k_cb"], "new token K")
+    assert_clear_margins(xv, inp["v_cb"], "new token V")
     ck, cv = oracle.encode(xk, inp["k_cb"]), oracle.encode(xv, inp["v_cb"])
     for b, l in enumerate(inp["lens"]):
         if l >= 1:
@@ -164,6 +167,8 @@ def test_paged_step_with_many_single_head_pairs():
                                        page_tokens=P)
     torch.cuda.synchronize()
     exp_k, exp_v = kp.copy(), vp.copy()
+    assert_clear_margins(xk, inp["k_cb"], "new token K")
+    assert_clear_margins(xv, inp["v_cb"], "new token V")
     ck, cv = oracle.encode(xk, inp["k_cb"]), oracle.encode(xv, inp["v_cb"])
     for b, l in enumerate(inp["lens"]):
         if l >= 1:
@@ -211,6 +216,8 @@ def test_step_with_many_single_head_pairs_two_chunks(paged):
             out = pq.pq_attn_decode_step(q, dev(xk), dev(xv), kc_d, vc_d, kcb, vcb, lens_d,
                                          desc=desc, workspace=ws)
         torch.cuda.synchronize()
+        assert_clear_margins(xk, inp["k_cb"], "new token K")
+        assert_clear_margins(xv, inp["v_cb"], "new token V")
         ck, cv = oracle.encode(xk, inp["k_cb"]), oracle.encode(xv, inp["v_cb"])
         for b, l in enumerate(lens):
             if l >= 1:

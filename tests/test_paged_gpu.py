@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
+from margins import assert_clear_margins
 from synth import gen
 
 torch = pytest.importorskip("torch")
@@ -139,6 +140,8 @@ def step_paged_expected(inp, kp, vp, table, lens, P, xk, xv):
     """Pools after the new token's codes (oracle encode) land at the slot of
     token lens[b] - 1, and the oracle's paged attention over them."""
     exp_k, exp_v = kp.copy(), vp.copy()
+    assert_clear_margins(xk, inp["k_cb"], "new token K")
+    assert_clear_margins(xv, inp["v_cb"], "new token V")
     ck, cv = oracle.encode(xk, inp["k_cb"]), oracle.encode(xv, inp["v_cb"])
     for b, l in enumerate(lens):
         if l >= 1:

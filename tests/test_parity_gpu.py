@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
+from margins import assert_clear_margins
 from synth import gen
 
 torch = pytest.importorskip("torch")
@@ -73,6 +74,7 @@ def test_tiny_workload_decode_and_encode():
     inp = gen.workload_inputs(1)
     assert_attn_close(decode_gpu(inp), oracle_out(inp), "tiny decode")
     for x, cb, src in ((inp["x_k"], inp["k_cb"], inp["src_k"]), (inp["x_v"], inp["v_cb"], inp["src_v"])):
+        assert_clear_margins(x, cb, "tiny encode")
         codes = torch.empty((x.shape[0], x.shape[1], cb.shape[1]), dtype=torch.uint8, device="cuda")
         pq.pq_encode(dev(x), dev(cb), codes)
         torch.cuda.synchronize()
@@ -143,6 +145,8 @@ def test_ragged_workload_encode_then_decode():
     # and the oracle's own encode agrees on a sample of vectors
     rng = np.random.default_rng(7)
     idx = np.sort(rng.choice(N, size=3000, replace=False))
+    assert_clear_margins(inp["x_k"][idx], inp["k_cb"], "ragged encode sample (K)")
+    assert_clear_margins(inp["x_v"][idx], inp["v_cb"], "ragged encode sample (V)")
     np.testing.assert_array_equal(oracle.encode(inp["x_k"][idx], inp["k_cb"]), kc_h[b_of[idx], :, t_of[idx]])
     np.testing.assert_array_equal(oracle.encode(inp["x_v"][idx], inp["v_cb"]), vc_h[b_of[idx], :, t_of[idx]])
     say("ragged: decode over the encoded cache")
@@ -304,6 +308,7 @@ def test_encode_strided_slots_and_out_of_range():
     B, H, L, M = 3, 4, 64, 8
     cb = gen.codebooks(rng, H, M, 256, 128 // M)
     x, src = gen.noisy_codewords(rng, cb, 10, 0.05)
+    assert_clear_margins(x, cb, "slot encode")
     cache = np.full((B, H, L, M), 0xEE, dtype=np.uint8)
     slots = np.array([0, 5, 63, 64 * 4 + 1, 2 * H * L + 7, 2 * H * L + 8, 2 * H * L + 63,
                       -1, B * H * L, 1 << 40], dtype=np.int64)
@@ -330,6 +335,9 @@ def test_encode_ties_lowest_index():
     x = np.zeros((2, 2, 128), dtype=np.float16)
     x[0, 1, 64:96] = cb[1, 2, 17]
     x[1, 0, 0:32] = cb[0, 0, 3]
+    built_tie = np.zeros((2, 2, 4), dtype=bool)
+    built_tie[0, 1, 2] = built_tie[1, 0, 0] = True
+    assert_clear_margins(x, cb, "encode ties (other segments)", mask=~built_tie)
     codes = torch.empty((2, 2, 4), dtype=torch.uint8, device="cuda")
     pq.pq_encode(dev(x), dev(cb), codes)
     torch.cuda.synchronize()
@@ -348,6 +356,8 @@ def test_encode_many_matches_single_calls():
     vcb = gen.codebooks(rng, H, M, 256, 128 // M)
     xk, srck = gen.noisy_codewords(rng, kcb, B, 0.05)
     xv, srcv = gen.noisy_codewords(rng, vcb, B, 0.05)
+    assert_clear_margins(xk, kcb, "encode_many K")
+    assert_clear_margins(xv, vcb, "encode_many V")
     slots = np.arange(B, dtype=np.int64) * H * L + np.array([0, 5, 63, 17])
     kc1, vc1 = dev(np.zeros((B, H, L, M), np.uint8)), dev(np.zeros((B, H, L, M), np.uint8))
     kc2, vc2 = dev(np.zeros((B, H, L, M), np.uint8)), dev(np.zeros((B, H, L, M), np.uint8))
@@ -373,6 +383,8 @@ def step_expected(inp, xk, xv, lens):
     """The cache after appending the new token at slot lens[b] - 1 (codes from
     the oracle's encode) and the oracle's attention over it."""
     exp_k, exp_v = inp["k_codes"].copy(), inp["v_codes"].copy()
+    assert_clear_margins(xk, inp["k_cb"], "new token K")
+    assert_clear_margins(xv, inp["v_cb"], "new token V")
     ck, cv = oracle.encode(xk, inp["k_cb"]), oracle.encode(xv, inp["v_cb"])
     L = exp_k.shape[2]
     for b, l in enumerate(lens):
