@@ -23,11 +23,15 @@
 //      2.2.3 (1)).
 //   4. V histogram Hist[m][k][h] = sum of p_t over the chunk's tokens whose
 //      segment-m V code is k.  LDS float atomics are slow on gfx950, so p is
-//      added as a 32-bit fixed-point integer (p * 2^31 / Tmax, rounded,
-//      which cannot overflow a bin), two heads per 64-bit ds_add_u64.  Every
-//      token lands in exactly one bin of segment 0, so l_c = sum_t p_t is
-//      the integer sum of those bins: exact, and the same quantised p that
-//      the contraction weights.
+//      added as a 32-bit fixed-point integer, two heads per 64-bit
+//      ds_add_u64.  The scale 2^S of a (chunk, head) comes from the chunk's
+//      mass: an upper estimate of l_c = sum_t p_t (one reduction) sets
+//      S = 30 - ceil(log2 l_c), so the bins of a segment, which add up to
+//      about l_c * 2^S, stay below 2^31 whatever the score distribution, and
+//      a chunk dominated by one token keeps ~29 bits for the rest.  Every
+//      token lands in exactly one bin of segment 0, so the l_c of the record
+//      is the integer sum of those bins: exact, and the same quantised p
+//      that the contraction weights.
 //   5. Contraction o[h][m*DS + j] = sum_k Hist[m][k][h] * Cv_g[m][k][j] on
 //      the matrix cores.  This equals sum_t p_t V_t because every V_t is
 //      made of codewords.  The histogram enters as fp16 hi + lo parts, so
@@ -128,6 +132,41 @@ __device__ __forceinline__ void row_max_n(float (&v)[N]) {
     x = max_f(x, dpp_f<kDppRor8>(x));
     v[i] = x;
   }
+}
+
+// Sum of N values over each row of 16 lanes (every lane of the row receives
+// its row's sums), as row_max_n.
+template <int N>
+__device__ __forceinline__ void row_sum_n(float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float x = v[i];
+    x += dpp_f<kDppXor1>(x);
+    x += dpp_f<kDppXor2>(x);
+    x += dpp_f<kDppRor4>(x);
+    x += dpp_f<kDppRor8>(x);
+    v[i] = x;
+  }
+}
+
+// Fixed point of the V histogram.  A (chunk, head) adds u_t = round(p_t 2^S)
+// per token, p_t = 2^(s_t - m_c) <= 1, into 32-bit bins.  S comes from an
+// upper estimate of the chunk's mass l_c = sum_t p_t, accumulated as
+// kMassBits fixed-point integers rounded up (lest = ceil-sums of l_c 2^16):
+// S = 30 - ceil(log2 l_c), clamped to [14, 30].  Then the u_t of a segment
+// sum to at most l_c 2^S + T/2 <= 2^30 + 2^11 < 2^31, so no bin and no
+// integer sum of bins overflows; a chunk whose mass is one dominant token
+// gets S = 29 or 30.  l_c >= 1 always (the maximum token has p = 1).
+constexpr int kMassBits = 16;
+__device__ __forceinline__ int fix_shift(uint32_t lest) {
+  const uint32_t x = lest > (1u << kMassBits) ? lest - 1u : (1u << kMassBits) - 1u;
+  return 30 - kMassBits + __builtin_clz(x);   // 30 - ceil(log2(lest 2^-16))
+}
+// 2^e as a float, for |e| < 127
+__device__ __forceinline__ float pow2i(int e) { return __builtin_bit_cast(float, uint32_t(127 + e) << 23); }
+// one row's mass estimate as a rounded-up fixed-point integer
+__device__ __forceinline__ uint32_t mass_fix(float row_sum) {
+  return uint32_t(__builtin_ceilf(row_sum * float(1u << kMassBits)));
 }
 
 // Float <-> int keys whose signed order is the float order (finite values
@@ -580,11 +619,6 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   static_assert(NTILE == 8 && KSPLIT == 2, "two contraction waves per output tile");
   static_assert(CPW == 1 || (CPW == 2 && M == 4 && NT % 2 == 0), "two chunks per workgroup need M = 4");
   constexpr int NTC = NT / CPW;               // token slots per thread in one chunk
-  // fixed point: a bin collects at most NTC*NTHR tokens of value <= 1, each
-  // p * 2^kFixBits with kFixBits = 31 - log2(NTC * NTHR)
-  static_assert((NTC & (NTC - 1)) == 0, "power-of-two token capacity");
-  constexpr float kFixBits = float(31 - ilog2(NTC * NTHR));
-  constexpr float kUnfix = float(NTC * NTHR) / float(1u << 31);
 
   // Table and histogram live in separate LDS regions, so the histogram can be
   // cleared while the workgroup still waits for its operands.
@@ -607,6 +641,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   char* hist_bytes = reinterpret_cast<char*>(hist);                        // [k][R] u64 (G >= 2)
   __shared__ uint32_t lsum[CPW][2 * G];       // l_c per chunk, head and bin slice, fixed point
   __shared__ __align__(16) int mkey[CPW][G];  // chunk max per head, as float_key
+  __shared__ uint32_t lest[CPW][G];           // upper estimate of l_c per chunk and head (fix_shift)
   __shared__ unsigned long long new_key[2][NW];  // step: per-wave argmax keys of the new K, V
   __shared__ uint32_t arrive_flag;
 
@@ -728,7 +763,10 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   // the histograms are cleared while the operands are in flight
   for (int i = tid; i < CPW * HIST_WORDS / 4; i += NTHR)
     reinterpret_cast<uint4*>(hist)[i] = make_uint4(0, 0, 0, 0);
-  if (tid < CPW * G) mkey[tid / G][tid % G] = float_key(-INFINITY);
+  if (tid < CPW * G) {
+    mkey[tid / G][tid % G] = float_key(-INFINITY);
+    lest[tid / G][tid % G] = 0;
+  }
 
   // ---- 1. lookup table on the matrix cores ----------------------------------
   // Step kernel, chunk with the new token: row 8 of every product starts at
@@ -879,6 +917,36 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   for (int p = 0; p < CPW; ++p)
 #pragma unroll
     for (int h = 0; h < G; ++h) m_c[p][h] = key_float(mkey[p][h]);
+  // p_t = 2^(s_t - m_c) in place of the scores, and the chunk's mass: row
+  // sums, then one rounded-up integer LDS add per (row, head)
+  {
+    float psum[CPW][G];
+#pragma unroll
+    for (int p = 0; p < CPW; ++p)
+#pragma unroll
+      for (int h = 0; h < G; ++h) psum[p][h] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const bool valid = t_begin + i * NTHR + tid < t_end;
+      const int pc = i / NTC;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float e = valid ? fast_exp2(s[i][h] - m_c[pc][h]) : 0.0f;
+        s[i][h] = e;
+        psum[pc][h] += e;
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < CPW; ++p) {
+      row_sum_n<G>(psum[p]);
+      if (l16 < G) {
+        float mine = psum[p][0];
+#pragma unroll
+        for (int h = 1; h < G; ++h) mine = (l16 == h) ? psum[p][h] : mine;
+        atomicAdd(&lest[p][l16], mass_fix(mine));
+      }
+    }
+  }
   if constexpr (STEP) {
     if (has_new) {   // the new token's V codes (per-wave keys written before the barrier above)
       const TokenCodes<M> nv = combine_new_codes<M, NW>(new_key[1]);
@@ -936,13 +1004,13 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     asm("" : "+v"(row_m[jm]));
   }
 
-  // exponent offset: 2^(s - m_c + kFixBits) = p * 2^kFixBits is the bin
-  // value before rounding
-  float m_fix[CPW][G];
+  __syncthreads();   // mass estimates complete
+  // the bin value before rounding is p * 2^S (exact: a power-of-two scale)
+  float fscale[CPW][G];
 #pragma unroll
   for (int p = 0; p < CPW; ++p)
 #pragma unroll
-    for (int h = 0; h < G; ++h) m_fix[p][h] = m_c[p][h] - kFixBits;
+    for (int h = 0; h < G; ++h) fscale[p][h] = pow2i(fix_shift(lest[p][h]));
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     const int t = t_begin + i * NTHR + tid;
@@ -952,7 +1020,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       uint32_t u[G];
 #pragma unroll
       for (int h = 0; h < G; ++h)
-        u[h] = uint32_t(fast_exp2(s[i][h] - m_fix[pc][h]) + 0.5f);   // <= 2^31 / Tmax, rounded
+        u[h] = uint32_t(fmaf(s[i][h], fscale[pc][h], 0.5f));   // round(p 2^S)
       if constexpr (G >= 2) {
         uint64_t pv[GP];
 #pragma unroll
@@ -1011,6 +1079,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   for (int p = 0; p < CPW; ++p) {
     const char* hb = hist_bytes + p * HIST_WORDS * 4;
     const uint32_t* h32 = hist32 + p * HIST_WORDS;
+    const float unfix = pow2i(-fix_shift(lest[p][hh < G ? hh : 0]));   // 2^-S of this row's head
     uint32_t raw[KSL / 32][4];
 #pragma unroll
     for (int st = 0; st < KSL / 32; ++st) {
@@ -1054,8 +1123,8 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       uint32_t hw[2], lw[2];   // packed fp16 pairs: high parts, low parts
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
-        const float f0 = float(raw[st][2 * v]) * kUnfix;
-        const float f1 = float(raw[st][2 * v + 1]) * kUnfix;
+        const float f0 = float(raw[st][2 * v]) * unfix;
+        const float f1 = float(raw[st][2 * v + 1]) * unfix;
         const _Float16 h0 = (_Float16)f0, h1 = (_Float16)f1;
         const _Float16 e0 = (_Float16)(f0 - (float)h0), e1 = (_Float16)(f1 - (float)h1);
         hw[v] = uint32_t(__builtin_bit_cast(uint16_t, h0)) | (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
@@ -1101,7 +1170,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
         const int h = 4 * q4 + r;
         if (h < G) {
           const float mh = key_float(mkey[p][h]);
-          const float lh = float(lsum[p][h] + lsum[p][G + h]) * kUnfix;
+          const float lh = float(lsum[p][h] + lsum[p][G + h]) * pow2i(-fix_shift(lest[p][h]));
           if (a.part_o == nullptr) {   // one chunk in all (C == 1)
             a.out[(row0 + h) * D + d] = lh > 0.0f ? o[r] * __builtin_amdgcn_rcpf(lh) : 0.0f;
           } else {

@@ -21,8 +21,9 @@
 // table builds and contractions per request, against R = 4; the next pass's
 // codes are requested as soon as the current pass's K codes are consumed.
 // LDS: the table
-// [m][r][k] (fp32), the histogram [r][m][k] (32-bit fixed point); a
-// request's l_c is the integer sum of its segment-0 bins.
+// [m][r][k] (fp32), the histogram [r][m][k] (32-bit fixed point scaled by
+// each request's mass, as in the per-request kernel); a request's l_c is the
+// integer sum of its segment-0 bins.
 #pragma once
 
 #include "decode_kernel.hpp"
@@ -48,16 +49,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
   static_assert(R == 4 || R == 8, "requests per workgroup");
   static_assert(R % RP == 0, "whole passes");
   static_assert(NTILE == 8 && KSPLIT == 2, "two contraction waves per output tile");
-  // fixed point: a bin collects at most NT*TPR tokens of value <= 1, each
-  // p * 2^kFixBits
-  static_assert((NT & (NT - 1)) == 0, "power-of-two token capacity");
-  constexpr float kFixBits = float(31 - ilog2(NT * TPR));
-  constexpr float kUnfix = float(NT * TPR) / float(1u << 31);
 
   __shared__ __align__(16) float lut[M * R * K];         // [m][r][k]
   __shared__ __align__(16) uint32_t hist[R * M * K];     // [r][m][k]
   __shared__ uint32_t lsum[2 * R];                       // l_c per request and bin slice
   __shared__ int mkey[R];
+  __shared__ uint32_t lest[R];                           // upper estimate of l_c (fix_shift)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -140,7 +137,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
   load_codes(0);
   for (int i = tid; i < R * M * K / 4; i += NTHR)
     reinterpret_cast<uint4*>(hist)[i] = make_uint4(0, 0, 0, 0);
-  if (tid < R) mkey[tid] = float_key(-INFINITY);
+  if (tid < R) {
+    mkey[tid] = float_key(-INFINITY);
+    lest[tid] = 0;
+  }
 
   // ---- 1. lookup tables of the R queries on the matrix cores --------------------
 #pragma unroll
@@ -204,6 +204,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
     }
     __syncthreads();
     const float m_r = key_float(mkey[r]);
+    // p_t = 2^(s_t - m_r) in place of the scores, and the request's mass (an
+    // upper estimate of l_c, which sets the histogram's fixed point)
+    {
+      float psum[1] = {0.0f};
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const float e = t_begin + li + j * TPR < t_end[p] ? fast_exp2(s[j] - m_r) : 0.0f;
+        s[j] = e;
+        psum[0] += e;
+      }
+      row_sum_n<1>(psum);
+      if (l16 == 0) atomicAdd(&lest[r], mass_fix(psum[0]));
+    }
 
     if (p == NP - 1) {
 #pragma unroll
@@ -214,14 +227,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
       }
     }
 
-    // ---- 4. probabilities and the request's V histogram --------------------------------
-    const float m_fix = m_r - kFixBits;   // 2^(s - m_fix) = p * 2^kFixBits
+    // ---- 4. the request's V histogram ---------------------------------------------------
+    __syncthreads();   // mass estimates complete
+    const float fscale = pow2i(fix_shift(lest[r]));   // bins hold round(p 2^S)
     uint32_t* hr = hist + r * M * K;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const int t = t_begin + li + j * TPR;
       if (t < t_end[p]) {
-        const uint32_t u = uint32_t(fast_exp2(s[j] - m_fix) + 0.5f);
+        const uint32_t u = uint32_t(fmaf(s[j], fscale, 0.5f));
 #pragma unroll
         for (int m = 0; m < M; ++m) atomicAdd(hr + m * K + vcode[p][j].get(m), u);
       }
@@ -267,13 +281,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
     if (lane < R) lsum[ksl * R + lane] = lpart;
   }
   f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = {0.f, 0.f, 0.f, 0.f};
+  const float unfix = pow2i(-fix_shift(lest[hh < R ? hh : 0]));   // 2^-S of this row's request
 #pragma unroll
   for (int st = 0; st < KSL / 32; ++st) {
     uint32_t hw[2], lw[2];
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
-      const float f0 = float(raw[st][2 * v]) * kUnfix;
-      const float f1 = float(raw[st][2 * v + 1]) * kUnfix;
+      const float f0 = float(raw[st][2 * v]) * unfix;
+      const float f1 = float(raw[st][2 * v + 1]) * unfix;
       const _Float16 h0 = (_Float16)f0, h1 = (_Float16)f1;
       const _Float16 e0 = (_Float16)(f0 - (float)h0), e1 = (_Float16)(f1 - (float)h1);
       hw[v] = uint32_t(__builtin_bit_cast(uint16_t, h0)) | (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
@@ -308,7 +323,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
       if (rr < R && b0 + rr < a.B) {
         const int64_t row = int64_t(b0 + rr) * a.Hq + g;
         const float mh = key_float(mkey[rr]);
-        const float lh = float(lsum[rr] + lsum[R + rr]) * kUnfix;
+        const float lh = float(lsum[rr] + lsum[R + rr]) * pow2i(-fix_shift(lest[rr]));
         if (a.part_o == nullptr) {
           a.out[row * D + d] = lh > 0.0f ? o[e] * __builtin_amdgcn_rcpf(lh) : 0.0f;
         } else {
