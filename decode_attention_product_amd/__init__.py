@@ -27,7 +27,8 @@ EXPORTED = ("pq_attn_num_chunks", "pq_attn_workspace_bytes", "pq_attn_decode",
             "pq_attn_partials_paged",
             "pq_attn_decode_step_paged", "pq_attn_decode_step_paged_timed", "pq_attn_reduce",
             "pq_encode", "pq_encode_many", "pq_codebook_update", "pq_kmeans",
-            "pq_kmeans_many", "pq_status_string")
+            "pq_kmeans_many", "pq_attn_decode_fp8cb", "pq_attn_partials_fp8cb",
+            "pq_encode_fp8cb", "pq_status_string")
 
 
 class PQError(RuntimeError):
@@ -118,6 +119,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pq_kmeans_many.argtypes = [ctypes.POINTER(PQEncodeDesc), ctypes.c_int32, ctypes.POINTER(P),
                                    ctypes.POINTER(P), ctypes.c_int32, ctypes.POINTER(P), P]
     lib.pq_kmeans_many.restype = ctypes.c_int
+    lib.pq_attn_decode_fp8cb.argtypes = [ctypes.POINTER(PQAttnDesc), P, P, P, P, P, P, P, P,
+                                         ctypes.c_size_t, P]
+    lib.pq_attn_decode_fp8cb.restype = ctypes.c_int
+    lib.pq_attn_partials_fp8cb.argtypes = [ctypes.POINTER(PQAttnDesc), P, P, P, P, P, P, P, P, P, P]
+    lib.pq_attn_partials_fp8cb.restype = ctypes.c_int
+    lib.pq_encode_fp8cb.argtypes = [ctypes.POINTER(PQEncodeDesc), P, P, P, P, P]
+    lib.pq_encode_fp8cb.restype = ctypes.c_int
     lib.pq_status_string.argtypes = [ctypes.c_int]
     lib.pq_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -180,15 +188,16 @@ def pq_attn_workspace_bytes(desc: PQAttnDesc) -> int:
     return int(load_library().pq_attn_workspace_bytes(ctypes.byref(desc)))
 
 
-def _check_attn_inputs(desc, q, k_codes, v_codes, k_cb, v_cb, lens):
+def _check_attn_inputs(desc, q, k_codes, v_codes, k_cb, v_cb, lens, cb_dtype=None):
     import torch
     B, Hq, Hkv, D = desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim
     M, K, L = desc.n_sub, desc.n_codes, desc.max_len
+    cb_dtype = torch.float16 if cb_dtype is None else cb_dtype
     _need(q, "q", torch.float16, (B, Hq, D))
     _need(k_codes, "k_codes", torch.uint8, (B, Hkv, L, M))
     _need(v_codes, "v_codes", torch.uint8, (B, Hkv, L, M))
-    _need(k_cb, "k_cb", torch.float16, (Hkv, M, K, D // M))
-    _need(v_cb, "v_cb", torch.float16, (Hkv, M, K, D // M))
+    _need(k_cb, "k_cb", cb_dtype, (Hkv, M, K, D // M))
+    _need(v_cb, "v_cb", cb_dtype, (Hkv, M, K, D // M))
     _need(lens, "lens", torch.int32, (B,))
 
 
@@ -246,6 +255,53 @@ def pq_attn_partials(q, k_codes, v_codes, k_cb, v_cb, lens, *, desc=None, chunk=
     else:
         st = lib.pq_attn_partials_timed(*args, events[0], events[1])
     _check(st, "pq_attn_partials")
+    return part_m, part_l, part_o
+
+
+def pq_attn_decode_fp8cb(q, k_codes, v_codes, k_cb, v_cb, lens, out=None, *, desc=None, chunk=0,
+                         scale=None, workspace=None, stream=None):
+    """pq_attn_decode with FP8 E4M3 codebooks (C entry point
+    pq_attn_decode_fp8cb): k_cb and v_cb are uint8 [Hkv, M, K, D/M] tensors
+    of E4M3 bytes.  Returns ``out`` (fp32 [B, Hq, D])."""
+    import torch
+    if desc is None:
+        desc = attn_desc(q, k_codes, k_cb, chunk=chunk, scale=scale)
+    _check_attn_inputs(desc, q, k_codes, v_codes, k_cb, v_cb, lens, torch.uint8)
+    if out is None:
+        out = torch.empty((desc.batch, desc.n_q_heads, desc.head_dim), dtype=torch.float32,
+                          device=q.device)
+    _need(out, "out", torch.float32, (desc.batch, desc.n_q_heads, desc.head_dim))
+    ws_bytes = pq_attn_workspace_bytes(desc)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().pq_attn_decode_fp8cb(
+        ctypes.byref(desc), _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_cb), _ptr(v_cb),
+        _ptr(lens), _ptr(out), _ptr(workspace), nbytes, _stream(stream))
+    _check(st, "pq_attn_decode_fp8cb")
+    return out
+
+
+def pq_attn_partials_fp8cb(q, k_codes, v_codes, k_cb, v_cb, lens, *, desc=None, chunk=0,
+                           scale=None, stream=None):
+    """Chunk statistics with FP8 E4M3 codebooks (C entry point
+    pq_attn_partials_fp8cb); returns (part_m, part_l, part_o) as
+    pq_attn_partials does."""
+    import torch
+    if desc is None:
+        desc = attn_desc(q, k_codes, k_cb, chunk=chunk, scale=scale)
+    _check_attn_inputs(desc, q, k_codes, v_codes, k_cb, v_cb, lens, torch.uint8)
+    C = pq_attn_num_chunks(desc)
+    if C < 1:
+        raise PQError(PQ_ERR_SHAPE_CODE, "pq_attn_partials_fp8cb")
+    B, Hq, D = desc.batch, desc.n_q_heads, desc.head_dim
+    part_m = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
+    part_l = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
+    part_o = torch.empty((B, Hq, C, D), dtype=torch.float32, device=q.device)
+    st = load_library().pq_attn_partials_fp8cb(
+        ctypes.byref(desc), _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_cb), _ptr(v_cb),
+        _ptr(lens), _ptr(part_m), _ptr(part_l), _ptr(part_o), _stream(stream))
+    _check(st, "pq_attn_partials_fp8cb")
     return part_m, part_l, part_o
 
 
@@ -443,6 +499,27 @@ def pq_encode(x, codebook, codes, *, slots=None, desc=None, stream=None):
     st = load_library().pq_encode(ctypes.byref(desc), _ptr(x), _ptr(codebook), _ptr(slots),
                                   _ptr(codes), _stream(stream))
     _check(st, "pq_encode")
+    return codes
+
+
+def pq_encode_fp8cb(x, codebook, codes, *, slots=None, desc=None, stream=None):
+    """pq_encode against an FP8 E4M3 codebook (C entry point
+    pq_encode_fp8cb): codebook is a uint8 [H, M, K, D/M] tensor of E4M3
+    bytes; everything else as for pq_encode."""
+    import torch
+    _need(x, "x", torch.float16, None)
+    _need(codebook, "codebook", torch.uint8, None)
+    _need(codes, "codes", torch.uint8, None)
+    if slots is not None:
+        _need(slots, "slots", torch.int64, None)
+    if desc is None:
+        N, H, D = x.shape
+        _, M, K, _ = codebook.shape
+        _need(codes, "codes", torch.uint8, (N, H, M))
+        desc = PQEncodeDesc(N, H, D, M, K, H * D, D, H * M, M, codes.numel())
+    st = load_library().pq_encode_fp8cb(ctypes.byref(desc), _ptr(x), _ptr(codebook), _ptr(slots),
+                                        _ptr(codes), _stream(stream))
+    _check(st, "pq_encode_fp8cb")
     return codes
 
 

@@ -2,7 +2,8 @@
 
     python -m decode_attention_product_amd.build
 
-Every call compiles from source.  The packed-FP32 instruction family is
+Every call compiles from source (one object per translation unit, in
+parallel, under _build/, then one link).  The packed-FP32 instruction family is
 switched off for the device code (``-packed-fp32-ops``); the host pass warns
 that it does not know that feature, which is harmless.
 """
@@ -19,8 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpqattn.so")
 
-SOURCES = ["api.hip", "plan.cpp"]
+SOURCES = ["api.hip", "api_fp8.hip", "plan.cpp"]
 ARCH = "gfx950"
+BUILD_DIR = os.path.join(PKG, "_build")
 
 
 def hipcc() -> str:
@@ -36,20 +38,43 @@ def compile_flags():
             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+_NOISE = "is not a recognized feature for this target"
+
+
+def _clean(stderr: str) -> str:
+    return "\n".join(l for l in stderr.splitlines() if _NOISE not in l)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile libpqattn.so; returns its path.  Raises on a compiler error."""
+    """Compile libpqattn.so; returns its path.  Raises on a compiler error.
+    The translation units compile in parallel, then link."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), *compile_flags(), "-c", "-o", obj, os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                            text=True)))
+        objs.append(obj)
+    failed = []
+    for src, pr in procs:
+        _, err = pr.communicate()
+        err = _clean(err)
+        if pr.returncode != 0:
+            failed.append(f"{src} ({pr.returncode}):\n{err}")
+        elif verbose and err.strip():
+            print(err, file=sys.stderr)
+    if failed:
+        raise RuntimeError("hipcc failed: " + "\n".join(failed))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *compile_flags(), "-shared", "-o", tmp,
-           *[os.path.join(CSRC, s) for s in SOURCES]]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+        raise RuntimeError(f"link failed ({r.returncode}):\n{_clean(r.stderr)}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -259,7 +259,7 @@ pq_status launch_reduce(int64_t rows, int32_t C, const float* pm, const float* p
                         float* out, hipStream_t stream, hipEvent_t stop = nullptr) {
   if (rows == 0) return PQ_OK;
   ReduceArgs a{pm, pl, po, out, C};
-  return launch(reinterpret_cast<const void*>(&reduce_kernel), dim3(unsigned(rows)),
+  return launch(reinterpret_cast<const void*>(&reduce_kernel<kHeadDim>), dim3(unsigned(rows)),
                 dim3(kReduceThreads), &a, stream, nullptr, stop);
 }
 

@@ -53,14 +53,52 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kDecodeThreads = 1024;
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Codebook element formats: fp16, or the 8-bit OCP FP8 E4M3 format (sign,
+// 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities;
+// bytes 0x7F and 0xFF are NaN and are not valid codebook entries) for the
+// low-precision codebooks of the AQPIM page, section 4.2.  Every E4M3 value
+// is an fp16 value, so the kernels convert on load and from there on run
+// the fp16 arithmetic unchanged: an FP8 codebook gives exactly the results
+// of its fp16 upcast.
+enum class CbFmt { F16, E4M3 };
+
+// Two E4M3 bytes (bits 0-7 and 8-15 of w) as two fp16 values.  The byte's
+// 7 magnitude bits shifted to bits 7..13 of an fp16 form exponent e and
+// mantissa f, i.e. (1 + f/8) 2^(e-15), or f 2^-17 for e = 0; times 2^8 that
+// is the E4M3 value (1 + f/8) 2^(e-7), resp. f 2^-9, exactly.  The sign bit
+// moves to bit 15.
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+  const uint32_t mag = ((w & 0x7Fu) << 7) | ((w & 0x7F00u) << 15);
+  const f16x2 v = __builtin_bit_cast(f16x2, mag) * f16x2{(_Float16)256.0f, (_Float16)256.0f};
+  return __builtin_bit_cast(uint32_t, v) | ((w & 0x80u) << 8) | ((w & 0x8000u) << 16);
+}
+// Four E4M3 bytes (little-endian in w) as four fp16 values.
+__device__ __forceinline__ f16x4 e4m3x4_to_f16x4(uint32_t w) {
+  const uint32_t lo = e4m3x2_to_f16x2(w), hi = e4m3x2_to_f16x2(w >> 16);
+  return __builtin_bit_cast(f16x4, make_uint2(lo, hi));
+}
+// Codebook elements e .. e+3 (e a multiple of 4) as fp16.
+template <CbFmt F>
+__device__ __forceinline__ f16x4 cb_load4(const void* base, int64_t e) {
+  if constexpr (F == CbFmt::F16) return *reinterpret_cast<const f16x4*>(static_cast<const _Float16*>(base) + e);
+  else return e4m3x4_to_f16x4(*reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(base) + e));
+}
+// Codebook element e as fp16.
+template <CbFmt F>
+__device__ __forceinline__ _Float16 cb_load1(const void* base, int64_t e) {
+  if constexpr (F == CbFmt::F16) return static_cast<const _Float16*>(base)[e];
+  else return __builtin_bit_cast(f16x2, e4m3x2_to_f16x2(static_cast<const uint8_t*>(base)[e]))[0];
+}
 
 struct DecodeArgs {
   const __half* q;           // [B][Hq][D]
   uint8_t* k_codes;          // [B][Hkv][Lmax][M]; written only by the step
   uint8_t* v_codes;          //   kernel, at the new token's slot
-  const __half* k_cb;        // [Hkv][M][K][DS]
-  const __half* v_cb;
+  const void* k_cb;          // [Hkv][M][K][DS], fp16 or E4M3 (the kernel's CbFmt)
+  const void* v_cb;
   const int32_t* lens;       // [B]
   float* part_m;             // [B*Hq][C]     chunk records; all three null:
   float* part_l;             // [B*Hq][C]     the normalised output is written
@@ -415,8 +453,6 @@ __device__ __forceinline__ void token_scores(const float* lut, const Codes& code
   }
 }
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
 // -|c|^2 / 2 of N codewords whose operand pieces this lane holds (codeword
 // n: 4 dims per k-step s in b[n][s]; the four lanes l16, l16+16, l16+32,
 // l16+48 hold the rest of it).  Every lane's partial sums (an fdot2 chain
@@ -603,7 +639,7 @@ __device__ __forceinline__ void merge_rows(const DecodeArgs& a, int64_t row0, in
 // records into the output.
 // PAGED: the codes are read (and the new token's written) through the block
 // table of a paged cache.
-template <int G, int M, int NT, bool STEP, bool PAGED, int CPW>
+template <int G, int M, int NT, bool STEP, bool PAGED, int CPW, CbFmt F = CbFmt::F16>
 __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   constexpr int NTHR = kDecodeThreads;
   constexpr int D = 128;
@@ -676,7 +712,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       page[i] = t < a.Lmax ? row[t >> a.page_shift] : 0;
     }
   }
-  const __half* ckg = a.k_cb + int64_t(g) * M * K * DS;
+  const int64_t cb_g = int64_t(g) * M * K * DS;   // first element of KV head g's codebooks
   // table build: wave w owns segment m_l = w % M and codeword tiles
   // nt = w / M + (NW / M) * i
   const int m_l = wave % M;
@@ -701,9 +737,9 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
 #pragma unroll
   for (int i = 0; i < LUT_JOBS; ++i) {
     const int nt = wave / M + (NW / M) * i;
-    const __half* row = ckg + (int64_t(m_l) * K + nt * 16 + l16) * DS + 4 * q4;
+    const int64_t row = cb_g + (int64_t(m_l) * K + nt * 16 + l16) * DS + 4 * q4;
 #pragma unroll
-    for (int s = 0; s < KSTEP_Q; ++s) ckb[i][s] = *reinterpret_cast<const f16x4*>(row + s * 16);
+    for (int s = 0; s < KSTEP_Q; ++s) ckb[i][s] = cb_load4<F>(a.k_cb, row + s * 16);
   }
 
   len = len < 0 ? 0 : (len > a.Lmax ? a.Lmax : len);
@@ -834,13 +870,12 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   // are needed by the scores and it is requested after them.
   f16x4 cvl[STEP ? LUT_JOBS : 1][KSTEP_Q];
   auto load_cvl = [&]() {
-    const __half* cvg_l = a.v_cb + int64_t(g) * M * K * DS;
 #pragma unroll
     for (int i = 0; i < LUT_JOBS; ++i) {
       const int nt = wave / M + (NW / M) * i;
-      const __half* row = cvg_l + (int64_t(m_l) * K + nt * 16 + l16) * DS + 4 * q4;
+      const int64_t row = cb_g + (int64_t(m_l) * K + nt * 16 + l16) * DS + 4 * q4;
 #pragma unroll
-      for (int s = 0; s < KSTEP_Q; ++s) cvl[i][s] = *reinterpret_cast<const f16x4*>(row + s * 16);
+      for (int s = 0; s < KSTEP_Q; ++s) cvl[i][s] = cb_load4<F>(a.v_cb, row + s * 16);
     }
   };
   constexpr bool kCvlEarly = NT <= 2;
@@ -966,7 +1001,6 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   // operand registers (the 16 lanes of a row group read 32 contiguous
   // bytes), so no VALU work puts them in MFMA order.
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-  const _Float16* cvg = reinterpret_cast<const _Float16*>(a.v_cb) + int64_t(g) * M * K * DS;
   const int tile = wave % NTILE;
   const int ksl = wave / NTILE;               // bins [ksl * KSL, (ksl + 1) * KSL)
   const int m_v = tile % M;
@@ -974,9 +1008,9 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   f16x8 cvb[KSL / 32];
 #pragma unroll
   for (int st = 0; st < KSL / 32; ++st) {
-    const _Float16* src = cvg + (int64_t(m_v) * K + ksl * KSL + st * 32 + 8 * q4) * DS + jt * 16 + l16;
+    const int64_t src = cb_g + (int64_t(m_v) * K + ksl * KSL + st * 32 + 8 * q4) * DS + jt * 16 + l16;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) cvb[st][j] = src[j * DS];
+    for (int j = 0; j < 8; ++j) cvb[st][j] = cb_load1<F>(a.v_cb, src + j * DS);
   }
 
   // ---- 4. V histogram (fixed point, integer LDS atomics) -----------------------
@@ -1192,9 +1226,10 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
 
 // G query heads per KV head, M segments, NT token slots per thread, STEP as
 // above; the codes in a dense [B][Hkv][Lmax][M] cache.
-template <int G, int M, int NT, bool STEP, int CPW = 1>
+// F: the codebooks' element format.
+template <int G, int M, int NT, bool STEP, int CPW = 1, CbFmt F = CbFmt::F16>
 __global__ __launch_bounds__(kDecodeThreads) void decode_partials_kernel(DecodeArgs a) {
-  score_chunk<G, M, NT, STEP, false, CPW>(a);
+  score_chunk<G, M, NT, STEP, false, CPW, F>(a);
 }
 
 // The same over a paged cache (block table and per-head page pools).
@@ -1212,8 +1247,8 @@ struct ReduceArgs {
   int32_t C;
 };
 
-__global__ __launch_bounds__(128) void reduce_kernel(ReduceArgs a) {
-  constexpr int D = 128;
+template <int D>
+__global__ __launch_bounds__(D) void reduce_kernel(ReduceArgs a) {
   const int64_t row = blockIdx.x;
   const int d = threadIdx.x;
   a.out[row * D + d] = merge_chunks(a.part_m + row * a.C, a.part_l + row * a.C,

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
       qa[s] = *reinterpret_cast<const f16x4*>(a.q + (int64_t(b0 + l16) * a.Hq + g) * D + m_l * DS +
                                               s * 16 + 4 * q4);
   }
-  const __half* ckg = a.k_cb + int64_t(g) * M * K * DS;
+  const __half* ckg = static_cast<const __half*>(a.k_cb) + int64_t(g) * M * K * DS;
   f16x4 ckb[LUT_JOBS][KSTEP_Q];
 #pragma unroll
   for (int i = 0; i < LUT_JOBS; ++i) {

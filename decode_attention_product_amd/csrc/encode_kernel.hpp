@@ -39,7 +39,7 @@ constexpr int kMaxEncodePlanes = 4;
 // with its own codebook and code array; blockIdx.z picks the plane.
 struct EncodeArgs {
   const __half* x[kMaxEncodePlanes];       // element (n, h, d) at x[n*sxv + h*sxh + d]
-  const __half* cb[kMaxEncodePlanes];      // [H][M][K][DS]
+  const void* cb[kMaxEncodePlanes];        // [H][M][K][DS], fp16 or E4M3 (the kernel's CbFmt)
   uint8_t* codes[kMaxEncodePlanes];        // code (n, h, m) at codes[s*scs + h*sch + m]
   const int64_t* slots;                    // [N] or null, shared by the planes
   int64_t N;
@@ -126,7 +126,8 @@ __device__ __forceinline__ unsigned long long tiles_best_key(const f32x4 (&acc)[
   return argmax_key(best, bk);
 }
 
-template <int M, int NV>
+// F: the codebooks' element format (converted to fp16 on load).
+template <int M, int NV, CbFmt F = CbFmt::F16>
 __global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
   constexpr int D = 128;
   constexpr int K = 256;
@@ -152,13 +153,13 @@ __global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
   const int nv = int(min<int64_t>(NV, a.N - n0));
 
   // ---- this half of the codebook of (h, m) as MFMA A operands ----------------
-  const __half* cb = a.cb[plane] + (int64_t(h) * M + m) * K * DS + int64_t(half) * (K / 2) * DS;
+  const int64_t cb0 = (int64_t(h) * M + m) * K * DS + int64_t(half) * (K / 2) * DS;
   f16x4 bop[NCT][KS];
 #pragma unroll
   for (int nt = 0; nt < NCT; ++nt)
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      bop[nt][s] = *reinterpret_cast<const f16x4*>(cb + (nt * 16 + l16) * DS + s * 16 + 4 * q4);
+      bop[nt][s] = cb_load4<F>(a.cb[plane], cb0 + (nt * 16 + l16) * DS + s * 16 + 4 * q4);
 
   // B operands (16 vectors x this segment) of one tile; the next tile's are
   // requested while the current one is scored

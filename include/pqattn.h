@@ -332,6 +332,40 @@ pq_status pq_kmeans_many(const pq_encode_desc* desc, int32_t n, const void* cons
                          void* const* codebook, int32_t n_iter, uint8_t* const* codes,
                          void* stream);
 
+/* ---- FP8 codebooks ------------------------------------------------------
+ * The AQPIM page, section 4.2, stores the codebooks as a low-precision float
+ * such as FP8.  These calls take K and V codebooks (and the encode's
+ * codebook) as uint8 [Hkv][M][K][D/M] (resp. [H][M][K][D/M]) arrays of OCP
+ * FP8 E4M3 values: bit 7 the sign, bits 6..3 the exponent e (bias 7), bits
+ * 2..0 the mantissa f; the value is (-1)^s (1 + f/8) 2^(e-7), or
+ * (-1)^s f 2^-9 for e = 0; bytes 0x7F and 0xFF (NaN) are not valid entries
+ * and give unspecified results.  A codebook is half the bytes of the fp16
+ * one (32 KB per KV head and tensor at M = 4, K = 256, D = 128).  Every E4M3
+ * value is an fp16 value and the kernels convert on load, so each call
+ * gives exactly (bit for bit) what its fp16 counterpart gives on the fp16
+ * upcast of the codebooks.  Every other argument, check and layout is the
+ * fp16 call's; the per-request score kernel runs for every shape (the
+ * request-batched one is fp16 only), with the chunking -- and so the
+ * workspace size -- of the fp16 call on the same descriptor. */
+
+/* pq_attn_decode with FP8 E4M3 codebooks. */
+pq_status pq_attn_decode_fp8cb(const pq_attn_desc* desc, const void* q,
+                               const uint8_t* k_codes, const uint8_t* v_codes,
+                               const uint8_t* k_cb, const uint8_t* v_cb, const int32_t* lens,
+                               float* out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* pq_attn_partials with FP8 E4M3 codebooks. */
+pq_status pq_attn_partials_fp8cb(const pq_attn_desc* desc, const void* q,
+                                 const uint8_t* k_codes, const uint8_t* v_codes,
+                                 const uint8_t* k_cb, const uint8_t* v_cb, const int32_t* lens,
+                                 float* part_m, float* part_l, float* part_o, void* stream);
+
+/* pq_encode against an FP8 E4M3 codebook: the nearest of the codewords'
+ * exact values (the decision of pq_encode on the fp16 upcast). */
+pq_status pq_encode_fp8cb(const pq_encode_desc* desc, const void* x, const uint8_t* codebook,
+                          const int64_t* slots, uint8_t* codes, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* pq_status_string(pq_status status);
 

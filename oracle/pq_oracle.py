@@ -33,6 +33,9 @@ It computes the plain definitions, slowly and in float64:
   encode above), then moves every codeword that received vectors to their
   mean -- the exact sum divided by the count in float64, rounded to the fp16
   codebook; a codeword that received none keeps its value.
+* FP8 codebooks (AQPIM page, section 4.2: codebooks kept as a low-precision
+  float such as FP8): bytes of the OCP FP8 E4M3 format are decoded exactly
+  to float64, and attention and encode then run on those codeword values.
 * Paged code cache (AQPIM page, section 5.1 (4): the index cache managed in
   pages as in vLLM; PAM page, section 2.2.2 (2): paged KV management with a
   global block table of where each token lives): token t of request b sits
@@ -58,6 +61,25 @@ import numpy as np
 def default_scale(head_dim: int) -> float:
     """Softmax temperature 1/sqrt(D) (the pages do not state one)."""
     return 1.0 / math.sqrt(head_dim)
+
+
+def fp8_e4m3_to_float64(b) -> np.ndarray:
+    """Exact value of OCP FP8 E4M3 bytes (AQPIM page, section 4.2: codebooks
+    stored as FP8), from the format's definition: bit 7 the sign s, bits 6..3
+    the exponent e (bias 7), bits 2..0 the mantissa f;
+      e > 0:  (-1)^s (1 + f/8) 2^(e - 7)
+      e = 0:  (-1)^s (f/8) 2^(1 - 7)          (subnormal; f = 0 is a signed zero)
+      e = 15 and f = 7: NaN (the format has no infinities).
+    b: uint8 array of any shape; returns float64 of the same shape."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    s = b >> 7
+    e = (b >> 3) & 0xF
+    f = b & 0x7
+    sign = np.where(s == 1, -1.0, 1.0)
+    normal = sign * (1.0 + f / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = sign * (f / 8.0) * 2.0 ** (1 - 7)
+    out = np.where(e == 0, sub, normal)
+    return np.where((e == 15) & (f == 7), np.nan, out)
 
 
 def reconstruct(codes: np.ndarray, cb: np.ndarray) -> np.ndarray:

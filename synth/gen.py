@@ -91,6 +91,14 @@ def codebooks(rng, n_heads, n_sub, n_codes, sub_dim):
     return _normal_f16(rng, (n_heads, n_sub, n_codes, sub_dim))
 
 
+def codebooks_fp8(rng, n_heads, n_sub, n_codes, sub_dim):
+    """uint8 [H][M][K][ds]: entries N(0, 1) rounded to the nearest OCP FP8
+    E4M3 value (ties to even, by torch's conversion), as bytes."""
+    import torch
+    x = rng.standard_normal((n_heads, n_sub, n_codes, sub_dim), dtype=np.float32)
+    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
 def codes(rng, batch, n_heads, max_len, n_sub, n_codes=256):
     """uint8 [B][H][Lmax][M], uniform."""
     return rng.integers(0, n_codes, size=(batch, n_heads, max_len, n_sub), dtype=np.uint8)

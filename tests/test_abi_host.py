@@ -353,3 +353,48 @@ def test_paged_partials_checks(lib):
         p = list(ptrs)
         p[which] = None
         assert lib.pq_attn_partials_paged(ctypes.byref(d), ctypes.byref(_pages()), *p, None) == 1
+
+
+# --------------------------------------------------------------------------
+# FP8-codebook entry points: the same host checks, nothing launched
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, 2), ("n_kv_heads", 3, 2), ("scale", 0.0, 2), ("head_dim", 64, 3),
+    ("n_sub", 2, 3), ("max_len", 40, 3),
+])
+def test_fp8_bad_descriptor(lib, field, value, status):
+    d = _desc(**{field: value})
+    assert lib.pq_attn_decode_fp8cb(ctypes.byref(d), *([FAKE] * 7), FAKE, 1 << 30, None) == status
+    assert lib.pq_attn_partials_fp8cb(ctypes.byref(d), *([FAKE] * 9), None) == status
+
+
+@pytest.mark.parametrize("which", range(7))
+def test_fp8_null_pointer(lib, which):
+    ptrs = [FAKE] * 7          # q, kc, vc, kcb, vcb, lens, out
+    ptrs[which] = None
+    assert lib.pq_attn_decode_fp8cb(ctypes.byref(_desc()), *ptrs, FAKE, 1 << 30, None) == 1
+
+
+def test_fp8_alignment_and_workspace(lib):
+    for which in range(5):
+        ptrs = [FAKE] * 7
+        ptrs[which] = FAKE + 4
+        assert lib.pq_attn_decode_fp8cb(ctypes.byref(_desc()), *ptrs, FAKE, 1 << 30, None) == 6
+    d = _desc(max_len=4096, chunk=256)
+    need = lib.pq_attn_workspace_bytes(ctypes.byref(d))
+    ptrs = [FAKE] * 7
+    assert lib.pq_attn_decode_fp8cb(ctypes.byref(d), *ptrs, None, need, None) == 4
+    assert lib.pq_attn_decode_fp8cb(ctypes.byref(d), *ptrs, FAKE, need - 1, None) == 4
+
+
+def test_fp8_encode_checks(lib):
+    for field, value, status in (("n_vec", -1, 2), ("n_codes", 512, 3), ("codes_bytes", 79, 2),
+                                 ("x_stride_head", 4, 6)):
+        d = _edesc(**{field: value})
+        assert lib.pq_encode_fp8cb(ctypes.byref(d), FAKE, FAKE, None, FAKE, None) == status
+    d = _edesc()
+    assert lib.pq_encode_fp8cb(ctypes.byref(d), None, FAKE, None, FAKE, None) == 1
+    assert lib.pq_encode_fp8cb(ctypes.byref(d), FAKE, None, None, FAKE, None) == 1
+    assert lib.pq_encode_fp8cb(ctypes.byref(d), FAKE, FAKE + 4, None, FAKE, None) == 6
+    assert lib.pq_encode_fp8cb(ctypes.byref(d), FAKE, FAKE, None, FAKE + 1, None) == 6

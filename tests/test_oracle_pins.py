@@ -590,3 +590,68 @@ def test_kmeans_fixed_point_and_segment_independence():
     b_cb, b_codes = oracle.kmeans(xs, case["cb_init"][:, [1, 0, 2, 3]], 2)
     np.testing.assert_array_equal(b_cb, a_cb[:, [1, 0, 2, 3]])
     np.testing.assert_array_equal(b_codes, a_codes[:, :, [1, 0, 2, 3]])
+
+
+# --------------------------------------------------------------------------
+# FP8 codebooks (AQPIM page, section 4.2: codebooks as a low-precision float
+# such as FP8): the E4M3 decode and what it implies
+# --------------------------------------------------------------------------
+
+def test_fp8_e4m3_values_by_hand():
+    """Bytes whose values follow from the format's fields by hand: sign,
+    exponent (bias 7), mantissa, the subnormal range, the largest value and
+    the NaN encoding."""
+    cases = {
+        0x00: 0.0, 0x38: 1.0, 0x40: 2.0, 0x3C: 1.5, 0x30: 0.5, 0x3F: 1.875,
+        0x7E: 448.0, 0xFE: -448.0, 0xB8: -1.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9,
+        0x07: 7 * 2.0 ** -9, 0x04: 2.0 ** -7, 0x77: 1.875 * 2.0 ** 7, 0x78: 256.0,
+    }
+    b = np.array(list(cases), dtype=np.uint8)
+    got = oracle.fp8_e4m3_to_float64(b)
+    np.testing.assert_array_equal(got, np.array(list(cases.values())))
+    neg0 = oracle.fp8_e4m3_to_float64(np.array([0x80], np.uint8))[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) == -1.0
+    assert np.isnan(oracle.fp8_e4m3_to_float64(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def test_fp8_e4m3_decode_matches_torch():
+    """All 256 bytes against torch's own float8_e4m3fn -> float64 conversion."""
+    torch = pytest.importorskip("torch")
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("this torch has no float8_e4m3fn")
+    b = np.arange(256, dtype=np.uint8)
+    ours = oracle.fp8_e4m3_to_float64(b)
+    ref = torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert (np.isnan(ours) == nan).all() and nan.sum() == 2
+    np.testing.assert_array_equal(ours[~nan], ref[~nan])
+    np.testing.assert_array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+def test_fp8_values_are_fp16_values():
+    """Every finite E4M3 value survives a round trip through fp16 -- the
+    fact the GPU path rests on (it converts codebooks to fp16 on load)."""
+    v = oracle.fp8_e4m3_to_float64(np.arange(256, dtype=np.uint8))
+    v = v[~np.isnan(v)]
+    np.testing.assert_array_equal(v.astype(np.float16).astype(np.float64), v)
+
+
+def test_fp8_codebook_is_half_the_page_size():
+    """At M=4, K=256, 32 dims an FP8 codebook set is 32 KB, half of the
+    page's 64 KB fp16 figure."""
+    f = _facts()["codebook"]
+    cb8 = gen.codebooks_fp8(np.random.default_rng(60), 2, f["n_sub"], f["n_codes"], f["sub_dim"])
+    assert cb8.dtype == np.uint8 and cb8[0].nbytes * 2 == f["bytes"] == 65536
+
+
+def test_fp8_generator_rounds_to_nearest():
+    """The generator's bytes decode to the E4M3 value nearest the drawn
+    normal (checked against all 254 finite values)."""
+    rng = np.random.default_rng(61)
+    cb8 = gen.codebooks_fp8(rng, 1, 1, 256, 8)
+    x = np.random.default_rng(61).standard_normal((1, 1, 256, 8), dtype=np.float32).astype(np.float64)
+    table = oracle.fp8_e4m3_to_float64(np.arange(256, dtype=np.uint8))
+    finite = table[~np.isnan(table)]
+    got = oracle.fp8_e4m3_to_float64(cb8)
+    best = np.abs(x[..., None] - finite).min(axis=-1)
+    np.testing.assert_array_equal(np.abs(x - got), best)
