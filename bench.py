@@ -9,22 +9,25 @@ A step is the whole hot path for one layer and one new token, in one launch
   3. the last workgroup of each (request, KV head) merges the chunks -> out.
 The same step through three launches (pq_encode_many, pq_attn_partials,
 pq_attn_reduce) is timed too and reported under "detail".
-The workload is the GQA decode shape (B=8, Hq=64, Hkv=8, L=8192, M=8,
-K=256).  Inputs live in HBM before timing starts; N seeded replicas of every
-input are rotated so that the working set (>= 512 MiB) is twice the 256 MB
-Infinity Cache and each step reads its codes from HBM.
+The headline workload is the GQA decode shape (B=8, Hq=64, Hkv=8, L=8192,
+M=8, K=256).  Inputs live in HBM before timing starts; N seeded replicas of
+every input are rotated so that the working set (>= 512 MiB) is twice the
+256 MB Infinity Cache and each step reads its codes from HBM.
 
-Further legs in the same line: "long_context" (the same one-launch step on
-the long-context split-K workload, B=1, Hq=64, Hkv=8, L=131072, M=4, 64
-chunks of 2048 tokens per KV head), "paged", "encode", "kmeans" and
-"stream_reference" (device copies of the step's size and of 512 MiB: what
-one launch reaches on the same box).
+Further legs in the same line: "workloads" (the step on every workload:
+tiny, page-sizing, gqa, long-splitk, ragged), "long_context" (chunk 2048 and
+the library's chunk), "paged", "fp8" (the plain decode with FP8 codebooks
+next to fp16 ones), "encode", "kmeans" and "stream_reference" (a read-only
+streaming kernel and device copies of the step's size and of 512 MiB: what
+one launch reaches on the same box), and "cpu_baselines" (the oracle on
+every workload).
 
 Prints one JSON line.  `value` = KV tokens scanned per second over the timed
 steps (sum of lens per step / step time).  `roofline` is the step kernel's
-algorithmic bytes per launch over its average duration, timed with HIP
-events the runtime stamps at the kernel's own start and end.  `cpu_baseline` is the
-CPU oracle on the same workload (repeated for 10+ s), on the host cores.
+algorithmic bytes per launch over its average duration in the timed region
+(the step is one launch, so that is the time per step between HIP events
+around K back-to-back steps).  `cpu_baseline` is the CPU oracle on the same
+workload (repeated for 10+ s), on the host cores.
 """
 from __future__ import annotations
 
@@ -112,33 +115,92 @@ def stored_traffic():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wid, min_seconds=10.0, max_seconds=30.0):
-    import oracle
-    from synth import gen
-    inp = gen.workload_inputs(wid, with_encode=False)
-    args = [inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")]
-    tokens = int(inp["lens"].sum())
+def _repeat(fn, min_seconds, max_seconds):
+    """Run fn until min_seconds have passed (or the next run would pass
+    max_seconds); returns (runs, seconds)."""
     reps = 0
     t0 = time.perf_counter()
     while True:
-        oracle.decode_attention(*args)
+        fn()
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds or el + el / reps > max_seconds:
-            break
-    return {"value": tokens * reps / el, "unit": "KV tokens/s", "cores": _oracle_threads(),
-            "kind": "oracle",
-            "sample": f"{gen.WORKLOADS[wid].name} workload, whole decode step, repeated {reps}x "
-                      f"({el:.1f} s)"}
+            return reps, el
 
 
-def _oracle_threads():
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
         n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
         return int(max(n)) if n else 1
     except Exception:
         return 1
+
+
+def _one_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(1)
+    except Exception:
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def cpu_baseline(wid, min_seconds=10.0, max_seconds=30.0, single_thread=False):
+    """The oracle's whole decode step on workload wid (every KV head), repeated
+    for min_seconds.  Its NumPy elementwise work is single-threaded; its
+    matrix-vector products run on the BLAS threads (`cores`), or on one with
+    single_thread."""
+    import oracle
+    from synth import gen
+    inp = gen.workload_inputs(wid, with_encode=False)
+    args = [inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")]
+    tokens = int(inp["lens"].sum())
+    import contextlib
+    with (_one_thread() if single_thread else contextlib.nullcontext()):
+        cores = 1 if single_thread else _blas_threads()
+        reps, el = _repeat(lambda: oracle.decode_attention(*args), min_seconds, max_seconds)
+    return {"value": tokens * reps / el, "unit": "KV tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{gen.WORKLOADS[wid].name} workload, whole decode step, repeated {reps}x "
+                      f"({el:.1f} s); elementwise NumPy on one thread, BLAS on {cores}"}
+
+
+def cpu_baselines(seconds=3.0):
+    """The oracle beside every workload, on bounded samples of a few seconds
+    each: the whole decode step of the tiny, page-sizing and ragged workloads
+    (the first two also on one thread), one KV head of the long-context one
+    (scaled to KV tokens: a token is one cached step of all 8 KV heads), and
+    the ragged prefill's encode on a 500-token sample of K vectors."""
+    import oracle
+    from synth import gen
+    res = {}
+    for wid in (1, 2):
+        name = gen.WORKLOADS[wid].name
+        res[name] = cpu_baseline(wid, seconds, 4 * seconds)
+        res[name + " (1 thread)"] = cpu_baseline(wid, seconds, 4 * seconds, single_thread=True)
+    w = gen.WORKLOADS[4]
+    inp = gen.workload_inputs(4, with_encode=False)
+    G = w.group
+    args = (inp["q"][:, :G], inp["k_codes"][:, :1], inp["v_codes"][:, :1], inp["k_cb"][:1],
+            inp["v_cb"][:1], inp["lens"])
+    reps, el = _repeat(lambda: oracle.decode_attention(*args), seconds, 4 * seconds)
+    head_tokens = int(inp["lens"].sum())
+    res[w.name] = {"value": head_tokens * reps / el / w.n_kv_heads, "unit": "KV tokens/s",
+                   "cores": _blas_threads(), "kind": "oracle",
+                   "sample": f"KV head 0 and its {G} query heads over {head_tokens} tokens, "
+                             f"repeated {reps}x ({el:.1f} s); scaled by 1/{w.n_kv_heads} KV heads"}
+    res["ragged"] = cpu_baseline(5, seconds, 4 * seconds)
+    w = gen.WORKLOADS[5]
+    rng = gen.rng_for(5)
+    cb = gen.codebooks(rng, w.n_kv_heads, w.n_sub, w.n_codes, w.sub_dim)
+    x, _ = gen.noisy_codewords(rng, cb, 500, w.encode_sigma)
+    reps, el = _repeat(lambda: oracle.encode(x, cb), seconds, 4 * seconds)
+    n = x.shape[0] * x.shape[1]
+    res["ragged prefill encode"] = {
+        "value": n * reps / el, "unit": "vectors/s", "cores": _blas_threads(), "kind": "oracle",
+        "sample": f"{n} K vectors (500 tokens x {w.n_kv_heads} heads) of the ragged prefill, "
+                  f"repeated {reps}x ({el:.1f} s)"}
+    return res
 
 
 def main():
@@ -156,7 +218,9 @@ def main():
     ap.add_argument("--paged-steps", type=int, default=500)
     ap.add_argument("--no-kmeans", action="store_true", help="skip the codebook-learning leg")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context step leg")
-    ap.add_argument("--no-stream", action="store_true", help="skip the device-copy reference")
+    ap.add_argument("--no-stream", action="store_true", help="skip the streaming references")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload step legs")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-codebook leg")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run 3 device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -267,7 +331,9 @@ def main():
 
     value = tokens_per_step / (step_ms_plain * 1e-3)
     alg = algorithmic_bytes(w, lens_np)
-    achieved = alg / (score_ms * 1e-3) / 1e9
+    # the step is one launch: its average duration in the timed region is the
+    # time per step between the events around K back-to-back steps
+    achieved = alg / (step_ms_plain * 1e-3) / 1e9
 
     result = {
         "metric": "PQ-KV decode attn: KV tokens scanned/s + % of HBM peak GB/s; encode vectors/s",
@@ -288,7 +354,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(),
                      "kernel": "decode_partials_kernel (decode-step variant)", "algorithmic_bytes": alg,
-                     "avg_launch_us": score_ms * 1e3},
+                     "avg_launch_us": step_ms_plain * 1e3,
+                     "avg_launch_us_kernel_events": score_ms * 1e3},
         "detail": {"step_us_with_kernel_events": step_ms * 1e3, "step_us": step_ms_plain * 1e3,
                    "step_kernel_us_p50": float(np.median(kern_ms)) * 1e3,
                    "step_us_three_launches": step_ms_three * 1e3,
@@ -303,19 +370,44 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         result["copy_probe_bytes"] = n
+    if not args.no_workloads:
+        result["workloads"] = {}
+        for wi in (1, 2, 3):
+            if wi == wid:
+                result["workloads"][w.name] = {
+                    "value": value, "unit": "KV tokens/s", "step_us": step_ms_plain * 1e3,
+                    "roofline": {"bound": "hbm", "achieved": achieved, "frac": achieved / HBM_PEAK_GBS,
+                                 "algorithmic_bytes": alg}}
+            else:
+                ww = gen.WORKLOADS[wi]
+                result["workloads"][ww.name] = step_leg(pq, torch, dev, wi, args.paged_steps,
+                                                        args.warmup, chunk=ww.chunk)
     if not args.no_long and wid != 4:
         result["long_context"] = long_context_leg(pq, torch, dev, args.paged_steps, args.warmup)
+        if "workloads" in result:
+            lc = result["long_context"]
+            result["workloads"]["long-splitk"] = {
+                k: lc[k] for k in ("workload", "chunk", "n_chunks", "value", "unit", "step_us", "roofline")}
     if not args.no_paged:
         result["paged"] = paged_leg(pq, torch, dev, args.paged_steps, args.warmup,
                                     step_ms_plain * 1e3 if wid == 3 else None)
+    if not args.no_fp8:
+        result["fp8"] = fp8_leg(pq, torch, dev, args.paged_steps, args.warmup)
     if not args.no_encode:
         result["encode"] = encode_leg(pq, torch, dev, args.encode_reps)
     if not args.no_kmeans:
         result["kmeans"] = kmeans_leg(pq, torch, dev)
     if not args.no_stream:
         result["stream_reference"] = stream_leg(torch, dev)
+    if "paged" in result and "workloads" in result:
+        rg = result["paged"]["ragged"]
+        result["workloads"]["ragged"] = {
+            "value": rg["dense_value"], "unit": "KV tokens/s", "step_us": rg["dense_step_us"],
+            "roofline": rg["dense_roofline"], "paged_step_us": rg["step_us"],
+            "note": "dense padded cache; the paged step is in paged.ragged"}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wid)
+        result["cpu_baselines"] = cpu_baselines()
     print(json.dumps(result), flush=True)
 
 
@@ -416,18 +508,28 @@ def paged_leg(pq, torch, dev, steps, warmup, dense_gqa_us):
         hip.destroy(raw)
         step_us = timed(paged)
         tokens = int(lens_np.sum())
-        achieved = alg / (kern_us * 1e-6) / 1e9
+        achieved = alg / (step_us * 1e-6) / 1e9
+        kernel = ("decode_paged_kernel (decode-step variant), one launch" if name == "gqa" else
+                  "encode_kernel (new tokens) + decode_mha_kernel (paged), two launches")
         leg = {"workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} Lmax={L} M={M}, {tokens} tokens",
                "value": tokens / (step_us * 1e-6), "unit": "KV tokens/s", "step_us": step_us,
-               "kernel_us": kern_us, "replicas": R,
+               "events_us": kern_us, "replicas": R,
                "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": alg,
-                            "kernel": "decode_paged_kernel (decode-step variant)"},
+                            "kernel": kernel},
                "pool_slots_per_head": n_pages * P, "padded_slots_per_head": B * L}
         if name == "gqa" and dense_gqa_us is not None:
             leg["dense_step_us"] = dense_gqa_us
         if name == "ragged":
             leg["dense_step_us"] = timed(dense)
+            alg_dense = algorithmic_bytes(w, lens_np)
+            ach = alg_dense / (leg["dense_step_us"] * 1e-6) / 1e9
+            leg["dense_value"] = tokens / (leg["dense_step_us"] * 1e-6)
+            leg["dense_roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                                     "algorithmic_bytes": alg_dense,
+                                     "kernel": "encode_kernel (new tokens) + decode_mha_kernel, "
+                                               "two launches"}
             # the plain decode over the same caches (no new token): with one
             # query head per KV head and 2048 pairs it runs the
             # request-batched score kernel
@@ -507,11 +609,11 @@ def long_context_leg(pq, torch, dev, steps, warmup):
         b.record(stream)
         torch.cuda.synchronize()
         step_us = a.elapsed_time(b) * 1e3 / steps
-        achieved = alg / (kern_us * 1e-6) / 1e9
+        achieved = alg / (step_us * 1e-6) / 1e9
         return {"chunk": chunk,
                 "n_chunks": pq.pq_attn_num_chunks(desc),
                 "value": tokens / (step_us * 1e-6), "unit": "KV tokens/s", "step_us": step_us,
-                "kernel_us": kern_us,
+                "events_us": kern_us,
                 "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": achieved / HBM_PEAK_GBS, "algorithmic_bytes": alg,
                              "kernel": "decode_partials_kernel (decode-step variant)"}}
@@ -524,14 +626,171 @@ def long_context_leg(pq, torch, dev, steps, warmup):
     return leg
 
 
-def stream_leg(torch, dev, reps=200):
-    """Reference HBM rates on the same box: device-to-device copies (one
-    read and one write per byte) of the step kernel's size (~10 MB, one
-    launch each) and of 512 MiB, rotated over enough buffers that the copies
-    miss the Infinity Cache.  What one launch of this size can reach, next to
-    the step kernel's roofline fraction."""
+def step_replicas(torch, dev, wid, seed, budget=512 << 20, max_reps=None):
+    """Seeded replicas of workload wid's inputs on the device plus each one's
+    new-token K and V, enough that they fill `budget` bytes."""
+    from synth import gen
+    w = gen.WORKLOADS[wid]
+    base = gen.workload_inputs(wid, with_encode=False)
+    alg = algorithmic_bytes(w, base["lens"])
+    R = max(2, math.ceil(budget / alg))
+    if max_reps:
+        R = min(R, max_reps)
+    reps = []
+    for r in range(R):
+        inp = base if r == 0 else gen.workload_inputs(wid, replica=r, with_encode=False)
+        rng = np.random.default_rng([seed + wid, r])
+        xk, _, xv, _ = gen.step_tokens(rng, inp["k_cb"], inp["v_cb"], w.batch)
+        t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev)
+             for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")}
+        t["xk"], t["xv"] = torch.from_numpy(xk).to(dev), torch.from_numpy(xv).to(dev)
+        reps.append(t)
+    return w, base["lens"], reps
+
+
+def step_leg(pq, torch, dev, wid, steps, warmup, chunk=0):
+    """The one-launch decode step on workload wid, timed as the headline step:
+    HIP events around `steps` back-to-back steps over rotated replicas."""
+    w, lens_np, reps = step_replicas(torch, dev, wid, 7400)
+    R = len(reps)
     stream = torch.cuda.current_stream()
+    B, Hq, D = w.batch, w.n_q_heads, w.head_dim
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    desc = pq.attn_desc(reps[0]["q"], reps[0]["k_codes"], reps[0]["k_cb"], chunk=chunk)
+    ws = pq.step_workspace(desc, dev)
+
+    def step(t):
+        pq.pq_attn_decode_step(t["q"], t["xk"], t["xv"], t["k_codes"], t["v_codes"], t["k_cb"],
+                               t["v_cb"], t["lens"], out, desc=desc, workspace=ws, stream=stream)
+
+    for i in range(warmup):
+        step(reps[i % R])
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(steps):
+        step(reps[i % R])
+    b.record(stream)
+    torch.cuda.synchronize()
+    step_us = a.elapsed_time(b) * 1e3 / steps
+    tokens = int(lens_np.sum())
+    alg = algorithmic_bytes(w, lens_np)
+    ach = alg / (step_us * 1e-6) / 1e9
+    return {"workload": f"{w.name}: B={B} Hq={Hq} Hkv={w.n_kv_heads} L={w.max_len} M={w.n_sub}",
+            "chunk": int(desc.chunk) or "library", "n_chunks": pq.pq_attn_num_chunks(desc),
+            "replicas": R, "value": tokens / (step_us * 1e-6), "unit": "KV tokens/s",
+            "step_us": step_us,
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBS, "algorithmic_bytes": alg,
+                         "kernel": "decode_partials_kernel (decode-step variant), one launch"}}
+
+
+def fp8_leg(pq, torch, dev, steps, warmup):
+    """The plain decode (score kernel + merge kernel) of the GQA workload with
+    FP8 E4M3 codebooks (pq_attn_decode_fp8cb) next to the same decode with
+    fp16 ones (pq_attn_decode): codebook bytes halve, the codes do not."""
+    from synth import gen
+    w, lens_np, reps = step_replicas(torch, dev, 3, 7500)
+    R = len(reps)
+    rng = np.random.default_rng(7501)
+    for t in reps:
+        t["k_cb8"] = torch.from_numpy(gen.codebooks_fp8(rng, w.n_kv_heads, w.n_sub, 256, w.sub_dim)).to(dev)
+        t["v_cb8"] = torch.from_numpy(gen.codebooks_fp8(rng, w.n_kv_heads, w.n_sub, 256, w.sub_dim)).to(dev)
+    stream = torch.cuda.current_stream()
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    desc = pq.attn_desc(reps[0]["q"], reps[0]["k_codes"], reps[0]["k_cb"])
+    ws = torch.empty(max(16, pq.pq_attn_workspace_bytes(desc)), dtype=torch.uint8, device=dev)
+
+    def f16(t):
+        pq.pq_attn_decode(t["q"], t["k_codes"], t["v_codes"], t["k_cb"], t["v_cb"], t["lens"], out,
+                          desc=desc, workspace=ws, stream=stream)
+
+    def f8(t):
+        pq.pq_attn_decode_fp8cb(t["q"], t["k_codes"], t["v_codes"], t["k_cb8"], t["v_cb8"], t["lens"],
+                                out, desc=desc, workspace=ws, stream=stream)
+
+    res = {"workload": f"{w.name}: B={w.batch} Hq={w.n_q_heads} Hkv={w.n_kv_heads} L={w.max_len} "
+                       f"M={w.n_sub}, plain decode (score + merge launches)", "replicas": R}
+    tokens = int(lens_np.sum())
+    cb16 = w.n_kv_heads * 2 * w.n_sub * w.n_codes * w.sub_dim * 2
+    for name, fn, alg in (("fp16", f16, algorithmic_bytes(w, lens_np, step=False)),
+                          ("fp8", f8, algorithmic_bytes(w, lens_np, step=False) - cb16 // 2)):
+        for i in range(warmup):
+            fn(reps[i % R])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(steps):
+            fn(reps[i % R])
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / steps
+        ach = alg / (us * 1e-6) / 1e9
+        res[name] = {"decode_us": us, "value": tokens / (us * 1e-6), "unit": "KV tokens/s",
+                     "algorithmic_bytes": alg, "hbm_gbs": ach, "frac": ach / HBM_PEAK_GBS}
+    return res
+
+
+def _bench_lib():
+    import ctypes
+    path = os.path.join(ROOT, "decode_attention_product_amd", "libpqbench.so")
+    lib = ctypes.CDLL(path)
+    lib.pqbench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.pqbench_stream_read.restype = ctypes.c_int
+    return lib
+
+
+def stream_read_leg(torch, dev, reps=200):
+    """Read-only streaming kernel (libpqbench.so, 16-byte loads, one checksum
+    word per workgroup out): the step's algorithmic bytes on the step kernel's grid (256
+    workgroups of 1024 threads) and on 2048 workgroups of 256, and 512 MiB,
+    rotated over 1 GiB of buffers so every launch reads HBM, not the
+    Infinity Cache.  Timed with HIP events around back-to-back launches."""
+    lib = _bench_lib()
+    stream = torch.cuda.current_stream()
+    chk = torch.zeros(8192, dtype=torch.int32, device=dev)
     res = {}
+    for name, nbytes, grid, block in (("10MB_256x1024", 9864192, 256, 1024),
+                                      ("10MB_2048x256", 9864192, 2048, 256),
+                                      ("512MiB_2048x256", 512 << 20, 2048, 256),
+                                      ("512MiB_8192x256", 512 << 20, 8192, 256)):
+        nbuf = max(2, math.ceil((1 << 30) / nbytes))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3) for _ in range(nbuf)]
+        n = reps if nbytes < (64 << 20) else 20
+
+        def run(i):
+            st = lib.pqbench_stream_read(bufs[i % nbuf].data_ptr(), nbytes, chk.data_ptr(), grid, block,
+                                         stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"pqbench_stream_read: hip error {st}")
+
+        for i in range(10):
+            run(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(n):
+            run(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / n
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"bytes": nbytes, "grid": [grid, block], "us_per_read": us, "gbs_read": gbs,
+                     "frac": gbs / HBM_PEAK_GBS}
+        del bufs
+    return res
+
+
+def stream_leg(torch, dev, reps=200):
+    """Reference HBM rates on the same box: the read-only streaming kernel
+    (stream_read_leg), and device-to-device copies (one read and one write per
+    byte) of the step kernel's size (~10 MB, one launch each) and of 512 MiB,
+    rotated over enough buffers that the copies miss the Infinity Cache.
+    What one launch of this size can reach, next to the step kernel's
+    roofline fraction."""
+    stream = torch.cuda.current_stream()
+    res = {"read_only": stream_read_leg(torch, dev, reps)}
     for name, nbytes in (("10MB", 9864192), ("512MiB", 512 << 20)):
         nbuf = max(2, math.ceil((1 << 30) / nbytes))
         bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1) for _ in range(nbuf)]

@@ -21,6 +21,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpqattn.so")
 
 SOURCES = ["api.hip", "api_fp8.hip", "plan.cpp"]
+# the benchmark's read-only streaming reference, a library of its own
+BENCH_SOURCES = ["stream_ref.hip"]
+BENCH_LIB = os.path.join(PKG, "libpqbench.so")
 ARCH = "gfx950"
 BUILD_DIR = os.path.join(PKG, "_build")
 
@@ -46,11 +49,12 @@ def _clean(stderr: str) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile libpqattn.so; returns its path.  Raises on a compiler error.
-    The translation units compile in parallel, then link."""
+    """Compile libpqattn.so (and the benchmark's libpqbench.so); returns the
+    path of libpqattn.so.  Raises on a compiler error.  The translation units
+    compile in parallel, then each library links."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs, procs = [], []
-    for src in SOURCES:
+    for src in SOURCES + BENCH_SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         cmd = [hipcc(), *compile_flags(), "-c", "-o", obj, os.path.join(CSRC, src)]
         if verbose:
@@ -68,14 +72,16 @@ def build(verbose: bool = False) -> str:
             print(err, file=sys.stderr)
     if failed:
         raise RuntimeError("hipcc failed: " + "\n".join(failed))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed ({r.returncode}):\n{_clean(r.stderr)}")
-    os.replace(tmp, LIB)
+    n = len(SOURCES)
+    for lib, lib_objs in ((LIB, objs[:n]), (BENCH_LIB, objs[n:])):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", tmp, *lib_objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed ({r.returncode}):\n{_clean(r.stderr)}")
+        os.replace(tmp, lib)
     return LIB
 
 

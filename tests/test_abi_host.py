@@ -398,3 +398,21 @@ def test_fp8_encode_checks(lib):
     assert lib.pq_encode_fp8cb(ctypes.byref(d), FAKE, None, None, FAKE, None) == 1
     assert lib.pq_encode_fp8cb(ctypes.byref(d), FAKE, FAKE + 4, None, FAKE, None) == 6
     assert lib.pq_encode_fp8cb(ctypes.byref(d), FAKE, FAKE, None, FAKE + 1, None) == 6
+
+
+def test_bench_library_exports_the_stream_reference():
+    path = os.path.join(os.path.dirname(pq.LIB_PATH), "libpqbench.so")
+    if not os.path.exists(path):
+        pytest.fail("libpqbench.so is not built (python -m decode_attention_product_amd.build)")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    assert re.search(r"\bT pqbench_stream_read$", out, flags=re.M)
+    lib = ctypes.CDLL(path)
+    lib.pqbench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    # invalid arguments are refused before any launch (hipErrorInvalidValue = 1)
+    assert lib.pqbench_stream_read(None, 16, FAKE, 1, 64, None) == 1
+    assert lib.pqbench_stream_read(FAKE, 15, FAKE, 1, 64, None) == 1
+    assert lib.pqbench_stream_read(FAKE + 8, 16, FAKE, 1, 64, None) == 1
+    assert lib.pqbench_stream_read(FAKE, 16, FAKE, 1, 100, None) == 1
+    assert lib.pqbench_stream_read(FAKE, 16, FAKE, 0, 64, None) == 1
