@@ -28,7 +28,7 @@ EXPORTED = ("pq_attn_num_chunks", "pq_attn_workspace_bytes", "pq_attn_decode",
             "pq_attn_decode_step_paged", "pq_attn_decode_step_paged_timed", "pq_attn_reduce",
             "pq_encode", "pq_encode_many", "pq_codebook_update", "pq_kmeans",
             "pq_kmeans_many", "pq_attn_decode_fp8cb", "pq_attn_partials_fp8cb",
-            "pq_encode_fp8cb", "pq_status_string")
+            "pq_encode_fp8cb", "pq_attn_decode_step_noalloc", "pq_status_string")
 
 
 class PQError(RuntimeError):
@@ -126,6 +126,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pq_attn_partials_fp8cb.restype = ctypes.c_int
     lib.pq_encode_fp8cb.argtypes = [ctypes.POINTER(PQEncodeDesc), P, P, P, P, P]
     lib.pq_encode_fp8cb.restype = ctypes.c_int
+    lib.pq_attn_decode_step_noalloc.argtypes = [ctypes.POINTER(PQAttnDesc), P, P, P, P, P, P, P, P,
+                                                P, P]
+    lib.pq_attn_decode_step_noalloc.restype = ctypes.c_int
     lib.pq_status_string.argtypes = [ctypes.c_int]
     lib.pq_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -349,6 +352,28 @@ def pq_attn_decode_step(q, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, out
     else:
         st = lib.pq_attn_decode_step_timed(*args, events[0], events[1])
     _check(st, "pq_attn_decode_step")
+    return out
+
+
+def pq_attn_decode_step_noalloc(q, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, out, *,
+                                desc=None, chunk=0, scale=None, stream=None):
+    """pq_attn_decode_step without a workspace (C entry point
+    pq_attn_decode_step_noalloc): the library's own device scratch holds the
+    chunk records and counters.  ``out`` (fp32 [B, Hq, D]) is required, so
+    nothing is allocated on this path either.  Calls that overlap in time on
+    one GPU race (they share the scratch)."""
+    import torch
+    if desc is None:
+        desc = attn_desc(q, k_codes, k_cb, chunk=chunk, scale=scale)
+    _check_attn_inputs(desc, q, k_codes, v_codes, k_cb, v_cb, lens)
+    shape_new = (desc.batch, desc.n_kv_heads, desc.head_dim)
+    _need(k_new, "k_new", torch.float16, shape_new)
+    _need(v_new, "v_new", torch.float16, shape_new)
+    _need(out, "out", torch.float32, (desc.batch, desc.n_q_heads, desc.head_dim))
+    st = load_library().pq_attn_decode_step_noalloc(
+        ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_codes), _ptr(v_codes),
+        _ptr(k_cb), _ptr(v_cb), _ptr(lens), _ptr(out), _stream(stream))
+    _check(st, "pq_attn_decode_step_noalloc")
     return out
 
 

@@ -5,6 +5,7 @@
 #include <hip/hip_ext.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "decode_kernel.hpp"
 #include "decode_mha_kernel.hpp"
@@ -266,6 +267,66 @@ pq_status launch_reduce(int64_t rows, int32_t C, const float* pm, const float* p
 }  // namespace
 }  // namespace pqattn
 
+namespace pqattn {
+namespace {
+
+// Where a decode step keeps its scratch: the chunk records (carved as in a
+// workspace of pq_attn_workspace_bytes from `records`) and the arrival
+// counters, B*Hkv 32-bit words that are zero on entry and left zero.
+struct StepScratch {
+  void* records = nullptr;
+  uint32_t* counters = nullptr;
+};
+
+// The checks every decode-step entry point makes before anything is
+// enqueued (the scratch aside).
+pq_status check_step(const pq_attn_desc* desc, const pq_page_table* pages, bool paged,
+                     const void* q, const void* k_new, const void* v_new, const uint8_t* k_codes,
+                     const uint8_t* v_codes, const void* k_cb, const void* v_cb,
+                     const int32_t* lens, const float* out, AttnPlan* p, PagePlan* pg) {
+  pq_status st = plan_attn(desc, p);
+  if (st != PQ_OK) return st;
+  if (paged && (st = plan_pages(*p, pages, pg)) != PQ_OK) return st;
+  st = check_attn_pointers(q, k_codes, v_codes, k_cb, v_cb, lens);
+  if (st != PQ_OK) return st;
+  if (!out || !k_new || !v_new) return PQ_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return PQ_ERR_ALIGN;
+  return PQ_OK;
+}
+
+// The decode step once checked, with its scratch placed.
+pq_status run_step(const AttnPlan& p, const PagePlan* pgp, const void* q, const void* k_new,
+                   const void* v_new, uint8_t* k_codes, uint8_t* v_codes, const void* k_cb,
+                   const void* v_cb, const int32_t* lens, float* out, const StepScratch& ss,
+                   hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  pq_status st;
+  ScoreIO io = score_inputs(q, k_codes, v_codes, k_cb, v_cb, lens, pgp);
+  if (p.C > 1) carve_records(p, ss.records, io);
+  if (p.R > 1) {
+    // one query head per KV head and many pairs: the encode kernel writes the
+    // new codes, then the request-batched score kernel (and the merge) reads
+    // the cache that holds them
+    st = launch_step_encode(p, pgp, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, s, e0);
+    if (st != PQ_OK) return st;
+    if (p.C == 1) {
+      io.out = out;
+      return launch_score(p, io, s, nullptr, e1);
+    }
+    st = launch_score(p, io, s);
+    if (st != PQ_OK) return st;
+    return launch_reduce(p.rows, p.C, io.pm, io.pl, io.po, out, s, e1);
+  }
+  // one launch: encode, attend and (C > 1) the fused merge
+  io.out = out;
+  io.k_new = k_new;
+  io.v_new = v_new;
+  if (p.C > 1) io.counters = ss.counters;
+  return launch_score(p, io, s, e0, e1);
+}
+
+}  // namespace
+}  // namespace pqattn
+
 using namespace pqattn;
 
 extern "C" {
@@ -382,7 +443,8 @@ size_t pq_attn_step_workspace_bytes(const pq_attn_desc* desc) {
   return plan_attn(desc, &p) == PQ_OK ? p.ws_step_bytes : 0;
 }
 
-// The decode step over a dense cache (pages NULL, paged false) or a paged one.
+// The decode step over a dense cache (pages NULL, paged false) or a paged one,
+// its scratch in the caller's workspace.
 static pq_status decode_step(const pq_attn_desc* desc, const void* q, const void* k_new,
                              const void* v_new, uint8_t* k_codes, uint8_t* v_codes,
                              const void* k_cb, const void* v_cb, const int32_t* lens, float* out,
@@ -390,41 +452,18 @@ static pq_status decode_step(const pq_attn_desc* desc, const void* q, const void
                              void* start_event, void* stop_event,
                              const pq_page_table* pages = nullptr, bool paged = false) {
   AttnPlan p;
-  pq_status st = plan_attn(desc, &p);
-  if (st != PQ_OK) return st;
   PagePlan pg;
-  if (paged && (st = plan_pages(p, pages, &pg)) != PQ_OK) return st;
-  const PagePlan* pgp = paged ? &pg : nullptr;
-  st = check_attn_pointers(q, k_codes, v_codes, k_cb, v_cb, lens);
+  pq_status st = check_step(desc, pages, paged, q, k_new, v_new, k_codes, v_codes, k_cb, v_cb,
+                            lens, out, &p, &pg);
   if (st != PQ_OK) return st;
-  if (!out || !k_new || !v_new) return PQ_ERR_NULL;
-  if (!aligned16(k_new) || !aligned16(v_new)) return PQ_ERR_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
   if (p.C > 1 && (!workspace || workspace_bytes < p.ws_step_bytes || !aligned16(workspace)))
     return PQ_ERR_WORKSPACE;
-  ScoreIO io = score_inputs(q, k_codes, v_codes, k_cb, v_cb, lens, pgp);
-  if (p.C > 1) carve_records(p, workspace, io);
-  if (p.R > 1) {
-    // one query head per KV head and many pairs: the encode kernel writes the
-    // new codes, then the request-batched score kernel (and the merge) reads
-    // the cache that holds them
-    st = launch_step_encode(p, pgp, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, s, e0);
-    if (st != PQ_OK) return st;
-    if (p.C == 1) {
-      io.out = out;
-      return launch_score(p, io, s, nullptr, e1);
-    }
-    st = launch_score(p, io, s);
-    if (st != PQ_OK) return st;
-    return launch_reduce(p.rows, p.C, io.pm, io.pl, io.po, out, s, e1);
-  }
-  // one launch: encode, attend and (C > 1) the fused merge
-  io.out = out;
-  io.k_new = k_new;
-  io.v_new = v_new;
-  if (p.C > 1) io.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + p.ws_cnt_off);
-  return launch_score(p, io, s, e0, e1);
+  StepScratch ss;
+  ss.records = workspace;
+  if (p.C > 1) ss.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + p.ws_cnt_off);
+  return run_step(p, paged ? &pg : nullptr, q, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, out,
+                  ss, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
+                  static_cast<hipEvent_t>(stop_event));
 }
 
 pq_status pq_attn_decode_step(const pq_attn_desc* desc, const void* q, const void* k_new,
@@ -633,5 +672,88 @@ pq_status pq_encode_many(const pq_encode_desc* desc, int32_t n, const void* cons
 }
 
 const char* pq_status_string(pq_status status) { return status_string(status); }
+
+}  // extern "C"
+
+// ---- The decode step for callers that cannot allocate ----------------------
+// Its scratch (arrival counters, then chunk records) is a file-scope device
+// array of fixed size instead of a caller's workspace.  In host code the
+// array's name stands for a host-side shadow, not a device address: the
+// device address comes from hipGetSymbolAddress, once per device, and only
+// that address is ever handed to a kernel.
+namespace pqattn {
+namespace {
+
+constexpr size_t kNoAllocCounters = 65536;                    // B * Hkv at most
+constexpr size_t kNoAllocCounterBytes = kNoAllocCounters * 4;  // 256 KiB
+constexpr size_t kNoAllocRecordBytes = size_t(8) << 20;       // chunk records, 8 MiB at most
+constexpr int kNoAllocMaxDevices = 64;
+
+}  // namespace
+}  // namespace pqattn
+
+static __device__ __align__(256) unsigned char scratch[pqattn::kNoAllocCounterBytes +
+                                                       pqattn::kNoAllocRecordBytes];
+
+namespace pqattn {
+namespace {
+
+__global__ void zero_words_kernel(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch[kNoAllocMaxDevices];   // device address of `scratch` per device, once set up
+
+// The current device's scratch address.  The first call on a device takes
+// the address with hipGetSymbolAddress and zeroes the counters with a fill
+// kernel on `stream` (no memset node, so the call can be captured); every
+// later step leaves them at zero again.
+pq_status device_scratch(hipStream_t stream, char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PQ_ERR_HIP;
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return PQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return PQ_ERR_HIP;
+    uint32_t* counters = static_cast<uint32_t*>(ptr);
+    uint32_t n = uint32_t(kNoAllocCounters);
+    void* args[] = {&counters, &n};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&zero_words_kernel), dim3(64), dim3(256), args,
+                        0, stream) != hipSuccess)
+      return PQ_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = static_cast<char*>(g_scratch[dev]);
+  return PQ_OK;
+}
+
+}  // namespace
+}  // namespace pqattn
+
+extern "C" {
+
+pq_status pq_attn_decode_step_noalloc(const pq_attn_desc* desc, const void* q, const void* k_new,
+                                      const void* v_new, uint8_t* k_codes, uint8_t* v_codes,
+                                      const void* k_cb, const void* v_cb, const int32_t* lens,
+                                      float* out, void* stream) {
+  AttnPlan p;
+  PagePlan pg;
+  pq_status st = check_step(desc, nullptr, false, q, k_new, v_new, k_codes, v_codes, k_cb, v_cb,
+                            lens, out, &p, &pg);
+  if (st != PQ_OK) return st;
+  if (size_t(p.B) * size_t(p.Hkv) > kNoAllocCounters || p.ws_bytes > kNoAllocRecordBytes)
+    return PQ_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = nullptr;
+  if ((st = device_scratch(s, &base)) != PQ_OK) return st;
+  StepScratch ss;
+  ss.counters = reinterpret_cast<uint32_t*>(base);
+  ss.records = base + kNoAllocCounterBytes;
+  return run_step(p, nullptr, q, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, out, ss, s,
+                  nullptr, nullptr);
+}
 
 }  // extern "C"

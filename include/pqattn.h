@@ -332,6 +332,24 @@ pq_status pq_kmeans_many(const pq_encode_desc* desc, int32_t n, const void* cons
                          void* const* codebook, int32_t n_iter, uint8_t* const* codes,
                          void* stream);
 
+/* pq_attn_decode_step for callers that cannot allocate device memory or pass
+ * a workspace -- code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments and results as
+ * pq_attn_decode_step on a dense cache, without workspace: the chunk records
+ * and arrival counters live in a device array inside the library, 8 MiB of
+ * records and 65,536 counters, held on each GPU the library runs on until
+ * the process ends.  Shapes whose step needs more (pq_attn_workspace_bytes
+ * above 8 MiB, or B * n_kv_heads above 65,536) return PQ_ERR_WORKSPACE
+ * with nothing launched.  The call allocates nothing; its first call on a
+ * device also enqueues one small kernel that zeroes the counters.  Every
+ * call on one GPU shares that GPU's array (each call leaves the counters at
+ * zero, the records are rewritten by every call), so calls that overlap in
+ * time on one GPU race: serialise them (one stream, or events). */
+pq_status pq_attn_decode_step_noalloc(const pq_attn_desc* desc, const void* q, const void* k_new,
+                                      const void* v_new, uint8_t* k_codes, uint8_t* v_codes,
+                                      const void* k_cb, const void* v_cb, const int32_t* lens,
+                                      float* out, void* stream);
+
 /* ---- FP8 codebooks ------------------------------------------------------
  * The AQPIM page, section 4.2, stores the codebooks as a low-precision float
  * such as FP8.  These calls take K and V codebooks (and the encode's

@@ -416,3 +416,17 @@ def test_bench_library_exports_the_stream_reference():
     assert lib.pqbench_stream_read(FAKE + 8, 16, FAKE, 1, 64, None) == 1
     assert lib.pqbench_stream_read(FAKE, 16, FAKE, 1, 100, None) == 1
     assert lib.pqbench_stream_read(FAKE, 16, FAKE, 0, 64, None) == 1
+
+
+def test_noalloc_step_rejects_what_its_scratch_cannot_hold(lib):
+    """Shapes whose chunk records exceed the built-in 8 MiB (or whose
+    counters exceed 65,536) are refused with PQ_ERR_WORKSPACE before any
+    device call; null pointers with PQ_ERR_NULL."""
+    big = _desc(batch=64, n_q_heads=64, n_kv_heads=8, max_len=131072, chunk=1024)
+    assert lib.pq_attn_workspace_bytes(ctypes.byref(big)) > 8 << 20
+    assert lib.pq_attn_decode_step_noalloc(ctypes.byref(big), *([FAKE] * 9), None) == 4
+    ptrs = [FAKE] * 9
+    ptrs[0] = None
+    assert lib.pq_attn_decode_step_noalloc(ctypes.byref(_desc()), *ptrs, None) == 1
+    bad = _desc(batch=0)
+    assert lib.pq_attn_decode_step_noalloc(ctypes.byref(bad), *([FAKE] * 9), None) == 2
