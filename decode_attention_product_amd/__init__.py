@@ -312,12 +312,32 @@ def pq_attn_step_workspace_bytes(desc: PQAttnDesc) -> int:
     return int(load_library().pq_attn_step_workspace_bytes(ctypes.byref(desc)))
 
 
+def _desc_key(desc: PQAttnDesc):
+    return (desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim, desc.n_sub, desc.n_codes,
+            desc.max_len, pq_attn_num_chunks(desc))
+
+
 def step_workspace(desc: PQAttnDesc, device):
     """A zero-filled workspace for pq_attn_decode_step (None when it needs
-    none).  Keep it for later steps: each call leaves it ready."""
+    none).  Keep it for later steps with the same descriptor: each call
+    leaves it ready.  It is tied to that descriptor (the arrival counters'
+    offset depends on the shape), and the step functions here refuse it
+    for another."""
     import torch
     n = pq_attn_step_workspace_bytes(desc)
-    return None if n == 0 else torch.zeros(n, dtype=torch.uint8, device=device)
+    if n == 0:
+        return None
+    ws = torch.zeros(n, dtype=torch.uint8, device=device)
+    ws._pq_step_key = _desc_key(desc)
+    return ws
+
+
+def _check_step_workspace(desc, workspace, where):
+    key = getattr(workspace, "_pq_step_key", None)
+    if key is not None and key != _desc_key(desc):
+        raise ValueError(f"{where}: this step workspace was made for another descriptor "
+                         f"{key}; its arrival counters would sit elsewhere -- use "
+                         "step_workspace(desc) for this one")
 
 
 def pq_attn_decode_step(q, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, out=None, *,
@@ -342,6 +362,7 @@ def pq_attn_decode_step(q, k_new, v_new, k_codes, v_codes, k_cb, v_cb, lens, out
     _need(out, "out", torch.float32, (desc.batch, desc.n_q_heads, desc.head_dim))
     if workspace is None:
         workspace = step_workspace(desc, q.device)
+    _check_step_workspace(desc, workspace, "pq_attn_decode_step")
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = load_library()
     args = (ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_codes), _ptr(v_codes),
@@ -470,6 +491,7 @@ def pq_attn_decode_step_paged(q, k_new, v_new, k_pool, v_pool, k_cb, v_cb, block
     _need(out, "out", torch.float32, (desc.batch, desc.n_q_heads, desc.head_dim))
     if workspace is None:
         workspace = step_workspace(desc, q.device)
+    _check_step_workspace(desc, workspace, "pq_attn_decode_step_paged")
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = load_library()
     args = (ctypes.byref(desc), ctypes.byref(table), _ptr(q), _ptr(k_new), _ptr(v_new),

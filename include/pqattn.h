@@ -144,10 +144,17 @@ size_t pq_attn_step_workspace_bytes(const pq_attn_desc* desc);
  *  workspace         at least pq_attn_step_workspace_bytes(); may be NULL
  *                    when that is 0.  When it is not 0 the buffer must be
  *                    zero-filled before its first use (e.g. hipMemsetAsync);
- *                    every call leaves it ready for the next one (its
- *                    counters back at zero), and a call that returns a
- *                    non-zero status does not touch it.  Two calls that may
- *                    run at the same time need their own workspaces.
+ *                    every call leaves it ready for the next call with
+ *                    the SAME descriptor (its counters back at zero), and
+ *                    a call that returns a non-zero status does not touch
+ *                    it.  A step workspace is tied to one descriptor: the
+ *                    counters sit after the chunk records, at an offset
+ *                    that depends on B, Hq and C, so a step of another
+ *                    shape would read old record bytes as counters and
+ *                    never merge.  Zero it again (or take a fresh one)
+ *                    before using it with another descriptor.  Two calls
+ *                    that may run at the same time need their own
+ *                    workspaces.
  * Other arguments as for pq_attn_decode.  The workgroup whose chunk holds
  * the new token encodes it; with C > 1 the last workgroup of each (b, KV
  * head) to finish merges the chunk records into out.  Exception: with one

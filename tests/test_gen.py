@@ -63,3 +63,22 @@ def test_noisy_codewords_recipe():
             for m in range(4):
                 d = x[n, h, m * 32:(m + 1) * 32].astype(np.float64) - cb[h, m, src[n, h, m]]
                 assert abs(d.std() - 0.05) < 0.03
+
+
+def test_step_workspace_is_tied_to_its_descriptor():
+    """The binding refuses a step workspace made for another shape (its
+    arrival counters sit at a shape-dependent offset): host-side check, no
+    GPU call."""
+    import pytest
+    torch = pytest.importorskip("torch")
+    import decode_attention_product_amd as pq
+    import os
+    if not os.path.exists(pq.LIB_PATH):
+        pytest.skip("library not built")
+    a = pq.PQAttnDesc(2, 16, 2, 128, 8, 256, 4096, 1024, 0.0883883)
+    b = pq.PQAttnDesc(4, 16, 2, 128, 8, 256, 4096, 1024, 0.0883883)
+    ws = torch.zeros(pq.pq_attn_step_workspace_bytes(a), dtype=torch.uint8)
+    ws._pq_step_key = pq._desc_key(a)
+    pq._check_step_workspace(a, ws, "same shape")          # accepted
+    with pytest.raises(ValueError):
+        pq._check_step_workspace(b, ws, "other shape")

@@ -604,3 +604,30 @@ def test_step_codes_equal_pq_encode_on_unstructured_vectors():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(kc[:, :, L - 1], ek.cpu().numpy())
         np.testing.assert_array_equal(vc[:, :, L - 1], ev.cpu().numpy())
+
+
+def test_step_shape_changes_between_steps():
+    """Steps of two shapes interleaved, each with the workspace made for its
+    descriptor (the binding refuses the other's): every step matches the
+    oracle and leaves its counters at zero."""
+    say("steps of two shapes, interleaved, one workspace each")
+    cases = []
+    for seed, B, L, lens in ((3800, 2, 2048, [2048, 1500]), (3801, 4, 4096, [4096, 1, 3000, 2049])):
+        _, inp = gen.random_case(seed, batch=B, n_q_heads=16, n_kv_heads=2, max_len=L, n_sub=8,
+                                 lens=lens)
+        q, kcb = dev(inp["q"]), dev(inp["k_cb"])
+        desc = pq.attn_desc(q, dev(inp["k_codes"]), kcb, chunk=512)
+        cases.append((inp, np.asarray(lens, np.int32), desc, pq.step_workspace(desc, q.device)))
+    with pytest.raises(ValueError):
+        inp, lens, desc, _ = cases[0]
+        run_step(inp, *gen.step_tokens(np.random.default_rng(1), inp["k_cb"], inp["v_cb"],
+                                       len(lens))[::2], lens, chunk=512, ws=cases[1][3])
+    for rnd in range(2):
+        for i, (inp, lens, desc, ws) in enumerate(cases):
+            xk, _, xv, _ = gen.step_tokens(np.random.default_rng(3900 + 10 * rnd + i), inp["k_cb"],
+                                           inp["v_cb"], len(lens))
+            d, _, kc, vc, out = run_step(inp, xk, xv, lens, chunk=512, ws=ws)
+            exp_k, exp_v, ref = step_expected(inp, xk, xv, lens)
+            np.testing.assert_array_equal(kc, exp_k)
+            assert_attn_close(out, ref, f"shape {i} round {rnd}")
+            check_counters_zero(d, ws)
