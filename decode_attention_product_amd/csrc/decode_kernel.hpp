@@ -340,17 +340,25 @@ __device__ __forceinline__ float merge_chunks(const float* pm, const float* pl, 
 // Arrival count for one (request, KV head), called by every thread of a
 // workgroup after its chunk records have been stored with rec_store<true>;
 // C is the number of workgroups that arrive (one per CPW chunks).
-// Every wave first waits until its own stores have completed (vmcnt = 0:
-// acknowledged at the device-coherent level), then thread 0 adds 1 to the
-// counter with a device-scope atomic.  So when a workgroup's add returns
-// C - 1, the C records are complete, and that workgroup -- the only one told
-// so -- reads them with rec_load<true>.
+// Memory model: the records are relaxed agent-scope atomic stores; the
+// workgroup barrier orders every thread's stores before thread 0's arrival,
+// an agent-scope release fetch-add, which makes the workgroup's records
+// visible at agent scope before the count can be seen.  The workgroup whose
+// add returns C - 1 (the last to arrive) then issues an agent-scope acquire
+// fence: it synchronises with the release of every earlier arrival (each
+// add reads the value the previous one wrote), so -- after the second
+// barrier -- that workgroup's relaxed agent-scope loads (rec_load<true>)
+// see all C records.  Only the merging workgroup pays for the acquire.
+// Each wave also waits for its own stores (vmcnt = 0) before the barrier.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, int C, uint32_t* flag) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0)
-    *flag = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                    uint32_t(C - 1) ? 1u : 0u;
+  if (threadIdx.x == 0) {
+    const bool last =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == uint32_t(C - 1);
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *flag = last ? 1u : 0u;
+  }
   __syncthreads();
   return *flag != 0;
 }
