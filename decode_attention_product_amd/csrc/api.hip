@@ -17,7 +17,8 @@
 namespace pqattn {
 namespace {
 
-static_assert(kMaxChunk == 4 * kDecodeThreads, "a chunk is at most 4 token slots per thread");
+static_assert(kMaxChunk == 4 * kDecodeThreads && kMaxChunkSmall == 8 * kDecodeThreads,
+              "a chunk is at most 4 token slots per thread (8 with one or two query heads)");
 
 constexpr int kReduceThreads = 128;
 constexpr int kEncodeVectors = 256;   // vectors per encode workgroup (one wave per segment)
@@ -62,6 +63,9 @@ DecodeFn pick_nt(int T, int cpw) {
   if (T <= kDecodeThreads) return kernel_for<G, M, 1, STEP, PAGED>();
   if (T <= 2 * kDecodeThreads) return kernel_for<G, M, 2, STEP, PAGED>();
   if (T <= 4 * kDecodeThreads) return kernel_for<G, M, 4, STEP, PAGED>();
+  if constexpr (G <= 2) {
+    if (T <= 8 * kDecodeThreads) return kernel_for<G, M, 8, STEP, PAGED>();
+  }
   return nullptr;
 }
 
@@ -80,7 +84,7 @@ DecodeFn pick_gm(int G, int M, int T, int cpw) {
   return nullptr;
 }
 
-// The kernel instance for (G, M), the chunk length T (T <= kMaxChunk), the
+// The kernel instance for (G, M) (query heads per workgroup), the chunk length T, the
 // chunks per workgroup, the plain or decode-step variant and the dense or
 // paged cache.
 DecodeFn pick_decode(int G, int M, int T, int cpw, bool step, bool paged) {
@@ -196,6 +200,7 @@ pq_status launch_score(const AttnPlan& p, const ScoreIO& io, hipStream_t stream,
   a.Lmax = p.Lmax;
   a.T = p.T;
   a.C = p.C;
+  a.hs = p.HS;
   a.qscale = p.scale * kLog2e;
   if (pages != nullptr) {
     a.block_table = pages->block_table;
@@ -212,10 +217,10 @@ pq_status launch_score(const AttnPlan& p, const ScoreIO& io, hipStream_t stream,
                   dim3(kDecodeThreads), &a, stream, start, stop);
   }
   const int cpw = p.CPW;   // the chunk records are the same either way
-  DecodeFn fn = pick_decode(p.G, p.M, p.T, cpw, step, pages != nullptr);
+  DecodeFn fn = pick_decode(p.GW, p.M, p.T, cpw, step, pages != nullptr);
   if (!fn) return PQ_ERR_UNSUPPORTED;
   return launch(reinterpret_cast<const void*>(fn),
-                dim3(unsigned(p.Hkv), unsigned((p.C + cpw - 1) / cpw), unsigned(p.B)),
+                dim3(unsigned(p.Hkv * p.HS), unsigned((p.C + cpw - 1) / cpw), unsigned(p.B)),
                 dim3(kDecodeThreads), &a, stream, start, stop);
 }
 
@@ -744,7 +749,7 @@ pq_status pq_attn_decode_step_noalloc(const pq_attn_desc* desc, const void* q, c
   pq_status st = check_step(desc, nullptr, false, q, k_new, v_new, k_codes, v_codes, k_cb, v_cb,
                             lens, out, &p, &pg);
   if (st != PQ_OK) return st;
-  if (size_t(p.B) * size_t(p.Hkv) > kNoAllocCounters || p.ws_bytes > kNoAllocRecordBytes)
+  if (size_t(p.B) * size_t(p.Hkv) * size_t(p.HS) > kNoAllocCounters || p.ws_bytes > kNoAllocRecordBytes)
     return PQ_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = nullptr;

@@ -25,6 +25,9 @@ DecodeFn pick_nt_f8(int T) {
   if (T <= kDecodeThreads) return &decode_partials_kernel<G, M, 1, false, 1, kF8>;
   if (T <= 2 * kDecodeThreads) return &decode_partials_kernel<G, M, 2, false, 1, kF8>;
   if (T <= 4 * kDecodeThreads) return &decode_partials_kernel<G, M, 4, false, 1, kF8>;
+  if constexpr (G <= 2) {
+    if (T <= 8 * kDecodeThreads) return &decode_partials_kernel<G, M, 8, false, 1, kF8>;
+  }
   return nullptr;
 }
 
@@ -49,8 +52,9 @@ pq_status launch_f8(const void* fn, dim3 grid, dim3 block, void* arg, hipStream_
 
 // The checked plan of an FP8-codebook call: the per-request score kernel
 // with one chunk per workgroup (the request-batched kernel and two-chunk
-// workgroups are built for fp16 codebooks only); the chunking, and so the
-// workspace size, are those of the fp16 call with the same descriptor.
+// workgroups are built for fp16 codebooks only); the chunking and the head
+// split, and so the workspace size, are those of the fp16 call with the
+// same descriptor.
 pq_status plan_f8(const pq_attn_desc* desc, const void* q, const uint8_t* kc, const uint8_t* vc,
                   const uint8_t* kcb, const uint8_t* vcb, const int32_t* lens, AttnPlan* p) {
   pq_status st = plan_attn(desc, p);
@@ -66,7 +70,7 @@ pq_status plan_f8(const pq_attn_desc* desc, const void* q, const uint8_t* kc, co
 pq_status launch_score_f8(const AttnPlan& p, const void* q, const uint8_t* kc, const uint8_t* vc,
                           const uint8_t* kcb, const uint8_t* vcb, const int32_t* lens, float* pm,
                           float* pl, float* po, float* out, hipStream_t stream) {
-  DecodeFn fn = pick_decode_f8(p.G, p.M, p.T);
+  DecodeFn fn = pick_decode_f8(p.GW, p.M, p.T);
   if (!fn) return PQ_ERR_UNSUPPORTED;
   DecodeArgs a{};
   a.q = static_cast<const __half*>(q);
@@ -85,8 +89,9 @@ pq_status launch_score_f8(const AttnPlan& p, const void* q, const uint8_t* kc, c
   a.Lmax = p.Lmax;
   a.T = p.T;
   a.C = p.C;
+  a.hs = p.HS;
   a.qscale = p.scale * kLog2e;
-  return launch_f8(reinterpret_cast<const void*>(fn), dim3(unsigned(p.Hkv), unsigned(p.C), unsigned(p.B)),
+  return launch_f8(reinterpret_cast<const void*>(fn), dim3(unsigned(p.Hkv * p.HS), unsigned(p.C), unsigned(p.B)),
                    dim3(kDecodeThreads), &a, stream);
 }
 

@@ -109,6 +109,9 @@ struct DecodeArgs {
   uint32_t* counters;        // [B*Hkv] chunk arrivals (step kernel with C > 1):
                              // zero on entry, zero again on exit
   int32_t B, Hq, Hkv, Lmax, T, C;
+  int32_t hs;                // head split: workgroups sharing one (b, KV head, chunk),
+                             // each taking G of its Hq / Hkv query heads (grid x
+                             // = hs * Hkv; counters [B*Hkv*hs])
   float qscale;              // scale * log2(e)
   // Paged cache only: k_codes and v_codes are pools [Hkv][n_pages][P][M] and
   // token t of request b lives at slot block_table[b][t >> page_shift] * P +
@@ -363,6 +366,17 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, int C, uint32_t* 
   return *flag != 0;
 }
 
+// Raw buffer resources (gfx9 descriptor word 3: raw dword access) let loads
+// be issued by every lane without a branch: a lane whose byte offset lies
+// past num_records gets 0 and makes no memory access.  Branch-free loads
+// also let the compiler count outstanding loads exactly, so a wait for an
+// early load (a codebook operand) does not wait for later ones (the codes).
+constexpr int kRsrcRaw = 0x00020000;
+constexpr uint32_t kOffNone = 0x80000000u;   // an offset past any buffer used here
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), kRsrcRaw);
+}
+
 // Code bytes of one token: M = 4 -> one dword, M = 8 -> two dwords.
 template <int M> struct TokenCodes;
 template <> struct TokenCodes<4> {
@@ -372,6 +386,10 @@ template <> struct TokenCodes<4> {
   }
   __device__ __forceinline__ void store(uint8_t* p) const { *reinterpret_cast<uint32_t*>(p) = w; }
   __device__ __forceinline__ void load(const uint8_t* p) { w = *reinterpret_cast<const uint32_t*>(p); }
+  // from a raw buffer (byte offset; out of range reads 0 and touches no memory)
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    w = uint32_t(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
   __device__ __forceinline__ int get(int m) const { return (w >> (8 * m)) & 0xff; }
   // the codes with byte j holding segment (j + r) % 4
   __device__ __forceinline__ TokenCodes rotated(int r) const {
@@ -388,6 +406,11 @@ template <> struct TokenCodes<8> {
   }
   __device__ __forceinline__ void store(uint8_t* p) const { *reinterpret_cast<uint2*>(p) = w; }
   __device__ __forceinline__ void load(const uint8_t* p) { w = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w = make_uint2(v[0], v[1]);
+  }
   __device__ __forceinline__ int get(int m) const {
     return ((m < 4 ? w.x : w.y) >> (8 * (m & 3))) & 0xff;
   }
@@ -539,7 +562,7 @@ __device__ __forceinline__ MergeState merge_states(const MergeState& x, const Me
 // all of them for C <= 8): served from the device-coherent level, so they
 // see the records the other workgroups completed before their arrival.
 template <int G>
-__device__ __forceinline__ void merge_rows(const DecodeArgs& a, int64_t row0, int64_t bg, float* scratch) {
+__device__ __forceinline__ void merge_rows(const DecodeArgs& a, int64_t row0, int64_t cnt, float* scratch) {
   constexpr int D = 128;
   const int C = a.C;
   if (C <= 8) {
@@ -634,7 +657,7 @@ __device__ __forceinline__ void merge_rows(const DecodeArgs& a, int64_t row0, in
     }
   }
   if (threadIdx.x == 0)   // ready for the next call
-    __hip_atomic_store(a.counters + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.counters + cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // G query heads per KV head, M segments, NT token slots per thread, CPW
@@ -695,15 +718,19 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
 
-  // Grid (Hkv, C / CPW, B), dispatched x fastest: consecutive workgroups go to
-  // different XCDs, so with Hkv a multiple of 8 every chunk of one KV head
-  // lands on the same XCD and shares its L2 copy of the codebooks.
-  const int g = blockIdx.x;
+  // Grid (hs * Hkv, C / CPW, B), dispatched x fastest: consecutive workgroups
+  // go to different XCDs, so with Hkv a multiple of 8 every chunk and head
+  // part of one KV head lands on the same XCD and shares its L2 copy of the
+  // codebooks (and, with a head split, of the codes).  Workgroup x takes
+  // KV head g = x % Hkv and query heads hp*G .. hp*G + G-1 of its group,
+  // hp = x / Hkv.
+  const int hp = blockIdx.x / a.Hkv;
+  const int g = blockIdx.x - hp * a.Hkv;
   const int c = blockIdx.y * CPW;             // first chunk of this workgroup
   const int b = blockIdx.z;
   const int t_begin = c * a.T;
   const int n_own = min(CPW, a.C - c);        // chunks this workgroup owns
-  const int64_t row0 = int64_t(b) * a.Hq + int64_t(g) * G;   // first query row
+  const int64_t row0 = int64_t(b) * a.Hq + int64_t(g) * G * a.hs + int64_t(hp) * G;   // first query row
 
   // ---- 0. requests --------------------------------------------------------------
   // What does not depend on lens[b] goes out before its value is waited for:
@@ -729,6 +756,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   // V, so the same instructions score the token against the codewords.
   constexpr int kNewRow = 8;
   const int64_t bg = int64_t(b) * a.Hkv + g;
+  const int64_t cnt = bg * a.hs + hp;         // arrival counter of this head part
   f16x4 qa[KSTEP_Q], xv[KSTEP_Q];
 #pragma unroll
   for (int s = 0; s < KSTEP_Q; ++s) {
@@ -766,8 +794,8 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       }
     }
     if constexpr (STEP) {
-      if (a.part_o != nullptr && arrive_last(a.counters + bg, int(gridDim.y), &arrive_flag))
-        merge_rows<G>(a, row0, bg, lut);
+      if (a.part_o != nullptr && arrive_last(a.counters + cnt, int(gridDim.y), &arrive_flag))
+        merge_rows<G>(a, row0, cnt, lut);
     }
     return;
   }
@@ -792,15 +820,27 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   if constexpr (STEP && PAGED) {
     if (has_new && tid == 0) page_new = a.block_table[int64_t(b) * a.max_pages + (t_new >> a.page_shift)];
   }
-  // the chunk's K and V codes (only tokens below lens[b] are read)
+  // the chunk's K and V codes: raw buffer loads from every lane (no branch);
+  // slots past lens[b] -- and, in the step kernel, the new token's slot,
+  // whose codes it computes and one workgroup writes -- get an offset past
+  // the buffer, so they read nothing.  Dense: the buffer is the chunk's
+  // valid tokens; paged: the KV head's pool (under 2 GiB, checked on the
+  // host).
   TokenCodes<M> kcode[NT], vcode[NT];
+  {
+    const uint8_t* kb = PAGED ? kc : kc + int64_t(t_begin) * M;
+    const uint8_t* vb = PAGED ? vc : vc + int64_t(t_begin) * M;
+    const uint32_t nbytes = PAGED ? uint32_t(a.pool_head_bytes) : uint32_t(t_end - t_begin) * M;
+    const __amdgpu_buffer_rsrc_t kr = raw_buffer(kb, nbytes), vr = raw_buffer(vb, nbytes);
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const int t = t_begin + i * NTHR + tid;
-    if (t < t_end) {
-      const int64_t off = slot(t, PAGED ? page[i] : 0) * M;
-      kcode[i].load(kc + off);
-      vcode[i].load(vc + off);
+    for (int i = 0; i < NT; ++i) {
+      const int t = t_begin + i * NTHR + tid;
+      const bool use = t < t_end && t != t_new;
+      uint32_t off;
+      if constexpr (PAGED) off = use ? uint32_t(slot(t, page[i])) * M : kOffNone;
+      else off = use ? uint32_t(t - t_begin) * M : kOffNone;
+      kcode[i].load(kr, off);
+      vcode[i].load(vr, off);
     }
   }
 
@@ -864,7 +904,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   if constexpr (STEP) {
     if (has_new) {   // the new token's K codes: into the cache and into its slot's registers
       TokenCodes<M> nk = combine_new_codes<M, NW>(new_key[0]);
-      if (tid == 0) nk.store(kc + slot(t_new, page_new) * M);
+      if (tid == 0 && hp == 0) nk.store(kc + slot(t_new, page_new) * M);   // one head part writes
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         if (t_begin + i * NTHR + tid == t_new) kcode[i] = nk;
@@ -993,7 +1033,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   if constexpr (STEP) {
     if (has_new) {   // the new token's V codes (per-wave keys written before the barrier above)
       const TokenCodes<M> nv = combine_new_codes<M, NW>(new_key[1]);
-      if (tid == 0) nv.store(vc + slot(t_new, page_new) * M);
+      if (tid == 0 && hp == 0) nv.store(vc + slot(t_new, page_new) * M);
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         if (t_begin + i * NTHR + tid == t_new) vcode[i] = nv;
@@ -1227,8 +1267,8 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     }
   }
   if constexpr (STEP) {
-    if (a.part_o != nullptr && arrive_last(a.counters + bg, int(gridDim.y), &arrive_flag))
-      merge_rows<G>(a, row0, bg, lut);
+    if (a.part_o != nullptr && arrive_last(a.counters + cnt, int(gridDim.y), &arrive_flag))
+      merge_rows<G>(a, row0, cnt, lut);
   }
 }
 

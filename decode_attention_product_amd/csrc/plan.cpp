@@ -19,6 +19,57 @@ bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
 }  // namespace
 
+// Estimated time (ns) of the per-request score kernel (and its merge) for
+// one split of the work: `blocks` workgroups of `tokens` tokens and GW query
+// heads each, over the 256 CUs in rounds of one workgroup per CU; fitted to
+// in-kernel clock stamps on MI355X (prologue and table build plus
+// contraction ~6 us per workgroup; table gathers and histogram atomics
+// ~0.067 ns per token per LDS instruction; chunk records, arrival and merge
+// ~4.5 us, ~1 us more past 8 chunks; a head split reads each code row
+// HS times through L2: ~2 us for 8192 tokens at M = 8, in proportion).
+double split_cost_ns(int64_t blocks, int64_t tokens, int GW, int M, int C, int HS) {
+  const int64_t rounds = (blocks + kTargetBlocks - 1) / kTargetBlocks;
+  const double lds_per_token = M * 0.067 * ((GW + 3) / 4 + (GW >= 2 ? GW / 2 : 1));
+  double t = double(rounds) * (6000.0 + lds_per_token * double(tokens));
+  if (C > 1) t += C > 8 ? 5500.0 : 4500.0;
+  if (HS > 1) t += double(rounds) * 2000.0 * double(tokens) * M / (8192.0 * 8.0);
+  return t;
+}
+
+void choose_split(int32_t B, int32_t Hkv, int32_t G, int32_t M, int32_t Lmax, int32_t* T_out,
+                  int32_t* HS_out) {
+  double best = 0.0;
+  int32_t bestT = 0, bestHS = 1;
+  const int32_t hs_options[2] = {1, G >= 4 ? G / 2 : 1};
+  for (int32_t hs : hs_options) {
+    if (hs == 1 && bestT != 0 && hs_options[1] == 1) break;
+    const int GW = G / hs;
+    const int32_t tmax = GW <= 2 ? kMaxChunkSmall : kMaxChunk;
+    for (int32_t t = kChunkGranule; t <= 2 * tmax; t *= 2) {
+      const int32_t T = t <= tmax ? (t < Lmax ? t : Lmax) : (Lmax <= tmax ? Lmax : 0);
+      if (T == 0) continue;
+      const int64_t C = (int64_t(Lmax) + T - 1) / T;
+      if (C > kMaxGridYZ) continue;
+      int64_t blocks = int64_t(B) * Hkv * hs * C;
+      int64_t tokens = T;
+      if (hs == 1 && M == 4 && C >= 2 && (T == 1024 || T == 2048) && blocks > kCpwCUs) {
+        blocks = (int64_t(B) * Hkv) * ((C + 1) / 2);   // two chunks per workgroup
+        tokens = 2 * T;
+      }
+      const double c = split_cost_ns(blocks, tokens, GW, M, int(C), hs);
+      // ties: fewer chunks, then no head split
+      if (bestT == 0 || c < best - 1.0 ||
+          (c <= best + 1.0 && (C < (int64_t(Lmax) + bestT - 1) / bestT))) {
+        best = c;
+        bestT = T;
+        bestHS = hs;
+      }
+    }
+  }
+  *T_out = bestT;
+  *HS_out = bestHS;
+}
+
 int32_t pick_chunk(int32_t B, int32_t Hkv, int32_t Lmax, int32_t target_blocks, int32_t granule) {
   const int64_t pairs = int64_t(B) * Hkv;
   int64_t want_chunks = (target_blocks + pairs - 1) / pairs;
@@ -55,8 +106,12 @@ pq_status plan_attn(const pq_attn_desc* d, AttnPlan* p) {
   p->DS = d->head_dim / d->n_sub;
   p->K = d->n_codes;
   p->Lmax = d->max_len;
-  p->T = d->chunk > 0 ? (d->chunk < d->max_len ? d->chunk : d->max_len)
-                      : pick_chunk(d->batch, d->n_kv_heads, d->max_len, kTargetBlocks, kChunkGranule);
+  int32_t hs_pick = 1;
+  if (d->chunk > 0) {
+    p->T = d->chunk < d->max_len ? d->chunk : d->max_len;
+  } else {
+    choose_split(d->batch, d->n_kv_heads, G, d->n_sub, d->max_len, &p->T, &hs_pick);
+  }
   // one query head per KV head and many (request, KV head) pairs: the
   // request-batched score kernel, with chunks as long as it takes
   p->R = 1;
@@ -68,13 +123,15 @@ pq_status plan_attn(const pq_attn_desc* d, AttnPlan* p) {
       p->T = tb;
     }
   }
-  if (p->T > kMaxChunk) return PQ_ERR_UNSUPPORTED;
+  p->HS = p->R == 1 ? hs_pick : 1;
+  p->GW = G / p->HS;
+  if (p->T > (p->GW <= 2 ? kMaxChunkSmall : kMaxChunk)) return PQ_ERR_UNSUPPORTED;
   p->C = int32_t((int64_t(p->Lmax) + p->T - 1) / p->T);
   p->scale = d->scale;
   p->rows = int64_t(p->B) * p->Hq;
   p->CPW = (p->R == 1 && p->M == 4 && p->C >= 2 && (p->T == 1024 || p->T == 2048) &&
             int64_t(p->B) * p->Hkv * p->C > kCpwCUs) ? 2 : 1;
-  p->blocks = int64_t(p->B) * p->Hkv * p->C;
+  p->blocks = int64_t(p->B) * p->Hkv * p->HS * p->C;
   if (p->blocks > kMaxBlocks || p->rows > kMaxBlocks) return PQ_ERR_UNSUPPORTED;
   // score-kernel grids (Hkv, C, B) and (Hkv, C, B / R): the y and z extents are 16-bit
   if (p->C > kMaxGridYZ || p->B > kMaxGridYZ) return PQ_ERR_UNSUPPORTED;
@@ -91,13 +148,14 @@ pq_status plan_attn(const pq_attn_desc* d, AttnPlan* p) {
     p->ws_o_off = p->ws_l_off + round_up(n_stat * 4, 256);
     p->ws_bytes = p->ws_o_off + round_up(n_stat * size_t(p->D) * 4, 256);
   }
-  // decode step: the chunk records plus one arrival counter per (b, kv head)
+  // decode step: the chunk records plus one arrival counter per (b, kv head,
+  // head part)
   if (p->C == 1) {
     p->ws_cnt_off = 0;
     p->ws_step_bytes = 0;
   } else {
     p->ws_cnt_off = p->ws_bytes;
-    p->ws_step_bytes = p->ws_cnt_off + round_up(size_t(p->B) * size_t(p->Hkv) * 4, 256);
+    p->ws_step_bytes = p->ws_cnt_off + round_up(size_t(p->B) * size_t(p->Hkv) * p->HS * 4, 256);
   }
   return PQ_OK;
 }
@@ -137,6 +195,8 @@ pq_status plan_pages(const AttnPlan& p, const pq_page_table* t, PagePlan* out) {
   // every pool offset (and Hkv pools side by side) must fit in 62 bits
   const int64_t head_bytes = int64_t(t->n_pages) * P * p.M;
   if (head_bytes > (int64_t(1) << 62) / p.Hkv) return PQ_ERR_SHAPE;
+  // the score kernels address a KV head's pool with 32-bit buffer offsets
+  if (head_bytes >= (int64_t(1) << 31)) return PQ_ERR_UNSUPPORTED;
   out->block_table = t->block_table;
   out->P = P;
   int shift = 0;

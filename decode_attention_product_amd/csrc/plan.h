@@ -13,7 +13,8 @@ namespace pqattn {
 constexpr int kHeadDim = 128;   // D supported by the kernels
 constexpr int kCodes = 256;     // K codewords per segment codebook
 constexpr int kLenAlign = 16;   // cache capacity granularity, tokens
-constexpr int kMaxChunk = 4096; // longest chunk one score workgroup takes
+constexpr int kMaxChunk = 4096; // longest chunk a score workgroup of 4 or 8 query heads takes
+constexpr int kMaxChunkSmall = 8192;  // ... of 1 or 2 query heads (8 token slots per thread)
 // Request batching for one query head per KV head: kMhaRequests requests of
 // a KV head per score workgroup (in passes of kMhaPassRequests) once there
 // are at least kMhaMinPairs (request, KV head) pairs; chunks of up to
@@ -28,6 +29,10 @@ constexpr int kMhaMaxChunkM8 = 2048;
 // each with its own prologue and table build) and two histograms fit in LDS:
 // M = 4 and chunks of exactly 1024 or 2048 tokens.
 constexpr int64_t kCpwCUs = 256;
+// When the library chooses the chunk (desc->chunk == 0) it also chooses
+// whether to split the query heads of a KV head over G / 2 workgroups of
+// two (G >= 4): among chunk lengths of 1024 * 2^k tokens (or the whole
+// cache) and the two head splits, the one split_cost_ns estimates fastest.
 
 // A checked decode-attention shape with the chunking resolved.
 struct AttnPlan {
@@ -36,6 +41,9 @@ struct AttnPlan {
                         // kMhaRequests for the request-batched kernel)
   int32_t CPW;          // chunks per workgroup of the per-request score kernel
                         // (1, or 2: see kCpwCUs)
+  int32_t HS;           // head split: workgroups per (b, KV head, chunk), each with
+                        // GW = G / HS query heads (see kSplitMinBlocks)
+  int32_t GW;
   float scale;
   int64_t rows;         // B * Hq
   int64_t blocks;       // score-kernel workgroups, B * Hkv * C
@@ -51,6 +59,13 @@ pq_status plan_attn(const pq_attn_desc* d, AttnPlan* p);
 // chunks that the score kernel has about `target_blocks` workgroups, each
 // chunk a multiple of `granule` tokens.
 int32_t pick_chunk(int32_t B, int32_t Hkv, int32_t Lmax, int32_t target_blocks, int32_t granule);
+
+// The time model behind the library's choice (ns, see plan.cpp) and the
+// choice itself: chunk length *T and head split *HS for the per-request
+// score kernel.
+double split_cost_ns(int64_t blocks, int64_t tokens, int GW, int M, int C, int HS);
+void choose_split(int32_t B, int32_t Hkv, int32_t G, int32_t M, int32_t Lmax, int32_t* T,
+                  int32_t* HS);
 
 struct EncodePlan {
   int64_t N;

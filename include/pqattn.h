@@ -198,7 +198,9 @@ typedef struct pq_page_table {
   int32_t page_tokens;        /* P: a power of two in [16, 65536]            */
   int32_t max_pages;          /* table row length; the attention descriptor's
                                  max_len must equal max_pages * page_tokens  */
-  int32_t n_pages;            /* pages per KV head in each pool, >= 1        */
+  int32_t n_pages;            /* pages per KV head in each pool, >= 1; one
+                                 KV head's pool, n_pages * P * M bytes, must
+                                 stay under 2 GiB (PQ_ERR_UNSUPPORTED)       */
 } pq_page_table;
 
 /* pq_attn_decode over a paged cache: out[b][h] is exactly what pq_attn_decode

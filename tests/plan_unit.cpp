@@ -31,9 +31,28 @@ int main() {
   pq_attn_desc d = base();
   EXPECT(plan_attn(&d, &p) == PQ_OK);
   EXPECT(p.G == 8 && p.DS == 16 && p.rows == 512);
-  EXPECT(p.blocks == int64_t(p.B) * p.Hkv * p.C);
+  // 64 (request, KV head) pairs and 8192 tokens: the query heads split in
+  // four parts of two, one chunk each
+  EXPECT(p.HS == 4 && p.GW == 2 && p.C == 1 && p.T == 8192 && p.ws_bytes == 0);
+  EXPECT(p.blocks == int64_t(p.B) * p.Hkv * p.HS * p.C);
   EXPECT(p.T * (p.C - 1) < p.Lmax && p.T * p.C >= p.Lmax);
   EXPECT(p.blocks >= 256);
+  {   // few pairs, or a cache longer than one chunk: the token split
+    pq_attn_desc e = base();
+    e.batch = 1;        // 8 pairs: split both, 2 heads x 1024 tokens per workgroup
+    EXPECT(plan_attn(&e, &p) == PQ_OK && p.HS == 4 && p.C == 8 && p.blocks == 256);
+    e = base();
+    e.max_len = 16384;
+    EXPECT(plan_attn(&e, &p) == PQ_OK && p.HS == 1 && p.GW == 8 && p.C > 1);
+    e = base();
+    e.n_q_heads = 32;   // G = 4 and 64 pairs: two parts give only 128 workgroups
+    EXPECT(plan_attn(&e, &p) == PQ_OK && p.HS == 1);
+    e.batch = 16;       // 128 pairs: two parts of two, 256 workgroups
+    EXPECT(plan_attn(&e, &p) == PQ_OK && p.HS == 2 && p.GW == 2 && p.C == 1);
+    e = base();
+    e.batch = 64;       // enough pairs for the token split
+    EXPECT(plan_attn(&e, &p) == PQ_OK && p.HS == 1);
+  }
 
   // explicit chunks
   d.chunk = 2048;
@@ -73,7 +92,7 @@ int main() {
   EXPECT(pick_chunk(1, 1, 16, 512, 256) == 16);
   EXPECT(pick_chunk(1, 1, 1 << 20, 256, 512) == kMaxChunk);
   d = base(); d.chunk = 0;
-  EXPECT(plan_attn(&d, &p) == PQ_OK && p.T <= kMaxChunk && p.T % 512 == 0);
+  EXPECT(plan_attn(&d, &p) == PQ_OK && p.T <= kMaxChunkSmall && p.T % 512 == 0);
 
   // encode
   pq_encode_desc e;
@@ -105,7 +124,9 @@ int main() {
     EXPECT(plan_attn(&md, &mp) == PQ_OK && mp.R == 1);
     md.batch = 64; md.n_q_heads = 64;               // two query heads per KV head
     EXPECT(plan_attn(&md, &mp) == PQ_OK && mp.R == 1);
-    md.n_q_heads = 32; md.max_len = 8192; md.chunk = 8192;   // longer than either kernel's chunk
+    md.n_q_heads = 32; md.max_len = 8192; md.chunk = 8192;   // longer than the batched kernel's
+    EXPECT(plan_attn(&md, &mp) == PQ_OK && mp.R == 1 && mp.T == 8192 && mp.C == 1);
+    md.max_len = 16384; md.chunk = 16384;                    // longer than any kernel's chunk
     EXPECT(plan_attn(&md, &mp) == PQ_ERR_UNSUPPORTED);
   }
 
@@ -153,8 +174,10 @@ int main() {
     EXPECT(plan_pages(pp, &t, &pg) == PQ_ERR_SHAPE);
     t.page_tokens = 256; t.max_pages = 32; t.n_pages = 0;
     EXPECT(plan_pages(pp, &t, &pg) == PQ_ERR_SHAPE);
-    t.n_pages = std::numeric_limits<int32_t>::max();   // 2^31 pages of 2 KB per head still fit
+    t.n_pages = (1 << 20) - 1;                 // a KV head's pool just under 2 GiB
     EXPECT(plan_pages(pp, &t, &pg) == PQ_OK && pg.pool_head_bytes == int64_t(t.n_pages) * 256 * 8);
+    t.n_pages = 1 << 20;                       // 2 GiB: past the kernels' 32-bit offsets
+    EXPECT(plan_pages(pp, &t, &pg) == PQ_ERR_UNSUPPORTED);
     t.block_table = nullptr;
     EXPECT(plan_pages(pp, &t, &pg) == PQ_ERR_NULL);
     EXPECT(plan_pages(pp, nullptr, &pg) == PQ_ERR_NULL);

@@ -119,15 +119,29 @@ def test_chunking_and_workspace_sizes(lib):
     # chunk larger than the cache is clamped to one chunk
     d2 = _desc(max_len=512, chunk=100000)
     assert lib.pq_attn_num_chunks(ctypes.byref(d2)) == 1
-    # the library's pick fills the chip: at least 256 workgroups when possible
+    # the library's pick fills the chip.  The GQA shape has too few (request,
+    # KV head) pairs, so the 8 query heads of a KV head are split over 4
+    # workgroups of two, each over the whole cache: one chunk, no records
     d3 = _desc(batch=8, n_q_heads=64, n_kv_heads=8, n_sub=8, max_len=8192)
-    C3 = lib.pq_attn_num_chunks(ctypes.byref(d3))
-    assert 8 * 8 * C3 >= 256 and 8192 % C3 == 0
+    assert lib.pq_attn_num_chunks(ctypes.byref(d3)) == 1
+    assert lib.pq_attn_workspace_bytes(ctypes.byref(d3)) == 0
+    assert lib.pq_attn_step_workspace_bytes(ctypes.byref(d3)) == 0
+    # an explicit chunk keeps the token split
+    d4 = _desc(batch=8, n_q_heads=64, n_kv_heads=8, n_sub=8, max_len=8192, chunk=2048)
+    assert lib.pq_attn_num_chunks(ctypes.byref(d4)) == 4
+    # longer caches than one chunk of 8192 tokens split the tokens: at least
+    # 256 workgroups when possible
+    d5 = _desc(batch=2, n_q_heads=64, n_kv_heads=8, n_sub=8, max_len=16384)
+    C5 = lib.pq_attn_num_chunks(ctypes.byref(d5))
+    assert 2 * 8 * C5 >= 256 and 16384 % C5 == 0
+    # so do few pairs (the split would leave most CUs idle)
+    d6 = _desc(batch=1, n_q_heads=64, n_kv_heads=8, n_sub=8, max_len=8192)
+    assert lib.pq_attn_num_chunks(ctypes.byref(d6)) > 1
 
 
 def test_step_workspace_sizes(lib):
     # records of pq_attn_workspace_bytes plus one 32-bit counter per (b, kv head)
-    d = _desc(batch=8, n_q_heads=64, n_kv_heads=8, n_sub=8, max_len=8192)
+    d = _desc(batch=8, n_q_heads=64, n_kv_heads=8, n_sub=8, max_len=8192, chunk=2048)
     rec = lib.pq_attn_workspace_bytes(ctypes.byref(d))
     step = lib.pq_attn_step_workspace_bytes(ctypes.byref(d))
     assert rec > 0 and step >= rec + 8 * 8 * 4 and step <= rec + 8 * 8 * 4 + 256

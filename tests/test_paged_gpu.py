@@ -203,18 +203,20 @@ def test_paged_step(G, M, P, Lmax, chunk, lens):
         assert (ws[rec:rec + desc.batch * desc.n_kv_heads * 4] == 0).all()
 
 
-def test_paged_step_gqa_workload():
+@pytest.mark.parametrize("chunk", [0, 2048])
+def test_paged_step_gqa_workload(chunk):
     """The benchmarked step shape (B=8, Hq=64, Hkv=8, L=8192, M=8) on 256-token
-    pages: codes and output as the oracle's, output equal to the dense step's."""
+    pages: codes and output as the oracle's, output equal to the dense step's
+    (the library's head split, and four merged chunks)."""
     P = 256
-    say(f"paged step on the gqa workload, pages of {P}")
+    say(f"paged step on the gqa workload, pages of {P}, chunk {chunk or 'library'}")
     inp = gen.workload_inputs(3, with_encode=False)
     lens = inp["lens"]
     kp, vp, table, _ = gen.paged_cache(np.random.default_rng(3256), inp["k_codes"],
                                        inp["v_codes"], lens, P)
     xk, sk, xv, sv = gen.step_tokens(np.random.default_rng(3001), inp["k_cb"], inp["v_cb"], 8)
-    desc, ws, kp_g, vp_g, out = run_step_paged(inp, kp, vp, table, lens, P, xk, xv)
-    assert pq.pq_attn_num_chunks(desc) > 1
+    desc, ws, kp_g, vp_g, out = run_step_paged(inp, kp, vp, table, lens, P, xk, xv, chunk=chunk)
+    assert pq.pq_attn_num_chunks(desc) == (1 if chunk == 0 else 4)
     exp_k, exp_v, ref = step_paged_expected(inp, kp, vp, table, lens, P, xk, xv)
     np.testing.assert_array_equal(kp_g, exp_k)
     np.testing.assert_array_equal(vp_g, exp_v)
@@ -222,7 +224,7 @@ def test_paged_step_gqa_workload():
     # the dense step on the same logical cache
     q, kcb, vcb = dev(inp["q"]), dev(inp["k_cb"]), dev(inp["v_cb"])
     kc, vc = dev(inp["k_codes"]), dev(inp["v_codes"])
-    dense = pq.pq_attn_decode_step(q, dev(xk), dev(xv), kc, vc, kcb, vcb, dev(lens))
+    dense = pq.pq_attn_decode_step(q, dev(xk), dev(xv), kc, vc, kcb, vcb, dev(lens), chunk=chunk)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out, dense.cpu().numpy())
 

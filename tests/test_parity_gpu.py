@@ -412,23 +412,77 @@ def check_counters_zero(desc, ws):
     if ws is None:
         return
     rec = pq.pq_attn_workspace_bytes(desc)
-    n = desc.batch * desc.n_kv_heads * 4
+    n = pq.pq_attn_step_workspace_bytes(desc) - rec     # every counter (and padding)
+    assert n >= desc.batch * desc.n_kv_heads * 4
     assert (ws[rec:rec + n] == 0).all(), "arrival counters not left at zero"
 
 
-def test_step_gqa_workload():
-    say("step on the gqa workload (B=8 Hq=64 Hkv=8 L=8192 M=8, library chunks): encode + attend + merge")
+@pytest.mark.parametrize("chunk", [0, 2048])
+def test_step_gqa_workload(chunk):
+    """The library's choice (the query heads of a KV head split over four
+    workgroups of two, one chunk each: no merge) and the token split into
+    four chunks of 2048 merged in the launch."""
+    say(f"step on the gqa workload (B=8 Hq=64 Hkv=8 L=8192 M=8, chunk {chunk or 'library'})")
     inp = gen.workload_inputs(3, with_encode=False)
     xk, sk, xv, sv = gen.step_tokens(np.random.default_rng(3001), inp["k_cb"], inp["v_cb"], 8)
     lens = inp["lens"]
-    desc, ws, kc, vc, out = run_step(inp, xk, xv, lens)
-    assert pq.pq_attn_num_chunks(desc) > 1
+    desc, ws, kc, vc, out = run_step(inp, xk, xv, lens, chunk=chunk)
+    assert pq.pq_attn_num_chunks(desc) == (1 if chunk == 0 else 4)
     exp_k, exp_v, ref = step_expected(inp, xk, xv, lens)
     np.testing.assert_array_equal(kc, exp_k)
     np.testing.assert_array_equal(vc, exp_v)
     np.testing.assert_array_equal(kc[np.arange(8), :, lens - 1], sk)
     assert_attn_close(out, ref, "gqa step")
     check_counters_zero(desc, ws)
+
+
+HEAD_SPLIT = [
+    # (G, M, B, Hkv, L, lens, C): shapes the library splits by query heads
+    # (G/2 workgroups of two per (request, KV head)), with one chunk or, with
+    # one request, several (records and the in-launch merge per head part)
+    (8, 8, 8, 8, 8192, [8192, 1, 0, 8191, 4096, 1025, 7000, 2], 1),
+    (8, 4, 32, 2, 4096, None, 1),
+    (4, 8, 16, 8, 2048, None, 1),
+    (4, 4, 24, 8, 8192, None, 1),
+    (8, 8, 1, 8, 8192, [8192], 8),
+    (8, 4, 1, 8, 8192, [5001], 8),
+]
+
+
+@pytest.mark.parametrize("G,M,B,Hkv,L,lens,C", HEAD_SPLIT)
+def test_head_split_decode_and_step(G, M, B, Hkv, L, lens, C):
+    rng = np.random.default_rng(3950 + G + M + B)
+    if lens is None:
+        lens = rng.integers(0, L + 1, B)
+        lens[:3] = [L, 1, 0]
+    lens = np.asarray(lens, np.int32)
+    say(f"head split G={G} M={M} B={B} Hkv={Hkv} L={L}")
+    _, inp = gen.random_case(3960 + G * M + B, batch=B, n_q_heads=G * Hkv, n_kv_heads=Hkv,
+                             max_len=L, n_sub=M, lens=lens)
+    t = gpu_inputs(inp)
+    desc = pq.attn_desc(t[0], t[1], t[3])
+    assert pq.pq_attn_num_chunks(desc) == C
+    assert (pq.pq_attn_workspace_bytes(desc) == 0) == (C == 1)
+    out = pq.pq_attn_decode(*t, desc=desc)
+    pm, pl, po = pq.pq_attn_partials(*t, desc=desc)
+    torch.cuda.synchronize()
+    assert_attn_close(out.cpu().numpy(), oracle_out(inp), f"head split decode G={G} M={M}")
+    rm, rl, ro = oracle.chunk_partials(*(inp[k] for k in ("q", "k_codes", "v_codes", "k_cb", "v_cb", "lens")),
+                                       chunk=-(-L // C))
+    empty = np.isneginf(rm)
+    assert (np.isneginf(pm.cpu().numpy()) == empty).all()
+    np.testing.assert_allclose(pm.cpu().numpy()[~empty], rm[~empty], rtol=0, atol=1e-4)
+    np.testing.assert_allclose(pl.cpu().numpy()[~empty], rl[~empty], rtol=2e-4, atol=0)
+    xk, _, xv, _ = gen.step_tokens(np.random.default_rng(3970 + G + M), inp["k_cb"], inp["v_cb"], B)
+    d2, ws, kc, vc, out2 = run_step(inp, xk, xv, lens)
+    exp_k, exp_v, ref = step_expected(inp, xk, xv, lens)
+    np.testing.assert_array_equal(kc, exp_k)
+    np.testing.assert_array_equal(vc, exp_v)
+    assert_attn_close(out2, ref, f"head split step G={G} M={M}")
+    for b, l in enumerate(lens):
+        if l == 0:
+            assert (out2[b] == 0).all()
+    check_counters_zero(d2, ws)
 
 
 def test_step_long_context_workload():
