@@ -28,7 +28,8 @@ EXPORTED = ("pq_attn_num_chunks", "pq_attn_workspace_bytes", "pq_attn_decode",
             "pq_attn_decode_step_paged", "pq_attn_decode_step_paged_timed", "pq_attn_reduce",
             "pq_encode", "pq_encode_many", "pq_codebook_update", "pq_kmeans",
             "pq_kmeans_many", "pq_attn_decode_fp8cb", "pq_attn_partials_fp8cb",
-            "pq_encode_fp8cb", "pq_attn_decode_step_noalloc", "pq_status_string")
+            "pq_encode_fp8cb", "pq_attn_decode_step_noalloc", "pq_attn_reduce_polyexp",
+            "pq_status_string")
 
 
 class PQError(RuntimeError):
@@ -107,6 +108,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pq_attn_decode_step_paged_timed.restype = ctypes.c_int
     lib.pq_attn_reduce.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
     lib.pq_attn_reduce.restype = ctypes.c_int
+    lib.pq_attn_reduce_polyexp.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P,
+                                           P, P]
+    lib.pq_attn_reduce_polyexp.restype = ctypes.c_int
     lib.pq_encode.argtypes = [ctypes.POINTER(PQEncodeDesc), P, P, P, P, P]
     lib.pq_encode.restype = ctypes.c_int
     lib.pq_encode_many.argtypes = [ctypes.POINTER(PQEncodeDesc), ctypes.c_int32,
@@ -505,9 +509,10 @@ def pq_attn_decode_step_paged(q, k_new, v_new, k_pool, v_pool, k_cb, v_cb, block
     return out
 
 
-def pq_attn_reduce(part_m, part_l, part_o, out=None, *, stream=None):
-    """Merge chunk statistics (C entry point pq_attn_reduce).  part_m and
-    part_l [..., C], part_o [..., C, D]; returns out [..., D] fp32."""
+def pq_attn_reduce(part_m, part_l, part_o, out=None, *, stream=None, polyexp=False):
+    """Merge chunk statistics (C entry point pq_attn_reduce, or
+    pq_attn_reduce_polyexp with ``polyexp``).  part_m and part_l [..., C],
+    part_o [..., C, D]; returns out [..., D] fp32."""
     import torch
     C, D = part_o.shape[-2], part_o.shape[-1]
     lead = tuple(part_o.shape[:-2])
@@ -520,9 +525,9 @@ def pq_attn_reduce(part_m, part_l, part_o, out=None, *, stream=None):
     if out is None:
         out = torch.empty((*lead, D), dtype=torch.float32, device=part_o.device)
     _need(out, "out", torch.float32, (*lead, D))
-    st = load_library().pq_attn_reduce(rows, C, D, _ptr(part_m), _ptr(part_l), _ptr(part_o),
-                                       _ptr(out), _stream(stream))
-    _check(st, "pq_attn_reduce")
+    fn = load_library().pq_attn_reduce_polyexp if polyexp else load_library().pq_attn_reduce
+    st = fn(rows, C, D, _ptr(part_m), _ptr(part_l), _ptr(part_o), _ptr(out), _stream(stream))
+    _check(st, "pq_attn_reduce_polyexp" if polyexp else "pq_attn_reduce")
     return out
 
 

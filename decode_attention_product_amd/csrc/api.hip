@@ -262,10 +262,12 @@ pq_status launch_step_encode(const AttnPlan& p, const PagePlan* pages, const voi
 }
 
 pq_status launch_reduce(int64_t rows, int32_t C, const float* pm, const float* pl, const float* po,
-                        float* out, hipStream_t stream, hipEvent_t stop = nullptr) {
+                        float* out, hipStream_t stream, hipEvent_t stop = nullptr, bool poly = false) {
   if (rows == 0) return PQ_OK;
   ReduceArgs a{pm, pl, po, out, C};
-  return launch(reinterpret_cast<const void*>(&reduce_kernel<kHeadDim>), dim3(unsigned(rows)),
+  const void* fn = poly ? reinterpret_cast<const void*>(&reduce_kernel<kHeadDim, true>)
+                        : reinterpret_cast<const void*>(&reduce_kernel<kHeadDim, false>);
+  return launch(fn, dim3(unsigned(rows)),
                 dim3(kReduceThreads), &a, stream, nullptr, stop);
 }
 
@@ -514,6 +516,16 @@ pq_status pq_attn_reduce(int64_t n_rows, int32_t n_chunks, int32_t head_dim, con
   if (!part_m || !part_l || !part_o || !out) return PQ_ERR_NULL;
   return launch_reduce(n_rows, n_chunks, part_m, part_l, part_o, out,
                        static_cast<hipStream_t>(stream));
+}
+
+pq_status pq_attn_reduce_polyexp(int64_t n_rows, int32_t n_chunks, int32_t head_dim,
+                                 const float* part_m, const float* part_l, const float* part_o,
+                                 float* out, void* stream) {
+  pq_status st = check_reduce(n_rows, n_chunks, head_dim);
+  if (st != PQ_OK) return st;
+  if (!part_m || !part_l || !part_o || !out) return PQ_ERR_NULL;
+  return launch_reduce(n_rows, n_chunks, part_m, part_l, part_o, out,
+                       static_cast<hipStream_t>(stream), nullptr, true);
 }
 
 }  // extern "C"

@@ -125,6 +125,35 @@ struct DecodeArgs {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^x by the reduction unit's method of the PAM page, section 3.2.2 (1): a
+// 6th-order polynomial in place of an exponential unit.  x = n + f with
+// n = floor(x), f in [0, 1); 2^f from a degree-6 minimax polynomial (Horner,
+// fp32; coefficients from exp2_poly_fit.py, Remez exchange on relative
+// error: 8.4e-8 at most in fp32), then 2^n through the exponent field.
+// x below -126 (a merge weight under 2^-126) gives 0; -inf gives 0.
+__device__ __forceinline__ float poly_exp2(float x) {
+  constexpr float c0 = 1.000000000e+00f, c1 = 6.931470037e-01f, c2 = 2.402298301e-01f,
+                  c3 = 5.548334122e-02f, c4 = 9.678840637e-03f, c5 = 1.243968727e-03f,
+                  c6 = 2.170225489e-04f;
+  if (!(x >= -126.0f)) return 0.0f;
+  const float n = __builtin_floorf(x);
+  const float f = x - n;
+  float p = fmaf(c6, f, c5);
+  p = fmaf(p, f, c4);
+  p = fmaf(p, f, c3);
+  p = fmaf(p, f, c2);
+  p = fmaf(p, f, c1);
+  p = fmaf(p, f, c0);
+  return __builtin_ldexpf(p, int(n));
+}
+
+// The merge's exponential: the hardware's, or the polynomial above.
+template <bool POLY>
+__device__ __forceinline__ float merge_exp2(float x) {
+  if constexpr (POLY) return poly_exp2(x);
+  else return fast_exp2(x);
+}
+
 // log2 of a power of two (compile time)
 constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
 
@@ -284,7 +313,7 @@ __device__ __forceinline__ float rec_load(const float* p) {
 // Merge of one output element over C chunk records (m in natural-log units):
 //   sum_c w_c o_c / sum_c w_c l_c,  w_c = exp(m_c - max_c m_c),
 // 0 when every chunk is empty (m = -inf, l = 0).
-template <bool COH = false>
+template <bool COH = false, bool POLY = false>
 __device__ __forceinline__ float merge_chunks(const float* pm, const float* pl, const float* po,
                                               int C, int stride_o) {
   constexpr int kFew = 8;   // up to this many chunks: every record load issued at once
@@ -303,7 +332,7 @@ __device__ __forceinline__ float merge_chunks(const float* pm, const float* pl, 
 #pragma unroll
       for (int c = 0; c < kFew; ++c) {
         if (m[c] == -INFINITY) continue;
-        const float w = fast_exp2((m[c] - m_star) * kLog2e);
+        const float w = merge_exp2<POLY>((m[c] - m_star) * kLog2e);
         num = fmaf(w, o[c], num);
         den = fmaf(w, l[c], den);
       }
@@ -324,13 +353,13 @@ __device__ __forceinline__ float merge_chunks(const float* pm, const float* pl, 
 #pragma unroll
       for (int j = 0; j < kFew; ++j) mb = max_f(mb, m[j]);
       if (mb == -INFINITY) continue;
-      const float r = fast_exp2((m_star - mb) * kLog2e);   // 0 while m_star = -inf
+      const float r = merge_exp2<POLY>((m_star - mb) * kLog2e);   // 0 while m_star = -inf
       num *= r;
       den *= r;
 #pragma unroll
       for (int j = 0; j < kFew; ++j) {
         if (m[j] == -INFINITY) continue;
-        const float w = fast_exp2((m[j] - mb) * kLog2e);
+        const float w = merge_exp2<POLY>((m[j] - mb) * kLog2e);
         num = fmaf(w, o[j], num);
         den = fmaf(w, l[j], den);
       }
@@ -1295,12 +1324,12 @@ struct ReduceArgs {
   int32_t C;
 };
 
-template <int D>
+template <int D, bool POLY = false>
 __global__ __launch_bounds__(D) void reduce_kernel(ReduceArgs a) {
   const int64_t row = blockIdx.x;
   const int d = threadIdx.x;
-  a.out[row * D + d] = merge_chunks(a.part_m + row * a.C, a.part_l + row * a.C,
-                                    a.part_o + row * a.C * D + d, a.C, D);
+  a.out[row * D + d] = merge_chunks<false, POLY>(a.part_m + row * a.C, a.part_l + row * a.C,
+                                                 a.part_o + row * a.C * D + d, a.C, D);
 }
 
 }  // namespace pqattn

@@ -685,3 +685,33 @@ def test_step_shape_changes_between_steps():
             np.testing.assert_array_equal(kc, exp_k)
             assert_attn_close(out, ref, f"shape {i} round {rnd}")
             check_counters_zero(d, ws)
+
+
+def test_reduce_polyexp_matches_oracle_merge():
+    """The merge with the reduction unit's polynomial exponential (PAM page,
+    section 3.2.2 (1)): against the oracle's exact merge, and within ~1e-6
+    of the hardware-exponential merge; empty rows and chunks, and statistics
+    spread over ~100 nats (weights far below 2^-126 count as zero)."""
+    say("reduce with the polynomial exp")
+    rng = np.random.default_rng(19)
+    rows, C, D = 53, 37, 128
+    m = (rng.normal(size=(rows, C)) * 8).astype(np.float32)
+    m[7] = np.linspace(0, -100, C).astype(np.float32)
+    l = rng.uniform(0.5, 3, size=(rows, C)).astype(np.float32)
+    o = rng.normal(size=(rows, C, D)).astype(np.float32)
+    m[3, :] = -np.inf
+    l[3, :] = 0
+    o[3] = 0
+    m[5, 2:] = -np.inf
+    l[5, 2:] = 0
+    o[5, 2:] = 0
+    t = (dev(m), dev(l), dev(o))
+    got = pq.pq_attn_reduce(*t, polyexp=True)
+    hw = pq.pq_attn_reduce(*t)
+    torch.cuda.synchronize()
+    ref = oracle.merge_partials(m, l, o)
+    assert (got[3] == 0).all()
+    assert_attn_close(got.cpu().numpy(), ref, "reduce polyexp vs oracle")
+    d = np.abs(got.cpu().numpy() - hw.cpu().numpy()).max() / np.abs(ref).max()
+    say(f"polyexp vs hardware exp merge: {d:.2e} of max|out|")
+    assert d <= 1e-6
