@@ -810,6 +810,13 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   len = len < 0 ? 0 : (len > a.Lmax ? a.Lmax : len);
   const int t_end = min(t_begin + n_own * a.T, len);
   if (t_begin >= t_end) {   // empty chunks (uniform over the workgroup)
+    // A use of the codebook operands on this path too, so the compiler keeps
+    // their loads ahead of the wait for lens[b] instead of sinking them into
+    // the other branch (which would put one memory latency after the other).
+#pragma unroll
+    for (int i = 0; i < LUT_JOBS; ++i)
+#pragma unroll
+      for (int s = 0; s < KSTEP_Q; ++s) asm volatile("" ::"v"(ckb[i][s]));
     for (int i = tid; i < n_own * G * D; i += NTHR) {
       const int cc = c + i / (G * D), h = (i / D) % G, d = i % D;
       if (a.part_o == nullptr) {
@@ -861,16 +868,20 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     const uint8_t* vb = PAGED ? vc : vc + int64_t(t_begin) * M;
     const uint32_t nbytes = PAGED ? uint32_t(a.pool_head_bytes) : uint32_t(t_end - t_begin) * M;
     const __amdgpu_buffer_rsrc_t kr = raw_buffer(kb, nbytes), vr = raw_buffer(vb, nbytes);
+    uint32_t off[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int t = t_begin + i * NTHR + tid;
       const bool use = t < t_end && t != t_new;
-      uint32_t off;
-      if constexpr (PAGED) off = use ? uint32_t(slot(t, page[i])) * M : kOffNone;
-      else off = use ? uint32_t(t - t_begin) * M : kOffNone;
-      kcode[i].load(kr, off);
-      vcode[i].load(vr, off);
+      if constexpr (PAGED) off[i] = use ? uint32_t(slot(t, page[i])) * M : kOffNone;
+      else off[i] = use ? uint32_t(t - t_begin) * M : kOffNone;
     }
+    // every K code before any V code: loads complete in issue order, so the
+    // scores wait for the K codes only
+#pragma unroll
+    for (int i = 0; i < NT; ++i) kcode[i].load(kr, off[i]);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) vcode[i].load(vr, off[i]);
   }
 
   // the histograms are cleared while the operands are in flight
@@ -940,6 +951,31 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       }
     }
   }
+
+  // V codebook operands of the contraction.  Wave w owns segment m_v and 16
+  // output columns jt*16..+15.  With 32-codeword steps lane (l16, q4) needs
+  // rows 8*q4 .. 8*q4+7 of column l16 of each block: eight 16-bit loads
+  // straight into the halves of the operand registers (the 16 lanes of a row
+  // group read 32 contiguous bytes), so no VALU work puts them in MFMA order.
+  // With one or two heads per workgroup there are registers to hold them
+  // through the gathers, so they are requested here, behind the codes; with
+  // more heads, once the scores are in registers.
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  const int tile = wave % NTILE;
+  const int ksl = wave / NTILE;               // bins [ksl * KSL, (ksl + 1) * KSL)
+  const int m_v = tile % M;
+  const int jt = tile / M;
+  f16x8 cvb[KSL / 32];
+  auto load_cvb = [&]() {
+#pragma unroll
+    for (int st = 0; st < KSL / 32; ++st) {
+      const int64_t src = cb_g + (int64_t(m_v) * K + ksl * KSL + st * 32 + 8 * q4) * DS + jt * 16 + l16;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cvb[st][j] = cb_load1<F>(a.v_cb, src + j * DS);
+    }
+  };
+  constexpr bool kCvbEarly = G <= 2;
+  if constexpr (kCvbEarly) load_cvb();
 
   // step kernel: the V codebook in the table build's B layout, for the new
   // token's V code.  Requested here so its latency overlaps the gathers
@@ -1069,26 +1105,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       }
     }
   }
-  // V codebook operands of the contraction, requested once the scores are
-  // in registers (earlier they would queue ahead of the table operands and
-  // hold registers through the gathers).
-  // Wave w owns segment m_v and 16 output columns jt*16..+15.  With
-  // 32-codeword steps lane (l16, q4) needs rows 8*q4 .. 8*q4+7 of column l16
-  // of each block: eight 16-bit loads straight into the halves of the
-  // operand registers (the 16 lanes of a row group read 32 contiguous
-  // bytes), so no VALU work puts them in MFMA order.
-  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-  const int tile = wave % NTILE;
-  const int ksl = wave / NTILE;               // bins [ksl * KSL, (ksl + 1) * KSL)
-  const int m_v = tile % M;
-  const int jt = tile / M;
-  f16x8 cvb[KSL / 32];
-#pragma unroll
-  for (int st = 0; st < KSL / 32; ++st) {
-    const int64_t src = cb_g + (int64_t(m_v) * K + ksl * KSL + st * 32 + 8 * q4) * DS + jt * 16 + l16;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) cvb[st][j] = cb_load1<F>(a.v_cb, src + j * DS);
-  }
+  if constexpr (!kCvbEarly) load_cvb();
 
   // ---- 4. V histogram (fixed point, integer LDS atomics) -----------------------
   // Lane rotation (G >= 2): at step (jm, jp) a lane updates segment
