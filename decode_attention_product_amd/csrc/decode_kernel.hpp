@@ -856,33 +856,32 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   if constexpr (STEP && PAGED) {
     if (has_new && tid == 0) page_new = a.block_table[int64_t(b) * a.max_pages + (t_new >> a.page_shift)];
   }
-  // the chunk's K and V codes: raw buffer loads from every lane (no branch);
+  // The chunk's K or V codes: raw buffer loads from every lane (no branch);
   // slots past lens[b] -- and, in the step kernel, the new token's slot,
   // whose codes it computes and one workgroup writes -- get an offset past
   // the buffer, so they read nothing.  Dense: the buffer is the chunk's
   // valid tokens; paged: the KV head's pool (under 2 GiB, checked on the
   // host).
-  TokenCodes<M> kcode[NT], vcode[NT];
-  {
-    const uint8_t* kb = PAGED ? kc : kc + int64_t(t_begin) * M;
-    const uint8_t* vb = PAGED ? vc : vc + int64_t(t_begin) * M;
+  auto load_codes = [&](TokenCodes<M> (&dst)[NT], const uint8_t* codes) {
+    const uint8_t* base = PAGED ? codes : codes + int64_t(t_begin) * M;
     const uint32_t nbytes = PAGED ? uint32_t(a.pool_head_bytes) : uint32_t(t_end - t_begin) * M;
-    const __amdgpu_buffer_rsrc_t kr = raw_buffer(kb, nbytes), vr = raw_buffer(vb, nbytes);
-    uint32_t off[NT];
+    const __amdgpu_buffer_rsrc_t r = raw_buffer(base, nbytes);
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int t = t_begin + i * NTHR + tid;
       const bool use = t < t_end && t != t_new;
-      if constexpr (PAGED) off[i] = use ? uint32_t(slot(t, page[i])) * M : kOffNone;
-      else off[i] = use ? uint32_t(t - t_begin) * M : kOffNone;
+      uint32_t off;
+      if constexpr (PAGED) off = use ? uint32_t(slot(t, page[i])) * M : kOffNone;
+      else off = use ? uint32_t(t - t_begin) * M : kOffNone;
+      dst[i].load(r, off);
     }
-    // every K code before any V code: loads complete in issue order, so the
-    // scores wait for the K codes only
-#pragma unroll
-    for (int i = 0; i < NT; ++i) kcode[i].load(kr, off[i]);
-#pragma unroll
-    for (int i = 0; i < NT; ++i) vcode[i].load(vr, off[i]);
-  }
+  };
+  // Only the K codes go out with the K codebook: the V codes are requested
+  // after the table build (the histogram needs them, after the scores), so
+  // the table's operands and the K codes reach the CU with less traffic
+  // queued ahead of them.
+  TokenCodes<M> kcode[NT], vcode[NT];
+  load_codes(kcode, kc);
 
   // the histograms are cleared while the operands are in flight
   for (int i = tid; i < CPW * HIST_WORDS / 4; i += NTHR)
@@ -941,14 +940,14 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   }
   __syncthreads();
 
+  // step kernel: the new token's K codes, into the cache (one head part
+  // writes) and, where its slot's codes are used below, in place of them
+  // (selected there, so nothing here waits for the codes in flight)
+  TokenCodes<M> nk;
   if constexpr (STEP) {
-    if (has_new) {   // the new token's K codes: into the cache and into its slot's registers
-      TokenCodes<M> nk = combine_new_codes<M, NW>(new_key[0]);
-      if (tid == 0 && hp == 0) nk.store(kc + slot(t_new, page_new) * M);   // one head part writes
-#pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        if (t_begin + i * NTHR + tid == t_new) kcode[i] = nk;
-      }
+    if (has_new) {
+      nk = combine_new_codes<M, NW>(new_key[0]);
+      if (tid == 0 && hp == 0) nk.store(kc + slot(t_new, page_new) * M);
     }
   }
 
@@ -958,8 +957,8 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   // straight into the halves of the operand registers (the 16 lanes of a row
   // group read 32 contiguous bytes), so no VALU work puts them in MFMA order.
   // With one or two heads per workgroup there are registers to hold them
-  // through the gathers, so they are requested here, behind the codes; with
-  // more heads, once the scores are in registers.
+  // through the gathers, so they are requested here, behind the V codes;
+  // with more heads, once the scores are in registers.
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   const int tile = wave % NTILE;
   const int ksl = wave / NTILE;               // bins [ksl * KSL, (ksl + 1) * KSL)
@@ -974,6 +973,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       for (int j = 0; j < 8; ++j) cvb[st][j] = cb_load1<F>(a.v_cb, src + j * DS);
     }
   };
+  load_codes(vcode, vc);
   constexpr bool kCvbEarly = G <= 2;
   if constexpr (kCvbEarly) load_cvb();
 
@@ -1002,7 +1002,11 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   for (int i = 0; i < NT; ++i) {
     const int t = t_begin + i * NTHR + tid;
     if (t < t_end) {
-      token_scores<G, M, K>(lut, kcode[i], s[i]);
+      TokenCodes<M> code = kcode[i];
+      if constexpr (STEP) {
+        if (t == t_new) code = nk;
+      }
+      token_scores<G, M, K>(lut, code, s[i]);
     } else {
 #pragma unroll
       for (int h = 0; h < G; ++h) s[i][h] = -INFINITY;
