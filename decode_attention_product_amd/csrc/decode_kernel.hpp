@@ -576,7 +576,7 @@ __device__ __forceinline__ MergeState merge_states(const MergeState& x, const Me
 }
 
 // The last workgroup of (request, KV head) bg: the normalised output of its
-// G query rows from the C chunk records.  Up to 8 chunks, one thread per
+// G query rows from the first nrec of the C record slots of each row.  Up to 8 chunks, one thread per
 // output element with every record load in flight at once.  Beyond that
 // the record loads are the critical path, so they are spread and widened:
 // thread (h, cq, d4) takes four output columns 4*d4.. of head h and the
@@ -591,15 +591,16 @@ __device__ __forceinline__ MergeState merge_states(const MergeState& x, const Me
 // all of them for C <= 8): served from the device-coherent level, so they
 // see the records the other workgroups completed before their arrival.
 template <int G>
-__device__ __forceinline__ void merge_rows(const DecodeArgs& a, int64_t row0, int64_t cnt, float* scratch) {
+__device__ __forceinline__ void merge_rows(const DecodeArgs& a, int64_t row0, int64_t cnt, float* scratch,
+                                           int nrec) {
   constexpr int D = 128;
-  const int C = a.C;
-  if (C <= 8) {
+  const int C = a.C;   // the records' row stride; the first nrec of a row are merged
+  if (nrec <= 8) {
     for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
       const int64_t row = row0 + i / D;
       const int d = i % D;
       a.out[row * D + d] = merge_chunks<true>(a.part_m + row * C, a.part_l + row * C,
-                                              a.part_o + row * C * D + d, C, D);
+                                              a.part_o + row * C * D + d, nrec, D);
     }
   } else {
     static_assert(G * D <= kDecodeThreads, "one thread per (head, chunk class, column quad)");
@@ -615,13 +616,13 @@ __device__ __forceinline__ void merge_rows(const DecodeArgs& a, int64_t row0, in
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           a.part_o + row * C * D, (short)0, C * D * 4, kRsrcWord3);
       constexpr int kB = 8;
-      for (int c0 = cq; c0 < C; c0 += 4 * kB) {
+      for (int c0 = cq; c0 < nrec; c0 += 4 * kB) {
         float m[kB], l[kB];
         f32x4v o[kB];
 #pragma unroll
         for (int j = 0; j < kB; ++j) {
           const int c = c0 + 4 * j;
-          const bool in = c < C;
+          const bool in = c < nrec;
           m[j] = in ? rec_load<true>(a.part_m + row * C + c) : -INFINITY;
           l[j] = in ? rec_load<true>(a.part_l + row * C + c) : 0.0f;
           o[j] = in ? __builtin_amdgcn_raw_buffer_load_b128(rs, (c * D + 4 * d4) * 4, 0, kSc1)
@@ -715,6 +716,10 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   static_assert(NTILE == 8 && KSPLIT == 2, "two contraction waves per output tile");
   static_assert(CPW == 1 || (CPW == 2 && M == 4 && NT % 2 == 0), "two chunks per workgroup need M = 4");
   constexpr int NTC = NT / CPW;               // token slots per thread in one chunk
+  // The step kernel's records are its own (the caller only sees the merged
+  // output): a workgroup of two chunks merges them and writes one record, at
+  // its grid index, which halves the records the last workgroup reads.
+  constexpr bool kWgRecord = STEP && CPW == 2;
 
   // Table and histogram live in separate LDS regions, so the histogram can be
   // cleared while the workgroup still waits for its operands.
@@ -817,8 +822,9 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     for (int i = 0; i < LUT_JOBS; ++i)
 #pragma unroll
       for (int s = 0; s < KSTEP_Q; ++s) asm volatile("" ::"v"(ckb[i][s]));
-    for (int i = tid; i < n_own * G * D; i += NTHR) {
-      const int cc = c + i / (G * D), h = (i / D) % G, d = i % D;
+    const int n_rec = kWgRecord ? 1 : n_own;
+    for (int i = tid; i < n_rec * G * D; i += NTHR) {
+      const int cc = (kWgRecord ? int(blockIdx.y) : c) + i / (G * D), h = (i / D) % G, d = i % D;
       if (a.part_o == nullptr) {
         a.out[(row0 + h) * D + d] = 0.0f;
       } else {
@@ -831,7 +837,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     }
     if constexpr (STEP) {
       if (a.part_o != nullptr && arrive_last(a.counters + cnt, int(gridDim.y), &arrive_flag))
-        merge_rows<G>(a, row0, cnt, lut);
+        merge_rows<G>(a, row0, cnt, lut, kWgRecord ? int(gridDim.y) : a.C);
     }
     return;
   }
@@ -1288,7 +1294,48 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
 
   // ---- 6. write (m, l, o) of each chunk, or the normalised output --------------
   __syncthreads();
-  if (ksl == 0) {
+  if (kWgRecord && ksl == 0) {
+    // both chunks' (m, l, o) merged into the workgroup's record (the max in
+    // log2 units inside the kernel, natural log in the records)
+    const int d = m_v * DS + jt * 16 + l16;
+    f32x4 o[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      o[p] = o_own[p];
+      const float4 other = part_tile[(p * NTILE + tile) * 64 + lane];
+      o[p][0] += other.x; o[p][1] += other.y; o[p][2] += other.z; o[p][3] += other.w;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * q4 + r;
+      if (h < G) {
+        float mp[2], lp[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const bool own = p < n_own;
+          mp[p] = own ? key_float(mkey[p][h]) : -INFINITY;
+          lp[p] = own ? float(lsum[p][h] + lsum[p][G + h]) * pow2i(-fix_shift(lest[p][h])) : 0.0f;
+        }
+        const float mh = max_f(mp[0], mp[1]);
+        float om = 0.0f, lm = 0.0f;
+        if (mh != -INFINITY) {
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const float w = mp[p] == -INFINITY ? 0.0f : fast_exp2(mp[p] - mh);
+            om = fmaf(w, o[p][r], om);
+            lm = fmaf(w, lp[p], lm);
+          }
+        }
+        const int64_t slot = (row0 + h) * a.C + blockIdx.y;
+        rec_store<STEP>(a.part_o + slot * D + d, om);
+        if (d == 0) {
+          rec_store<STEP>(a.part_m + slot, mh * kLn2);
+          rec_store<STEP>(a.part_l + slot, lm);
+        }
+      }
+    }
+  }
+  if (!kWgRecord && ksl == 0) {
     const int d = m_v * DS + jt * 16 + l16;
 #pragma unroll
     for (int p = 0; p < CPW; ++p) {
@@ -1318,7 +1365,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   }
   if constexpr (STEP) {
     if (a.part_o != nullptr && arrive_last(a.counters + cnt, int(gridDim.y), &arrive_flag))
-      merge_rows<G>(a, row0, cnt, lut);
+      merge_rows<G>(a, row0, cnt, lut, kWgRecord ? int(gridDim.y) : a.C);
   }
 }
 
