@@ -711,9 +711,12 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   constexpr int LUT_JOBS = (M * 16) / NW;     // (m, 16-codeword tile) jobs per wave
   constexpr int GP = G >= 2 ? G / 2 : 1;      // 64-bit histogram words per (m, k)
   constexpr int NTILE = M * DS / 16;         // 16-column output tiles of the contraction
-  constexpr int KSPLIT = NW / NTILE;          // waves sharing a tile, each a slice of the bins
+  // waves sharing a tile, each a slice of the bins: with one or two heads a
+  // single wave takes all 256 bins of its tile (8 waves contract, each on
+  // its own, with no cross-wave sum and no barrier before the output)
+  constexpr int KSPLIT = G <= 2 ? 1 : NW / NTILE;
   constexpr int KSL = K / KSPLIT;             // bins per slice
-  static_assert(NTILE == 8 && KSPLIT == 2, "two contraction waves per output tile");
+  static_assert(NTILE == 8 && (KSPLIT == 1 || KSPLIT == 2), "one or two contraction waves per output tile");
   static_assert(CPW == 1 || (CPW == 2 && M == 4 && NT % 2 == 0), "two chunks per workgroup need M = 4");
   constexpr int NTC = NT / CPW;               // token slots per thread in one chunk
   // The step kernel's records are its own (the caller only sees the merged
@@ -968,10 +971,12 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   const int tile = wave % NTILE;
   const int ksl = wave / NTILE;               // bins [ksl * KSL, (ksl + 1) * KSL)
+  const bool cwave = wave < NTILE * KSPLIT;   // this wave takes part in the contraction
   const int m_v = tile % M;
   const int jt = tile / M;
   f16x8 cvb[KSL / 32];
   auto load_cvb = [&]() {
+    if (!cwave) return;
 #pragma unroll
     for (int st = 0; st < KSL / 32; ++st) {
       const int64_t src = cb_g + (int64_t(m_v) * K + ksl * KSL + st * 32 + 8 * q4) * DS + jt * 16 + l16;
@@ -980,7 +985,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     }
   };
   load_codes(vcode, vc);
-  constexpr bool kCvbEarly = G <= 2;
+  constexpr bool kCvbEarly = G <= 2 && KSPLIT == 2;
   if constexpr (kCvbEarly) load_cvb();
 
   // step kernel: the V codebook in the table build's B layout, for the new
@@ -1213,8 +1218,12 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   const int kh = lo_row ? 4 : 0;
   float4* part_tile = reinterpret_cast<float4*>(lut);   // [CPW][NTILE][64]; the table is dead
   f32x4 o_own[CPW];
+  uint32_t lwave[CPW];   // KSPLIT == 1: l_c of head l16 & 7, from this wave's bins
 #pragma unroll
   for (int p = 0; p < CPW; ++p) {
+    lwave[p] = 0;
+    o_own[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!cwave) continue;
     const char* hb = hist_bytes + p * HIST_WORDS * 4;
     const uint32_t* h32 = hist32 + p * HIST_WORDS;
     const float unfix = pow2i(-fix_shift(lest[p][hh < G ? hh : 0]));   // 2^-S of this row's head
@@ -1238,7 +1247,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     // l_c: the waves of segment 0, first column tile (one per bin slice), add
     // their bins in integers; lanes (h, q4) and (h + 8, q4) hold complementary
     // bins of head h, so a row_ror:8 and two lane swaps complete the slice.
-    if (tile == 0) {
+    if (KSPLIT == 1 || tile == 0) {
       uint32_t lpart = 0;
 #pragma unroll
       for (int st = 0; st < KSL / 32; ++st)
@@ -1253,7 +1262,11 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
         const auto r = __builtin_amdgcn_permlane32_swap(lpart, lpart, false, false);
         lpart = uint32_t(r[0]) + uint32_t(r[1]);
       }
-      if (lane < G) lsum[p][ksl * G + lane] = lpart;
+      if constexpr (KSPLIT == 2) {
+        if (lane < G) lsum[p][ksl * G + lane] = lpart;
+      } else {
+        lwave[p] = lpart;
+      }
     }
     f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1293,17 +1306,30 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   }
 
   // ---- 6. write (m, l, o) of each chunk, or the normalised output --------------
-  __syncthreads();
-  if (kWgRecord && ksl == 0) {
+  if constexpr (KSPLIT == 2) __syncthreads();
+  // the integer l_c of the heads 4*q4 + r this lane writes (whole waves)
+  auto lsums = [&](int p, uint32_t (&l)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = min(4 * q4 + r, G - 1);
+      if constexpr (KSPLIT == 2) l[r] = lsum[p][h] + lsum[p][G + h];
+      else l[r] = uint32_t(__shfl(int(lwave[p]), h, 64));
+    }
+  };
+  if (kWgRecord && cwave && ksl == 0) {
     // both chunks' (m, l, o) merged into the workgroup's record (the max in
     // log2 units inside the kernel, natural log in the records)
     const int d = m_v * DS + jt * 16 + l16;
     f32x4 o[2];
+    uint32_t lr[2][4];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       o[p] = o_own[p];
-      const float4 other = part_tile[(p * NTILE + tile) * 64 + lane];
-      o[p][0] += other.x; o[p][1] += other.y; o[p][2] += other.z; o[p][3] += other.w;
+      if constexpr (KSPLIT == 2) {
+        const float4 other = part_tile[(p * NTILE + tile) * 64 + lane];
+        o[p][0] += other.x; o[p][1] += other.y; o[p][2] += other.z; o[p][3] += other.w;
+      }
+      lsums(p, lr[p]);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1314,7 +1340,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
         for (int p = 0; p < 2; ++p) {
           const bool own = p < n_own;
           mp[p] = own ? key_float(mkey[p][h]) : -INFINITY;
-          lp[p] = own ? float(lsum[p][h] + lsum[p][G + h]) * pow2i(-fix_shift(lest[p][h])) : 0.0f;
+          lp[p] = own ? float(lr[p][r]) * pow2i(-fix_shift(lest[p][h])) : 0.0f;
         }
         const float mh = max_f(mp[0], mp[1]);
         float om = 0.0f, lm = 0.0f;
@@ -1335,21 +1361,25 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       }
     }
   }
-  if (!kWgRecord && ksl == 0) {
+  if (!kWgRecord && cwave && ksl == 0) {
     const int d = m_v * DS + jt * 16 + l16;
 #pragma unroll
     for (int p = 0; p < CPW; ++p) {
       if (p >= n_own) break;   // the grid's last workgroup may own fewer chunks
       const int cc = c + p;
       f32x4 o = o_own[p];
-      const float4 other = part_tile[(p * NTILE + tile) * 64 + lane];
-      o[0] += other.x; o[1] += other.y; o[2] += other.z; o[3] += other.w;
+      if constexpr (KSPLIT == 2) {
+        const float4 other = part_tile[(p * NTILE + tile) * 64 + lane];
+        o[0] += other.x; o[1] += other.y; o[2] += other.z; o[3] += other.w;
+      }
+      uint32_t lr[4];
+      lsums(p, lr);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * q4 + r;
         if (h < G) {
           const float mh = key_float(mkey[p][h]);
-          const float lh = float(lsum[p][h] + lsum[p][G + h]) * pow2i(-fix_shift(lest[p][h]));
+          const float lh = float(lr[r]) * pow2i(-fix_shift(lest[p][h]));
           if (a.part_o == nullptr) {   // one chunk in all (C == 1)
             a.out[(row0 + h) * D + d] = lh > 0.0f ? o[r] * __builtin_amdgcn_rcpf(lh) : 0.0f;
           } else {
