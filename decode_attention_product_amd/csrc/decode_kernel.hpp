@@ -965,9 +965,8 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   // rows 8*q4 .. 8*q4+7 of column l16 of each block: eight 16-bit loads
   // straight into the halves of the operand registers (the 16 lanes of a row
   // group read 32 contiguous bytes), so no VALU work puts them in MFMA order.
-  // With one or two heads per workgroup there are registers to hold them
-  // through the gathers, so they are requested here, behind the V codes;
-  // with more heads, once the scores are in registers.
+  // They are requested once the scores are in registers (earlier they would
+  // hold registers through the gathers).
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   const int tile = wave % NTILE;
   const int ksl = wave / NTILE;               // bins [ksl * KSL, (ksl + 1) * KSL)
@@ -985,8 +984,6 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     }
   };
   load_codes(vcode, vc);
-  constexpr bool kCvbEarly = G <= 2 && KSPLIT == 2;
-  if constexpr (kCvbEarly) load_cvb();
 
   // step kernel: the V codebook in the table build's B layout, for the new
   // token's V code.  Requested here so its latency overlaps the gathers
@@ -1120,7 +1117,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       }
     }
   }
-  if constexpr (!kCvbEarly) load_cvb();
+  load_cvb();
 
   // ---- 4. V histogram (fixed point, integer LDS atomics) -----------------------
   // Lane rotation (G >= 2): at step (jm, jp) a lane updates segment
