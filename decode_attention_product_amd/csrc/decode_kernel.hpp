@@ -974,13 +974,21 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   const int m_v = tile % M;
   const int jt = tile / M;
   f16x8 cvb[KSL / 32];
+  // With two or four heads the histogram's bins of one segment lie 64 or
+  // 128 bytes apart, so the four bins a lane reads per step share a bank
+  // group with every other lane's: lane group q4 reads them in an order
+  // rotated by q4 instead (four bank groups), and the operands' k order
+  // within each lane follows -- position j holds bin perm(j) in both the
+  // histogram and the codebook operand, which leaves the sum over k as it is.
+  constexpr bool kRot = G == 2 || G == 4;
+  auto perm = [&](int j) { return kRot ? ((((j & 3) + q4) & 3) | (j & 4)) : j; };
   auto load_cvb = [&]() {
     if (!cwave) return;
 #pragma unroll
     for (int st = 0; st < KSL / 32; ++st) {
       const int64_t src = cb_g + (int64_t(m_v) * K + ksl * KSL + st * 32 + 8 * q4) * DS + jt * 16 + l16;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) cvb[st][j] = cb_load1<F>(a.v_cb, src + j * DS);
+      for (int j = 0; j < 8; ++j) cvb[st][j] = cb_load1<F>(a.v_cb, src + perm(j) * DS);
     }
   };
   load_codes(vcode, vc);
@@ -1206,7 +1214,8 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   // A[i][k]: rows i < 8 carry the fp16 high part of Hist[m_v][k][i], rows
   // i >= 8 the low part of Hist[m_v][k][i - 8] (zero for heads >= G), so one
   // 16x16x32 instruction covers both parts; o[h] = C[h] + C[h + 8].
-  // Lane (i, q4) needs bins 8*q4 .. 8*q4+7 of a 32-bin step.  The lanes i and
+  // Lane (i, q4) needs bins 8*q4 .. 8*q4+7 of a 32-bin step (position j
+  // holding bin perm(j), in the order its codebook operand was loaded in).  The lanes i and
   // i + 8 (same head, hi and lo) each convert half of them -- bins +0..3 on
   // the hi lane, +4..7 on the lo lane -- into both parts, and swap the part
   // the other one needs with one DPP move per word.
@@ -1234,7 +1243,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
         if constexpr (G >= 2) {
           const char* src = hb + (k0 * R + (hh >> 1) * M + m_v) * 8 + (hh & 1) * 4;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) raw[st][v] = *reinterpret_cast<const uint32_t*>(src + v * R * 8);
+          for (int v = 0; v < 4; ++v) raw[st][v] = *reinterpret_cast<const uint32_t*>(src + perm(v) * R * 8);
         } else {
           const uint4 w = *reinterpret_cast<const uint4*>(h32 + m_v * K + k0);
           raw[st][0] = w.x; raw[st][1] = w.y; raw[st][2] = w.z; raw[st][3] = w.w;
