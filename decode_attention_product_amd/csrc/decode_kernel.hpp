@@ -965,8 +965,12 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   // rows 8*q4 .. 8*q4+7 of column l16 of each block: eight 16-bit loads
   // straight into the halves of the operand registers (the 16 lanes of a row
   // group read 32 contiguous bytes), so no VALU work puts them in MFMA order.
-  // They are requested once the scores are in registers (earlier they would
-  // hold registers through the gathers).
+  // A wave waits for these loads where it issues them (two halves are packed
+  // per register as they arrive), so they are requested inside the histogram,
+  // before its last quarter of token slots: the issuing waves wait there
+  // while the others keep the LDS busy with their updates, instead of every
+  // wave waiting at a barrier.  With one slot per thread they go out just
+  // before the histogram.
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   const int tile = wave % NTILE;
   const int ksl = wave / NTILE;               // bins [ksl * KSL, (ksl + 1) * KSL)
@@ -1125,7 +1129,8 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       }
     }
   }
-  load_cvb();
+  constexpr int kCvbSlot = NT >= 2 ? (NT * 3) / 4 : 0;   // histogram slot before which they are requested
+  if constexpr (kCvbSlot == 0) load_cvb();
 
   // ---- 4. V histogram (fixed point, integer LDS atomics) -----------------------
   // Lane rotation (G >= 2): at step (jm, jp) a lane updates segment
@@ -1161,6 +1166,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     for (int h = 0; h < G; ++h) fscale[p][h] = pow2i(fix_shift(lest[p][h]));
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
+    if (kCvbSlot != 0 && i == kCvbSlot) load_cvb();
     const int t = t_begin + i * NTHR + tid;
     constexpr int kHistBytes = HIST_WORDS * 4;
     const int pc = i / NTC;                   // chunk of this slot (compile time)
