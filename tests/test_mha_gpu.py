@@ -119,9 +119,10 @@ def test_batched_paged_decode():
 
 
 def test_step_with_many_single_head_pairs():
-    """The decode step (one launch, per-request kernel) on a shape whose plain
-    decode is request-batched: same chunk length, output and codes as the
-    oracle's, and as the batched plain decode over the updated cache."""
+    """The decode step on a request-batched shape (the encode kernel writes
+    the new codes, then the request-batched kernel attends): codes and output
+    as the oracle's, and the batched plain decode over the updated cache
+    agrees."""
     B, H, L, M = 64, 16, 1024, 4
     say(f"step with many G=1 pairs B={B} H={H} L={L}")
     rng = np.random.default_rng(2300)
