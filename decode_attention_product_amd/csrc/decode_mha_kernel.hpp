@@ -218,14 +218,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
       if (l16 == 0) atomicAdd(&lest[r], mass_fix(psum[0]));
     }
 
-    if (p == NP - 1) {
+    // the contraction's codebook operands (last pass): a wave waits for
+    // them where it requests them (two 16-bit values packed per register),
+    // so they go out inside the histogram, before its last quarter of slots
+    auto load_cvb = [&]() {
 #pragma unroll
       for (int st = 0; st < KSL / 32; ++st) {
         const _Float16* src = cvg + (int64_t(m_v) * K + ksl * KSL + st * 32 + 8 * q4) * DS + jt * 16 + l16;
 #pragma unroll
         for (int j = 0; j < 8; ++j) cvb[st][j] = src[j * DS];
       }
-    }
+    };
+    constexpr int kCvbSlot = NT >= 2 ? (NT * 3) / 4 : 0;
+    if (p == NP - 1 && kCvbSlot == 0) load_cvb();
 
     // ---- 4. the request's V histogram ---------------------------------------------------
     __syncthreads();   // mass estimates complete
@@ -233,6 +238,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mha_kernel(DecodeArgs a
     uint32_t* hr = hist + r * M * K;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
+      if (kCvbSlot != 0 && p == NP - 1 && j == kCvbSlot) load_cvb();
       const int t = t_begin + li + j * TPR;
       if (t < t_end[p]) {
         const uint32_t u = uint32_t(fmaf(s[j], fscale, 0.5f));
