@@ -848,6 +848,44 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   // step kernel: does this chunk hold the new token (slot lens[b] - 1)?
   const int t_new = STEP ? len - 1 : -1;
   const bool has_new = STEP && t_new >= t_begin && t_new < t_end;   // uniform
+  // step kernel: the V codebook in the table build's B layout, for the new
+  // token's V code.  With one or two token slots per thread and fp16
+  // codebooks it is requested here, as soon as lens[b] is known, so its
+  // latency overlaps the table build; E4M3 codebooks request it after the
+  // table build, and with more slots the registers are needed by the scores
+  // and it is requested after them.
+  f16x4 cvl[STEP ? LUT_JOBS : 1][KSTEP_Q];
+  auto load_cvl = [&]() {
+#pragma unroll
+    for (int i = 0; i < LUT_JOBS; ++i) {
+      const int nt = wave / M + (NW / M) * i;
+      const int64_t row = cb_g + (int64_t(m_l) * K + nt * 16 + l16) * DS + 4 * q4;
+#pragma unroll
+      for (int s = 0; s < KSTEP_Q; ++s) cvl[i][s] = cb_load4<F>(a.v_cb, row + s * 16);
+    }
+  };
+  // With fp16 codebooks the early request is made by every wave as raw
+  // buffer loads, with an offset past the buffer where the chunk lacks the
+  // new token (no memory access): no branch, so the compiler's count of
+  // loads in flight stays exact and the table build waits only for its own.
+  constexpr bool kCvlEarly = NT <= 2;
+  constexpr bool kCvlRaw = STEP && kCvlEarly && F == CbFmt::F16;
+  typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+  u32x2v cvl_raw[kCvlRaw ? LUT_JOBS : 1][KSTEP_Q];
+  if constexpr (kCvlRaw) {
+    const __amdgpu_buffer_rsrc_t vr =
+        raw_buffer(static_cast<const _Float16*>(a.v_cb) + cb_g, uint32_t(M * K * DS * 2));
+#pragma unroll
+    for (int i = 0; i < LUT_JOBS; ++i) {
+      const int nt = wave / M + (NW / M) * i;
+#pragma unroll
+      for (int s = 0; s < KSTEP_Q; ++s) {
+        const uint32_t off = has_new ? uint32_t(((m_l * K + nt * 16 + l16) * DS + 4 * q4 + s * 16) * 2) : kOffNone;
+        cvl_raw[i][s] = __builtin_amdgcn_raw_buffer_load_b64(vr, off, 0, 0);
+      }
+    }
+  }
+
   // this (b, KV head)'s codes: a row of the dense cache, or a head's pool
   const int64_t code_base = PAGED ? int64_t(g) * a.pool_head_bytes : bg * a.Lmax * M;
   uint8_t* const kc = a.k_codes + code_base;
@@ -996,23 +1034,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
     }
   };
   load_codes(vcode, vc);
-
-  // step kernel: the V codebook in the table build's B layout, for the new
-  // token's V code.  Requested here so its latency overlaps the gathers
-  // below, except with four token slots per thread, where the registers
-  // are needed by the scores and it is requested after them.
-  f16x4 cvl[STEP ? LUT_JOBS : 1][KSTEP_Q];
-  auto load_cvl = [&]() {
-#pragma unroll
-    for (int i = 0; i < LUT_JOBS; ++i) {
-      const int nt = wave / M + (NW / M) * i;
-      const int64_t row = cb_g + (int64_t(m_l) * K + nt * 16 + l16) * DS + 4 * q4;
-#pragma unroll
-      for (int s = 0; s < KSTEP_Q; ++s) cvl[i][s] = cb_load4<F>(a.v_cb, row + s * 16);
-    }
-  };
-  constexpr bool kCvlEarly = NT <= 2;
-  if constexpr (STEP && kCvlEarly) {
+  if constexpr (STEP && kCvlEarly && !kCvlRaw) {
     if (has_new) load_cvl();
   }
 
@@ -1036,6 +1058,12 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   if constexpr (STEP) {
     if (has_new) {   // the new token's V: same products as its K above, per-wave argmax
       if constexpr (!kCvlEarly) load_cvl();
+      if constexpr (kCvlRaw) {
+#pragma unroll
+        for (int i = 0; i < LUT_JOBS; ++i)
+#pragma unroll
+          for (int s = 0; s < KSTEP_Q; ++s) cvl[i][s] = __builtin_bit_cast(f16x4, cvl_raw[i][s]);
+      }
       float best_v = -INFINITY;
       int idx_v = 0;
       // four jobs at a time: norms (cross-lane sums), products, then compares
