@@ -794,16 +794,38 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   constexpr int kNewRow = 8;
   const int64_t bg = int64_t(b) * a.Hkv + g;
   const int64_t cnt = bg * a.hs + hp;         // arrival counter of this head part
+  // Rows 0..G-1 of the A operand are the queries, row 8 (step) the new
+  // token's K (xv: its V); the other rows only feed output rows that are
+  // never read.  With one or two token slots per thread (a latency-bound
+  // workgroup) every lane loads with no branch, the other rows' lanes any
+  // valid row (query row 0): under branches the loads and zero fills of the
+  // same registers take different lane masks, and the compiler then waits
+  // for the first loads before the codebook requests below.  With more
+  // slots the branch form measured 0.2 us faster on the benchmark's GQA and
+  // long-context steps, so it stays there.
+  constexpr bool kQBranchFree = NT <= 2;
   f16x4 qa[KSTEP_Q], xv[KSTEP_Q];
+  if constexpr (kQBranchFree) {
+    const int64_t qoff = (row0 + (l16 < G ? l16 : 0)) * D + m_l * DS + 4 * q4;
+    const int64_t noff = bg * D + m_l * DS + 4 * q4;
+    const __half* ksrc = (STEP && l16 == kNewRow) ? a.k_new + noff : a.q + qoff;
 #pragma unroll
-  for (int s = 0; s < KSTEP_Q; ++s) {
-    qa[s] = f16x4{0, 0, 0, 0};
-    xv[s] = f16x4{0, 0, 0, 0};
-    if (l16 < G) {
-      qa[s] = *reinterpret_cast<const f16x4*>(a.q + (row0 + l16) * D + m_l * DS + s * 16 + 4 * q4);
-    } else if (STEP && l16 == kNewRow) {
-      qa[s] = *reinterpret_cast<const f16x4*>(a.k_new + bg * D + m_l * DS + s * 16 + 4 * q4);
-      xv[s] = *reinterpret_cast<const f16x4*>(a.v_new + bg * D + m_l * DS + s * 16 + 4 * q4);
+    for (int s = 0; s < KSTEP_Q; ++s) {
+      qa[s] = *reinterpret_cast<const f16x4*>(ksrc + s * 16);
+      xv[s] = f16x4{0, 0, 0, 0};
+      if constexpr (STEP) xv[s] = *reinterpret_cast<const f16x4*>(a.v_new + noff + s * 16);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < KSTEP_Q; ++s) {
+      qa[s] = f16x4{0, 0, 0, 0};
+      xv[s] = f16x4{0, 0, 0, 0};
+      if (l16 < G) {
+        qa[s] = *reinterpret_cast<const f16x4*>(a.q + (row0 + l16) * D + m_l * DS + s * 16 + 4 * q4);
+      } else if (STEP && l16 == kNewRow) {
+        qa[s] = *reinterpret_cast<const f16x4*>(a.k_new + bg * D + m_l * DS + s * 16 + 4 * q4);
+        xv[s] = *reinterpret_cast<const f16x4*>(a.v_new + bg * D + m_l * DS + s * 16 + 4 * q4);
+      }
     }
   }
   f16x4 ckb[LUT_JOBS][KSTEP_Q];
@@ -818,13 +840,21 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
   len = len < 0 ? 0 : (len > a.Lmax ? a.Lmax : len);
   const int t_end = min(t_begin + n_own * a.T, len);
   if (t_begin >= t_end) {   // empty chunks (uniform over the workgroup)
-    // A use of the codebook operands on this path too, so the compiler keeps
-    // their loads ahead of the wait for lens[b] instead of sinking them into
-    // the other branch (which would put one memory latency after the other).
+    // A use of the codebook and query operands on this path too, so the
+    // compiler keeps their loads ahead of the wait for lens[b] instead of
+    // sinking them into the other branch (which would put one memory latency
+    // after the other).
 #pragma unroll
     for (int i = 0; i < LUT_JOBS; ++i)
 #pragma unroll
       for (int s = 0; s < KSTEP_Q; ++s) asm volatile("" ::"v"(ckb[i][s]));
+    if constexpr (kQBranchFree) {
+#pragma unroll
+      for (int s = 0; s < KSTEP_Q; ++s) {
+        asm volatile("" ::"v"(qa[s]));
+        if constexpr (STEP) asm volatile("" ::"v"(xv[s]));
+      }
+    }
     const int n_rec = kWgRecord ? 1 : n_own;
     for (int i = tid; i < n_rec * G * D; i += NTHR) {
       const int cc = (kWgRecord ? int(blockIdx.y) : c) + i / (G * D), h = (i / D) % G, d = i % D;
