@@ -10,8 +10,8 @@
 //
 //   0. The operands are requested in the order they are used: q and the K
 //      codebook (table build) before lens[b] is even waited for, then the
-//      chunk's K and V codes, and -- once the table is built -- the V
-//      codebook operands of the contraction.
+//      chunk's K codes; once the table is built, the V codes; and inside the
+//      histogram, the V codebook operands of the contraction.
 //   1. Lookup table LUT[m][k][h] = q_h[m] . Ck_g[m][k] -- the query's partial
 //      dot product with every K codeword (AQPIM page, section 4.1; kept on
 //      chip as the page's GPU note suggests) -- computed as M small
