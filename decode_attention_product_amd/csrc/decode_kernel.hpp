@@ -10,7 +10,8 @@
 //
 //   0. The operands are requested in the order they are used: q and the K
 //      codebook (table build) before lens[b] is even waited for, then the
-//      chunk's K codes; once the table is built, the V codes; and inside the
+//      chunk's K codes (with several token slots per thread, once the
+//      codebook is in); once the table is built, the V codes; and inside the
 //      histogram, the V codebook operands of the contraction.
 //   1. Lookup table LUT[m][k][h] = q_h[m] . Ck_g[m][k] -- the query's partial
 //      dot product with every K codeword (AQPIM page, section 4.1; kept on
@@ -953,12 +954,16 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       dst[i].load(r, off);
     }
   };
-  // Only the K codes go out with the K codebook: the V codes are requested
-  // after the table build (the histogram needs them, after the scores), so
-  // the table's operands and the K codes reach the CU with less traffic
-  // queued ahead of them.
+  // The V codes are requested after the table build (the histogram needs
+  // them, after the scores), so less traffic is queued ahead of the table's
+  // operands.  With four or more token slots per thread the K codes wait
+  // too, until the codebook operands are in: the workgroup's table reads
+  // then start on codes that arrive behind a codebook that came alone
+  // (measured faster on the GQA step, the same on the long-context one);
+  // with one or two slots (latency-bound) they go out with the codebook.
+  constexpr bool kKcLate = NT >= 4;
   TokenCodes<M> kcode[NT], vcode[NT];
-  load_codes(kcode, kc);
+  if constexpr (!kKcLate) load_codes(kcode, kc);
 
   // the histograms are cleared while the operands are in flight
   for (int i = tid; i < CPW * HIST_WORDS / 4; i += NTHR)
@@ -1015,6 +1020,7 @@ __device__ __forceinline__ void score_chunk(const DecodeArgs& a) {
       if (lane == 16 * (kNewRow / 4)) new_key[0][wave] = argmax_key(best_k, idx_k);
     }
   }
+  if constexpr (kKcLate) load_codes(kcode, kc);
   __syncthreads();
 
   // step kernel: the new token's K codes, into the cache (one head part
