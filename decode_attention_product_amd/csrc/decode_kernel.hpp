@@ -288,8 +288,10 @@ __device__ __forceinline__ void argmax_pair32(float& s, int& k) {
 
 // 64-bit key whose unsigned order is (score, then lower index): the integer
 // LDS max of keys is the argmax with the lowest index among equal scores.
+// Adding +0 turns a -0 score into +0, so the two zeros count as equal here
+// as they do in the float compares.
 __device__ __forceinline__ unsigned long long argmax_key(float score, int k) {
-  const uint32_t hi = uint32_t(float_key(score)) ^ 0x80000000u;
+  const uint32_t hi = uint32_t(float_key(score + 0.0f)) ^ 0x80000000u;
   return (static_cast<unsigned long long>(hi) << 32) | uint32_t(255 - k);
 }
 __device__ __forceinline__ int argmax_key_index(unsigned long long key) {

@@ -105,22 +105,23 @@ __device__ __forceinline__ f32x4 tile_scores(const f16x4 (&c)[KS], const f16x4 (
 
 // The best (score, index) over NCT tiles of scores (codeword kbase + nt*16 +
 // 4*q4 + r for acc[nt][r]) as an argmax key, the same in the four lanes of
-// column j: each lane walks its codewords in ascending order (ties keep the
-// lower), then rows q4 ^ 1 and q4 ^ 2 are combined by lane swaps.
+// column j.  Each lane takes the largest of its scores (the compiler forms
+// three-operand maxima: one instruction per two scores), then the lowest of
+// its codewords that holds it, by a scan from the top; rows q4 ^ 1 and
+// q4 ^ 2 are then combined by lane swaps.  Ties go to the lowest index, -0
+// and +0 counting as equal.
 template <int NCT>
 __device__ __forceinline__ unsigned long long tiles_best_key(const f32x4 (&acc)[NCT], int kbase,
                                                              int q4) {
   float best = acc[0][0];
-  int bk = kbase + 4 * q4;
 #pragma unroll
-  for (int nt = 0; nt < NCT; ++nt) {
+  for (int i = 1; i < 4 * NCT; ++i) best = fmaxf(best, acc[i / 4][i % 4]);
+  int off = (NCT - 1) * 16 + 3;   // the last codeword, unless a lower one holds the maximum
 #pragma unroll
-    for (int r = (nt == 0 ? 1 : 0); r < 4; ++r) {
-      const bool take = acc[nt][r] > best;
-      best = take ? acc[nt][r] : best;
-      bk = take ? kbase + nt * 16 + 4 * q4 + r : bk;
-    }
-  }
+  for (int nt = NCT - 1; nt >= 0; --nt)
+#pragma unroll
+    for (int r = (nt == NCT - 1 ? 2 : 3); r >= 0; --r) off = acc[nt][r] == best ? nt * 16 + r : off;
+  int bk = kbase + 4 * q4 + off;
   argmax_pair16(best, bk);   // rows q4 and q4 ^ 1
   argmax_pair32(best, bk);   // rows q4 and q4 ^ 2
   return argmax_key(best, bk);

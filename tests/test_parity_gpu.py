@@ -346,6 +346,30 @@ def test_encode_ties_lowest_index():
     np.testing.assert_array_equal(got, oracle.encode(x, cb))
 
 
+def test_encode_zero_score_ties_lowest_index():
+    """Zero codewords against a zero segment all score exactly 0 (as -0 or +0,
+    however the sums round; the segment of vector 1 is negative zeros); the
+    lowest of them must win whether the others sit in the same lane, in
+    another lane or in the other half of the codebook."""
+    say("encode zero-score ties")
+    rng = np.random.default_rng(602)
+    cb = gen.codebooks(rng, 1, 4, 256, 32)
+    for m, ks in {0: (21, 5, 200), 1: (200, 77), 2: (250, 44, 40)}.items():
+        cb[0, m, list(ks)] = 0
+    x, _ = gen.noisy_codewords(rng, cb, 3, 0.05)
+    x[0, 0, :96] = 0
+    x[1, 0, 32:64] = np.float16(-0.0)
+    built_tie = np.zeros((3, 1, 4), dtype=bool)
+    built_tie[0, 0, :3] = built_tie[1, 0, 1] = True
+    assert_clear_margins(x, cb, "encode zero ties (other segments)", mask=~built_tie)
+    codes = torch.empty((3, 1, 4), dtype=torch.uint8, device="cuda")
+    pq.pq_encode(dev(x), dev(cb), codes)
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy()
+    assert list(got[0, 0, :3]) == [5, 77, 40] and got[1, 0, 1] == 77
+    np.testing.assert_array_equal(got, oracle.encode(x, cb))
+
+
 def test_encode_many_matches_single_calls():
     """K and V of a batch of new tokens in one launch (pq_encode_many) give
     exactly what two pq_encode calls give, into a cache through slots."""
