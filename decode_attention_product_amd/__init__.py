@@ -163,9 +163,14 @@ def _stream(stream) -> Optional[int]:
 
 
 def _need(t, name, dtype, shape=None, device=True):
-    import torch
     if t is None:
         return
+    # fast path (a call per launch argument): dtypes are singletons, and a
+    # torch.Size equals the tuple of its sizes
+    if (t.dtype is dtype and (shape is None or t.shape == shape) and t.is_contiguous()
+            and (t.is_cuda or not device)):
+        return
+    import torch
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
@@ -316,9 +321,17 @@ def pq_attn_step_workspace_bytes(desc: PQAttnDesc) -> int:
     return int(load_library().pq_attn_step_workspace_bytes(ctypes.byref(desc)))
 
 
+_num_chunks_memo = {}
+
+
 def _desc_key(desc: PQAttnDesc):
-    return (desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim, desc.n_sub, desc.n_codes,
-            desc.max_len, pq_attn_num_chunks(desc))
+    shape = (desc.batch, desc.n_q_heads, desc.n_kv_heads, desc.head_dim, desc.n_sub, desc.n_codes,
+             desc.max_len)
+    fields = shape + (desc.chunk,)
+    c = _num_chunks_memo.get(fields)
+    if c is None:   # the planner is a pure function of these fields
+        c = _num_chunks_memo[fields] = pq_attn_num_chunks(desc)
+    return shape + (c,)
 
 
 def step_workspace(desc: PQAttnDesc, device):
