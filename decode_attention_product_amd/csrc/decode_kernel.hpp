@@ -66,19 +66,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // of its fp16 upcast.
 enum class CbFmt { F16, E4M3 };
 
-// Two E4M3 bytes (bits 0-7 and 8-15 of w) as two fp16 values.  The byte's
-// 7 magnitude bits shifted to bits 7..13 of an fp16 form exponent e and
-// mantissa f, i.e. (1 + f/8) 2^(e-15), or f 2^-17 for e = 0; times 2^8 that
-// is the E4M3 value (1 + f/8) 2^(e-7), resp. f 2^-9, exactly.  The sign bit
-// moves to bit 15.
+// Two E4M3 bytes (bits 0-7 and 8-15 of w) as two fp16 values, by gfx950's
+// packed FP8 conversion with a scale of 1 (every E4M3 value, subnormals
+// included, is an fp16 value, so the conversion is exact).
 __device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
-  const uint32_t mag = ((w & 0x7Fu) << 7) | ((w & 0x7F00u) << 15);
-  const f16x2 v = __builtin_bit_cast(f16x2, mag) * f16x2{(_Float16)256.0f, (_Float16)256.0f};
-  return __builtin_bit_cast(uint32_t, v) | ((w & 0x80u) << 8) | ((w & 0x8000u) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
 }
 // Four E4M3 bytes (little-endian in w) as four fp16 values.
 __device__ __forceinline__ f16x4 e4m3x4_to_f16x4(uint32_t w) {
-  const uint32_t lo = e4m3x2_to_f16x2(w), hi = e4m3x2_to_f16x2(w >> 16);
+  const uint32_t lo = e4m3x2_to_f16x2(w);
+  const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
   return __builtin_bit_cast(f16x4, make_uint2(lo, hi));
 }
 // Codebook elements e .. e+3 (e a multiple of 4) as fp16.
