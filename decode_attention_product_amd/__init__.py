@@ -330,6 +330,8 @@ def _desc_key(desc: PQAttnDesc):
     fields = shape + (desc.chunk,)
     c = _num_chunks_memo.get(fields)
     if c is None:   # the planner is a pure function of these fields
+        if len(_num_chunks_memo) >= 4096:
+            _num_chunks_memo.clear()
         c = _num_chunks_memo[fields] = pq_attn_num_chunks(desc)
     return shape + (c,)
 

@@ -82,3 +82,42 @@ def test_step_workspace_is_tied_to_its_descriptor():
     pq._check_step_workspace(a, ws, "same shape")          # accepted
     with pytest.raises(ValueError):
         pq._check_step_workspace(b, ws, "other shape")
+
+
+def test_step_workspace_key_follows_the_chunk():
+    """The workspace key reuses the planner's chunk count per descriptor
+    fields; a descriptor that differs only in its chunk gets its own count."""
+    import pytest
+    pytest.importorskip("torch")
+    import decode_attention_product_amd as pq
+    import os
+    if not os.path.exists(pq.LIB_PATH):
+        pytest.skip("library not built")
+    a = pq.PQAttnDesc(1, 64, 8, 128, 4, 256, 131072, 2048, 0.0883883)
+    b = pq.PQAttnDesc(1, 64, 8, 128, 4, 256, 131072, 4096, 0.0883883)
+    for _ in range(2):     # first call fills the memo, second reads it
+        assert pq._desc_key(a)[-1] == pq.pq_attn_num_chunks(a) == 64
+        assert pq._desc_key(b)[-1] == pq.pq_attn_num_chunks(b) == 32
+    b.chunk = 2048         # mutated in place: the key follows
+    assert pq._desc_key(b) == pq._desc_key(a)
+
+
+def test_tensor_checks_fast_path_and_errors():
+    """The binding's tensor checks: the fast path accepts what the detailed
+    checks accept (a shape given as a list too) and every failure still
+    raises with its own message.  CPU tensors, device check off."""
+    import pytest
+    torch = pytest.importorskip("torch")
+    import decode_attention_product_amd as pq
+    t = torch.zeros((2, 3, 128), dtype=torch.float16)
+    pq._need(t, "t", torch.float16, (2, 3, 128), device=False)
+    pq._need(t, "t", torch.float16, [2, 3, 128], device=False)
+    pq._need(None, "t", torch.float16, (1,), device=False)
+    with pytest.raises(TypeError, match="expected torch.float16"):
+        pq._need(t.float(), "t", torch.float16, (2, 3, 128), device=False)
+    with pytest.raises(ValueError, match="expected shape"):
+        pq._need(t, "t", torch.float16, (2, 3, 64), device=False)
+    with pytest.raises(ValueError, match="contiguous"):
+        pq._need(t.transpose(0, 1), "t", torch.float16, (3, 2, 128), device=False)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        pq._need(t, "t", torch.float16, (2, 3, 128))
