@@ -179,6 +179,37 @@ __global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
   f16x4 acur[KS], anext[KS];
   load_a(0, acur);
 
+  // Where vector v of this workgroup goes: the slot map, or the decode
+  // step's lens and block-table lookups; -1: not written.  With one tile of
+  // vectors (a decode step's new tokens) the lookups are requested here, so
+  // that their round trips overlap the products instead of following the
+  // last barrier; with 256-vector tiles (a prefill) they stay at the end,
+  // where they measured faster.
+  static_assert(NV <= 128 * M, "one vector per thread in the write-out");
+  auto dest = [&](int v) -> int64_t {
+    const int64_t n = n0 + v;
+    int64_t s = a.slots ? a.slots[n] : n;
+    if (a.lens != nullptr) {
+      int l = a.lens[n];
+      l = l < 0 ? 0 : (l > a.Lmax ? a.Lmax : l);
+      const int t = l - 1;
+      if (l == 0) return -1;
+      if (a.table != nullptr) {
+        const uint32_t pg = min(uint32_t(a.table[n * a.max_pages + (t >> a.page_shift)]), a.n_pages - 1u);
+        s = (int64_t(pg) << a.page_shift) | int64_t(t & ((1 << a.page_shift) - 1));
+      } else {
+        s = n * a.Hkv * a.Lmax + t;
+      }
+    }
+    return s;
+  };
+  constexpr bool kEarlyDest = NTILE == 1;
+  const int vw = threadIdx.x;
+  int64_t s_early = -1;
+  if constexpr (kEarlyDest) {
+    if (vw < nv) s_early = dest(vw);
+  }
+
   f32x4 cinit[NCT];
   score_inits<KS, NCT>(bop, cinit, q4);
 
@@ -205,33 +236,22 @@ __global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
   }
   __syncthreads();
 
-  for (int v = threadIdx.x; v < nv; v += 128 * M) {
-    const int64_t n = n0 + v;
-    int64_t s = a.slots ? a.slots[n] : n;
-    if (a.lens != nullptr) {
-      int l = a.lens[n];
-      l = l < 0 ? 0 : (l > a.Lmax ? a.Lmax : l);
-      if (l == 0) continue;
-      const int t = l - 1;
-      if (a.table != nullptr) {
-        const uint32_t pg = min(uint32_t(a.table[n * a.max_pages + (t >> a.page_shift)]), a.n_pages - 1u);
-        s = (int64_t(pg) << a.page_shift) | int64_t(t & ((1 << a.page_shift) - 1));
-      } else {
-        s = n * a.Hkv * a.Lmax + t;
-      }
-    }
-    if (s < 0 || (a.scs > 0 && s > a.codes_bytes / a.scs)) continue;
-    const int64_t off = s * a.scs + int64_t(h) * a.sch;
-    if (off < 0 || off + M > a.codes_bytes) continue;
-    int code[M];
+  if (vw < nv) {
+    const int v = vw;
+    const int64_t s = kEarlyDest ? s_early : dest(v);
+    const bool slot_ok = s >= 0 && !(a.scs > 0 && s > a.codes_bytes / a.scs);
+    const int64_t off = slot_ok ? s * a.scs + int64_t(h) * a.sch : -1;
+    if (slot_ok && off >= 0 && off + M <= a.codes_bytes) {
+      int code[M];
 #pragma unroll
-    for (int j = 0; j < M; ++j) {
-      const unsigned long long k0 = keys[v][j][0], k1 = keys[v][j][1];
-      code[j] = argmax_key_index(k1 > k0 ? k1 : k0);
+      for (int j = 0; j < M; ++j) {
+        const unsigned long long k0 = keys[v][j][0], k1 = keys[v][j][1];
+        code[j] = argmax_key_index(k1 > k0 ? k1 : k0);
+      }
+      TokenCodes<M> tc;
+      tc.set(code);
+      tc.store(codes + off);
     }
-    TokenCodes<M> tc;
-    tc.set(code);
-    tc.store(codes + off);
   }
 }
 
