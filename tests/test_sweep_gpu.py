@@ -146,3 +146,31 @@ def test_sweep(i):
     if c["path"].endswith("step") and ws is not None:
         rec = pq.pq_attn_workspace_bytes(desc)
         assert (ws[rec:rec + desc.batch * desc.n_kv_heads * 4] == 0).all(), "arrival counters not reset"
+
+
+FP8_CASES = [dict(draw_case(1000 + i), path="decode") for i in range(24)]
+
+
+@pytest.mark.parametrize("i", range(len(FP8_CASES)))
+def test_sweep_fp8_codebooks(i):
+    """The same sweep of shapes for the dense decode with E4M3 codebooks: the
+    oracle on the exactly decoded bytes, and bit for bit the fp16 call on the
+    fp16 upcast."""
+    c = FP8_CASES[i]
+    say(f"fp8 case {i}: {c}")
+    _, inp = gen.random_case(c["seed"], batch=c["B"], n_q_heads=c["G"] * c["Hkv"],
+                             n_kv_heads=c["Hkv"], max_len=c["Lmax"], n_sub=c["M"], lens=c["lens"])
+    rng = np.random.default_rng(c["seed"] + 2)
+    k8 = gen.codebooks_fp8(rng, c["Hkv"], c["M"], 256, 128 // c["M"])
+    v8 = gen.codebooks_fp8(rng, c["Hkv"], c["M"], 256, 128 // c["M"])
+    kf, vf = oracle.fp8_e4m3_to_float64(k8), oracle.fp8_e4m3_to_float64(v8)
+    lens = np.asarray(c["lens"], np.int32)
+    ref = oracle.decode_attention(inp["q"], inp["k_codes"], inp["v_codes"], kf, vf, lens)
+    q, kc, vc, lens_d = dev(inp["q"]), dev(inp["k_codes"]), dev(inp["v_codes"]), dev(lens)
+    out8 = pq.pq_attn_decode_fp8cb(q, kc, vc, dev(k8), dev(v8), lens_d, chunk=c["chunk"])
+    out16 = pq.pq_attn_decode(q, kc, vc, dev(kf.astype(np.float16)), dev(vf.astype(np.float16)),
+                              lens_d, chunk=c["chunk"])
+    torch.cuda.synchronize()
+    got = out8.cpu().numpy()
+    assert_attn_close(got, ref, f"fp8 case {i}")
+    np.testing.assert_array_equal(got, out16.cpu().numpy())
