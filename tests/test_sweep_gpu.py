@@ -174,3 +174,52 @@ def test_sweep_fp8_codebooks(i):
     got = out8.cpu().numpy()
     assert_attn_close(got, ref, f"fp8 case {i}")
     np.testing.assert_array_equal(got, out16.cpu().numpy())
+
+
+def draw_encode_case(i):
+    rng = np.random.default_rng(9700 + i)
+    return dict(N=int(rng.choice([1, 7, 16, 17, 255, 256, 257, int(rng.integers(1, 1500))])),
+                H=int(rng.choice([1, 2, 3, 8, 32, 40])), M=int(rng.choice([4, 8])),
+                slots=bool(rng.integers(0, 2)), fp8=bool(rng.integers(0, 3) == 0), seed=9800 + i)
+
+
+ENC_CASES = [draw_encode_case(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("i", range(len(ENC_CASES)))
+def test_sweep_encode(i):
+    """Encode over a sweep of vector counts (one tile, tile edges, many
+    tiles), head counts and both segment counts, into a dense code array or
+    through a permuted slot map, with fp16 or E4M3 codebooks: bit-exact
+    against the oracle and the generating index on margin-checked inputs."""
+    c = ENC_CASES[i]
+    say(f"encode case {i}: {c}")
+    rng = np.random.default_rng(c["seed"])
+    N, H, M = c["N"], c["H"], c["M"]
+    if c["fp8"]:
+        cb8 = gen.codebooks_fp8(rng, H, M, 256, 128 // M)
+        cb = oracle.fp8_e4m3_to_float64(cb8).astype(np.float16)
+    else:
+        cb = gen.codebooks(rng, H, M, 256, 128 // M)
+    x, src = gen.noisy_codewords(rng, cb, N, 0.05)
+    assert_clear_margins(x, cb, f"encode case {i}")
+    exp = oracle.encode(x, cb)
+    np.testing.assert_array_equal(exp, src)
+    cb_d = dev(cb8) if c["fp8"] else dev(cb)
+    enc = pq.pq_encode_fp8cb if c["fp8"] else pq.pq_encode
+    if c["slots"]:
+        # vector n goes to row perm[n] of a larger code array; other rows untouched
+        rows = N + 5
+        perm = rng.permutation(rows)[:N].astype(np.int64)
+        codes = torch.full((rows, H, M), 77, dtype=torch.uint8, device="cuda")
+        desc = pq.PQEncodeDesc(N, H, 128, M, 256, H * 128, 128, H * M, M, codes.numel())
+        enc(dev(x), cb_d, codes, slots=dev(perm), desc=desc)
+        torch.cuda.synchronize()
+        want = np.full((rows, H, M), 77, dtype=np.uint8)
+        want[perm] = exp
+        np.testing.assert_array_equal(codes.cpu().numpy(), want)
+    else:
+        codes = torch.empty((N, H, M), dtype=torch.uint8, device="cuda")
+        enc(dev(x), cb_d, codes)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(codes.cpu().numpy(), exp)
