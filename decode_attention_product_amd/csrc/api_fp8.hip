@@ -165,14 +165,21 @@ pq_status pq_encode_fp8cb(const pq_encode_desc* desc, const void* x, const uint8
   const int64_t big = (p.N + kEncodeVectorsF8 - 1) / kEncodeVectorsF8;
   const int nv = big * p.H < kEncodeCUsF8 ? kEncodeVectorsF8Small : kEncodeVectorsF8;
   const void* fn;
-  if (nv == kEncodeVectorsF8Small)
+  const unsigned tiles = unsigned((p.N + nv - 1) / nv);
+  // one segment per workgroup when that still fits the CUs in one round (as
+  // for fp16 codebooks)
+  const bool seg = nv == kEncodeVectorsF8Small && int64_t(tiles) * p.H * p.M <= kEncodeCUsF8;
+  if (seg)
+    fn = p.M == 4 ? reinterpret_cast<const void*>(&encode_kernel<4, kEncodeVectorsF8Small, kF8, true>)
+                  : reinterpret_cast<const void*>(&encode_kernel<8, kEncodeVectorsF8Small, kF8, true>);
+  else if (nv == kEncodeVectorsF8Small)
     fn = p.M == 4 ? reinterpret_cast<const void*>(&encode_kernel<4, kEncodeVectorsF8Small, kF8>)
                   : reinterpret_cast<const void*>(&encode_kernel<8, kEncodeVectorsF8Small, kF8>);
   else
     fn = p.M == 4 ? reinterpret_cast<const void*>(&encode_kernel<4, kEncodeVectorsF8, kF8>)
                   : reinterpret_cast<const void*>(&encode_kernel<8, kEncodeVectorsF8, kF8>);
-  const unsigned tiles = unsigned((p.N + nv - 1) / nv);
-  return launch_f8(fn, dim3(unsigned(p.H), tiles, 1u), dim3(128 * p.M), &a, static_cast<hipStream_t>(stream));
+  return launch_f8(fn, dim3(unsigned(p.H), tiles, seg ? unsigned(p.M) : 1u), dim3(seg ? 128 : 128 * p.M), &a,
+                   static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

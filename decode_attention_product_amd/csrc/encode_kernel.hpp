@@ -127,9 +127,12 @@ __device__ __forceinline__ unsigned long long tiles_best_key(const f32x4 (&acc)[
   return argmax_key(best, bk);
 }
 
-// F: the codebooks' element format (converted to fp16 on load).
-template <int M, int NV, CbFmt F = CbFmt::F16>
-__global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
+// F: the codebooks' element format (converted to fp16 on load).  SEG: one
+// segment per workgroup (two waves, grid z = plane * M + segment), so a
+// workgroup loads 1/M of the codebook; for one-tile launches (a decode
+// step's new tokens), where the codebook's arrival is most of the time.
+template <int M, int NV, CbFmt F = CbFmt::F16, bool SEG = false>
+__global__ __launch_bounds__(SEG ? 128 : 128 * M) void encode_kernel(EncodeArgs a) {
   constexpr int D = 128;
   constexpr int K = 256;
   constexpr int DS = D / M;
@@ -137,17 +140,20 @@ __global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
   constexpr int NTILE = NV / 16;       // 16-vector tiles
   constexpr int NCT = K / 32;          // 16-codeword tiles per half
 
+  constexpr int NTHR = SEG ? 128 : 128 * M;
+  constexpr int MK = SEG ? 1 : M;      // segments per workgroup
   // per (vector, segment, half): the half's best as an argmax key
-  __shared__ unsigned long long keys[NV][M][2];
+  __shared__ unsigned long long keys[NV][MK][2];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int m = wave % M;              // this wave's segment
-  const int half = wave / M;           // and codeword half
+  const int m = SEG ? int(blockIdx.z) % M : wave % M;   // this wave's segment
+  const int mk = SEG ? 0 : m;
+  const int half = SEG ? wave : wave / M;               // and codeword half
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
   const int h = blockIdx.x;            // heads fastest: the heads of one vector row are read together
-  const int plane = blockIdx.z;
+  const int plane = SEG ? int(blockIdx.z) / M : int(blockIdx.z);
   const __half* xp = a.x[plane];
   uint8_t* codes = a.codes[plane];
   const int64_t n0 = int64_t(blockIdx.y) * NV;
@@ -185,7 +191,7 @@ __global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
   // that their round trips overlap the products instead of following the
   // last barrier; with 256-vector tiles (a prefill) they stay at the end,
   // where they measured faster.
-  static_assert(NV <= 128 * M, "one vector per thread in the write-out");
+  static_assert(NV <= NTHR, "one vector per thread in the write-out");
   auto dest = [&](int v) -> int64_t {
     const int64_t n = n0 + v;
     int64_t s = a.slots ? a.slots[n] : n;
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
     const unsigned long long key = tiles_best_key<NCT>(acc, kbase, q4);
     if (q4 == 0) {
       const int v = t * 16 + l16;
-      if (v < nv) keys[v][m][half] = key;
+      if (v < nv) keys[v][mk][half] = key;
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) acur[s] = anext[s];
@@ -242,15 +248,20 @@ __global__ __launch_bounds__(128 * M) void encode_kernel(EncodeArgs a) {
     const bool slot_ok = s >= 0 && !(a.scs > 0 && s > a.codes_bytes / a.scs);
     const int64_t off = slot_ok ? s * a.scs + int64_t(h) * a.sch : -1;
     if (slot_ok && off >= 0 && off + M <= a.codes_bytes) {
-      int code[M];
+      if constexpr (SEG) {   // this workgroup's segment: one byte
+        const unsigned long long k0 = keys[v][0][0], k1 = keys[v][0][1];
+        codes[off + m] = uint8_t(argmax_key_index(k1 > k0 ? k1 : k0));
+      } else {
+        int code[M];
 #pragma unroll
-      for (int j = 0; j < M; ++j) {
-        const unsigned long long k0 = keys[v][j][0], k1 = keys[v][j][1];
-        code[j] = argmax_key_index(k1 > k0 ? k1 : k0);
+        for (int j = 0; j < M; ++j) {
+          const unsigned long long k0 = keys[v][j][0], k1 = keys[v][j][1];
+          code[j] = argmax_key_index(k1 > k0 ? k1 : k0);
+        }
+        TokenCodes<M> tc;
+        tc.set(code);
+        tc.store(codes + off);
       }
-      TokenCodes<M> tc;
-      tc.set(code);
-      tc.store(codes + off);
     }
   }
 }
